@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle.
+
+This module holds no attention arithmetic: it only draws random numbers and
+lays them out.  Every draw comes from one CPU ``torch.Generator`` seeded by
+the caller, in a fixed order, so the GPU path and the CPU oracle consume the
+very same bits.
+
+Recipe (per call):
+  1. ragged lengths, if requested: ``torch.randint(lo, hi + 1, (B,))``;
+  2. q: float32 ``randn`` [B, H, d] (times ``q_scale``), then cast;
+  3. k_cache: float32 ``randn`` [K, S_max, d] for b = 0..B-1 in turn, cast;
+  4. v_cache: likewise;
+  5. k_new, v_new: float32 ``randn`` [B, K, d] each, then cast.
+Cache rows at positions >= L_b are then overwritten with NaN, so that any
+read of an unused row poisons the output.
+
+The named workloads mirror the model shapes the pages discuss: a 16-head /
+4-group toy example, Llama-3-8B (32 query heads, 8 KV heads, d = 128),
+Llama-2/3-70B (64 query heads, 8 KV heads), a 128K-token context, and a
+4096-token causal prefill.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str               # "decode" or "prefill"
+    B: int
+    H: int
+    K: int
+    d: int
+    dtype: str              # "f32" or "bf16"
+    L: int = 0              # uniform cached length (decode) or S (prefill)
+    ragged: tuple | None = None   # (lo, hi) inclusive for ragged decode
+    q_scale: float = 1.0
+    append: bool = False    # decode step preceded by one cache append
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "decode_tiny_f32": Workload(
+        "decode_tiny_f32", "decode", B=1, H=16, K=4, d=64, dtype="f32", L=256,
+        note="16 query heads in 4 groups, fp32; also run with K=16 (MHA) and K=1 (MQA)"),
+    "decode_llama3_8b": Workload(
+        "decode_llama3_8b", "decode", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
+        append=True, note="Llama-3-8B-shaped layer, 8192 cached tokens + 1 appended"),
+    "decode_70b_ragged": Workload(
+        "decode_70b_ragged", "decode", B=64, H=64, K=8, d=128, dtype="bf16",
+        ragged=(512, 4096), note="Llama-2/3-70B-shaped layer, lengths U{512..4096}"),
+    "decode_long_131k": Workload(
+        "decode_long_131k", "decode", B=4, H=32, K=8, d=128, dtype="bf16", L=131072,
+        q_scale=2.0, note="131072-token context, q scaled by 2"),
+    "prefill_causal_4k": Workload(
+        "prefill_causal_4k", "prefill", B=2, H=64, K=8, d=128, dtype="bf16", L=4096,
+        note="causal prefill, S=4096, 64 query heads over 8 KV heads"),
+}
+
+
+def _nan_tail(cache: torch.Tensor, lens: torch.Tensor) -> None:
+    for b in range(cache.shape[0]):
+        cache[b, :, int(lens[b]):, :] = float("nan")
+
+
+def decode_inputs(B: int, H: int, K: int, d: int, dtype: str, seed: int = 0,
+                  L: int | None = None, lens=None, ragged: tuple | None = None,
+                  q_scale: float = 1.0, s_max: int | None = None,
+                  nan_tail: bool = True) -> dict:
+    """Draw one decode batch (CPU tensors).
+
+    Exactly one of ``L`` (every sequence at L), ``lens`` (explicit list) or
+    ``ragged`` ((lo, hi) inclusive, drawn first) gives the cached lengths.
+    ``s_max`` defaults to max(lens) + 1 so that one append always fits.
+    """
+    dt = _DT[dtype]
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    if ragged is not None:
+        seq = torch.randint(int(ragged[0]), int(ragged[1]) + 1, (B,), generator=g)
+    elif lens is not None:
+        seq = torch.as_tensor(list(lens), dtype=torch.int64)
+    else:
+        seq = torch.full((B,), int(L), dtype=torch.int64)
+    if seq.numel() != B:
+        raise ValueError("lens must have B entries")
+    smax = int(seq.max().item()) + 1 if s_max is None else int(s_max)
+    if int(seq.max().item()) > smax:
+        raise ValueError("s_max smaller than a length")
+    q = (torch.randn((B, H, d), generator=g) * float(q_scale)).to(dt)
+    kc = torch.empty((B, K, smax, d), dtype=dt)
+    vc = torch.empty((B, K, smax, d), dtype=dt)
+    for b in range(B):
+        kc[b] = torch.randn((K, smax, d), generator=g).to(dt)
+    for b in range(B):
+        vc[b] = torch.randn((K, smax, d), generator=g).to(dt)
+    k_new = torch.randn((B, K, d), generator=g).to(dt)
+    v_new = torch.randn((B, K, d), generator=g).to(dt)
+    if nan_tail:
+        _nan_tail(kc, seq)
+        _nan_tail(vc, seq)
+    return {"q": q, "k_cache": kc, "v_cache": vc, "k_new": k_new, "v_new": v_new,
+            "seq_lens": seq.to(torch.int32), "S_max": smax, "seed": int(seed)}
+
+
+def prefill_inputs(B: int, H: int, K: int, S: int, d: int, dtype: str, seed: int = 0,
+                   s_max: int | None = None) -> dict:
+    """Draw one causal-prefill batch: q [B,H,S,d], k/v [B,K,S_max,d] (CPU).
+
+    Rows [S, S_max) of k and v, if any, are NaN and must never be read."""
+    dt = _DT[dtype]
+    smax = S if s_max is None else int(s_max)
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = torch.randn((B, H, S, d), generator=g).to(dt)
+    k = torch.full((B, K, smax, d), float("nan"), dtype=dt)
+    v = torch.full((B, K, smax, d), float("nan"), dtype=dt)
+    k[:, :, :S] = torch.randn((B, K, S, d), generator=g).to(dt)
+    v[:, :, :S] = torch.randn((B, K, S, d), generator=g).to(dt)
+    return {"q": q, "k": k, "v": v, "S_max": smax, "seed": int(seed)}
+
+
+def meanpool_inputs(outer: int, H: int, inner: int, dtype: str, seed: int = 0) -> torch.Tensor:
+    """Draw a [outer, H, inner] weight-like tensor (CPU)."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    return torch.randn((outer, H, inner), generator=g).to(_DT[dtype])
+
+
+def workload_inputs(w: Workload, seed: int = 0, s_max: int | None = None) -> dict:
+    """Inputs of a named workload."""
+    if w.kind == "prefill":
+        return prefill_inputs(w.B, w.H, w.K, w.L, w.d, w.dtype, seed=seed, s_max=s_max)
+    if w.ragged is not None:
+        return decode_inputs(w.B, w.H, w.K, w.d, w.dtype, seed=seed, ragged=w.ragged,
+                             q_scale=w.q_scale, s_max=s_max)
+    return decode_inputs(w.B, w.H, w.K, w.d, w.dtype, seed=seed, L=w.L,
+                         q_scale=w.q_scale, s_max=s_max)

@@ -1,0 +1,27 @@
+"""CPU oracle for grouped-query attention over a KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) imports, calls or links anything in this package; only
+the test-suite, the smoke check and the CPU-baseline leg of the benchmark do.
+
+It is a plain, slow, obviously-correct float64 NumPy restatement of what the
+hot path computes, written from the pages' description of the method:
+
+* ``gqa_oracle``  -- the definitions (decode, causal prefill, cache append,
+  mean-pool conversion, KV-cache byte count), vectorised with NumPy.
+* ``bruteforce``  -- the same definitions as pure-Python scalar loops, for
+  tiny inputs only; it derives the query-head -> KV-head grouping from the
+  page's 1-based group formula independently of ``gqa_oracle``.
+
+The two modules share no code with each other beyond the standard library
+and NumPy, and none with the GPU path.
+"""
+from .gqa_oracle import (  # noqa: F401
+    decode_ref,
+    decode_weights_ref,
+    prefill_causal_ref,
+    kv_append_ref,
+    meanpool_convert_ref,
+    kv_cache_bytes,
+    kv_head_of,
+)

@@ -1,0 +1,212 @@
+"""Float64 NumPy oracle for grouped-query attention (GQA) over a KV cache.
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
+baseline of the benchmark, never by the product path.
+
+Sources (web pages; cited by host, title and section heading):
+
+* [CAI]  compassingai.com, concept page "分組查詢注意力" (Grouped-Query
+  Attention), sections "技術原理" (technical principle) and "關鍵引數"
+  (key parameters).
+* [PHY]  pinghaoyang.com.cn/aigc/posts/gqa, "GQA 完全拆解", sections
+  "解码推理的内存账本" (the decode memory ledger), "MQA：一次性把 KV 头砍到只剩一个"
+  (MQA), "GQA：插值在 MHA 与 MQA 之间的分组共享" (GQA as interpolation),
+  "Uptraining：把现成 MHA 检查点改造成 GQA" (uptraining / mean pooling),
+  "主流模型里的 GQA：KV 缓存账本" (KV ledger of mainstream models) and
+  "工程实现：权重布局、repeat 与 Kernel 融合" (engineering).
+* [CSDN] aicoding.csdn.net, "LLaMa3与DeepSeek采用的GQA技术", section
+  "2. KV Cache的数学本质与工程挑战" (the mathematics of the KV cache).
+
+Notation: B batch, H query heads, K KV heads, G = H / K query heads per KV
+head, d head dimension, S_max cache capacity, L_b valid length of sequence b.
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes of the repository):
+
+* Query head h uses KV head floor(h / G): the groups are consecutive runs of
+  G query heads ([PHY] GQA section gives the 1-based range of group g; [CAI]
+  technical principle reshapes [.., H, d] into [.., K, H/K, d]).
+* Decode attends over cache rows [0, L_b) and the new token's row is
+  appended *before* attending, so that one decode step equals the last row
+  of causal attention ([PHY] memory ledger: the step-t query meets keys 1..t).
+* L_b = 0 gives a zero output row; append into a full cache writes nothing.
+* The scale is an input (the pages use 1/sqrt(d_k)); callers pass the
+  float32 value and the oracle uses it exactly.
+* The causal mask keeps key j for query i iff j <= i (diagonal included).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def kv_head_of(h: int, H: int, K: int) -> int:
+    """KV head shared by query head ``h`` (0-based).
+
+    [PHY] GQA section: group g (1-based) holds the consecutive query heads
+    (g-1)*H/K + 1 .. g*H/K, i.e. in 0-based terms head h belongs to group
+    floor(h / (H/K)).
+    """
+    if H % K != 0:
+        raise ValueError("H must be divisible by K")
+    return h // (H // K)
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis; subtracting the row max changes nothing
+    mathematically and keeps exp() finite."""
+    s = s - s.max(axis=-1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def decode_weights_ref(q, k_cache, seq_lens, scale) -> list:
+    """Attention weights of one decode step, per (b, h): a float64 vector of
+    length L_b that is softmax(scale * q[b,h] . k_cache[b, kv(h), j]) over
+    j in [0, L_b).
+
+    [CSDN] section 2 (scores = q k^T / sqrt(d_k), then softmax) applied per
+    group as in [CAI] technical principle.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, d = q.shape
+    K = k_cache.shape[1]
+    G = H // K
+    w = []
+    for b in range(B):
+        L = int(seq_lens[b])
+        row = []
+        for h in range(H):
+            if L == 0:
+                row.append(np.zeros(0))
+                continue
+            kc = np.asarray(k_cache[b, h // G, :L, :], dtype=np.float64)
+            row.append(_softmax_rows(float(scale) * (kc @ q[b, h])))
+        w.append(row)
+    return w
+
+
+def decode_ref(q, k_cache, v_cache, seq_lens, scale) -> np.ndarray:
+    """One GQA decode step: out[b, h] = sum_j p_j * V[b, kv(h), j] with
+    p = softmax_j(scale * q[b, h] . K[b, kv(h), j]), j in [0, L_b).
+
+    q        [B, H, d]        (any real dtype; converted to float64)
+    k_cache  [B, K, S_max, d] (rows >= L_b are never read)
+    v_cache  [B, K, S_max, d]
+    seq_lens [B] integers, 0 <= L_b <= S_max
+    returns  [B, H, d] float64; a row with L_b = 0 is zero.
+
+    Follows [CAI] technical principle (per group g the G query heads attend
+    to the one shared K_g, V_g with softmax(Q_g K_g^T / sqrt(d_k)) V_g),
+    [PHY] memory ledger (the step-t query meets all cached rows) and [CSDN]
+    section 2 (scores, softmax, weighted sum of cached values).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, d = q.shape
+    Bk, K, S_max, dk = k_cache.shape
+    if Bk != B or dk != d or H % K != 0:
+        raise ValueError("shape mismatch")
+    G = H // K
+    out = np.zeros((B, H, d), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if not 0 <= L <= S_max:
+            raise ValueError("seq_lens out of range")
+        if L == 0:
+            continue
+        for k in range(K):
+            Qg = q[b, k * G:(k + 1) * G, :]                          # [G, d]
+            Kc = np.asarray(k_cache[b, k, :L, :], dtype=np.float64)  # [L, d]
+            Vc = np.asarray(v_cache[b, k, :L, :], dtype=np.float64)  # [L, d]
+            p = _softmax_rows(float(scale) * (Qg @ Kc.T))            # [G, L]
+            out[b, k * G:(k + 1) * G, :] = p @ Vc
+    return out
+
+
+def prefill_causal_ref(q, k, v, scale, rows=None) -> np.ndarray:
+    """Causal GQA attention over a whole prefix (prefill).
+
+    out[b, h, i] = sum_{j <= i} softmax_j(scale * q[b,h,i] . k[b,kv(h),j]) v[b,kv(h),j]
+
+    q     [B, H, S, d]
+    k, v  [B, K, S_kv, d] with S_kv >= S; only rows [0, S) are used
+    rows  optional sequence of query positions to evaluate (default: all S)
+    returns [B, H, len(rows), d] float64
+
+    [PHY] memory ledger (prefill processes the whole prefix in parallel; row
+    i is exactly what decode step i computes), [CAI] technical principle for
+    the grouping; the lower-triangular mask keeps the diagonal.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, S, d = q.shape
+    K = k.shape[1]
+    if H % K != 0 or k.shape[2] < S:
+        raise ValueError("shape mismatch")
+    G = H // K
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, H, len(rows), d), dtype=np.float64)
+    keep = np.arange(S)[None, :] <= rows[:, None]                    # [R, S]
+    for b in range(B):
+        for g in range(K):
+            Kc = np.asarray(k[b, g, :S, :], dtype=np.float64)           # [S, d]
+            Vc = np.asarray(v[b, g, :S, :], dtype=np.float64)
+            for h in range(g * G, (g + 1) * G):
+                s = float(scale) * (q[b, h, rows, :] @ Kc.T)            # [R, S]
+                s = np.where(keep, s, -np.inf)
+                out[b, h] = _softmax_rows(s) @ Vc
+    return out
+
+
+def kv_append_ref(k_new, v_new, k_cache, v_cache, seq_lens):
+    """Append one token's K and V rows per (b, kv head) at position L_b.
+
+    k_new, v_new [B, K, d]; caches [B, K, S_max, d]; seq_lens [B].
+    Returns new (k_cache, v_cache, seq_lens) copies: rows L_b of every (b, k)
+    are replaced bit-for-bit by the new rows and L_b becomes L_b + 1; a
+    sequence whose cache is full (L_b == S_max) is left unchanged.
+
+    Works on any element dtype (pass integer views to compare bits).
+    [CAI] technical principle (each generated token writes a [batch, 1, K,
+    d_k] row), [PHY] memory ledger (the new K, V row is appended each step).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    sl = np.array(seq_lens, copy=True)
+    S_max = kc.shape[2]
+    for b in range(kc.shape[0]):
+        L = int(sl[b])
+        if L >= S_max:
+            continue
+        kc[b, :, L, :] = k_new[b]
+        vc[b, :, L, :] = v_new[b]
+        sl[b] = L + 1
+    return kc, vc, sl
+
+
+def meanpool_convert_ref(src, K: int) -> np.ndarray:
+    """Mean-pool H per-head blocks into K group blocks.
+
+    src [outer, H, inner] -> [outer, K, inner] float64 with
+    dst[o, g, i] = (1/G) * sum_{r < G} src[o, g*G + r, i].
+
+    [PHY] uptraining section (the new key projection of group g is the mean
+    of the original key-head projections in that group; the same for values)
+    and [CAI] technical principle (arithmetic mean over the H/K heads of a
+    group; query projections unchanged).
+    """
+    src = np.asarray(src, dtype=np.float64)
+    outer, H, inner = src.shape
+    if H % K != 0:
+        raise ValueError("H must be divisible by K")
+    G = H // K
+    return src.reshape(outer, K, G, inner).mean(axis=2)
+
+
+def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int,
+                   elem_bytes: int, tokens: int = 1) -> int:
+    """KV-cache size in bytes: 2 * layers * kv_heads * head_dim * bytes per
+    element * tokens (one K and one V row per layer, KV head and token).
+
+    [PHY] memory ledger and GQA section (S_KV = 2 L G d_k B, with G the number
+    of KV heads in that page's notation).
+    """
+    return 2 * int(layers) * int(kv_heads) * int(head_dim) * int(elem_bytes) * int(tokens)

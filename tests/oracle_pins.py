@@ -1,0 +1,359 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Every ``check_*`` takes the oracle module ``O`` as its argument (so that the
+mutation tests can hand it a copy with a planted mistake) and raises
+AssertionError (or any exception) when the oracle disagrees with:
+
+* numbers the pages print (KV-cache bytes, tests/golden/kv_cache_bytes.json);
+* a pure-Python brute force written from the 1-based group formula;
+* torch's fp64 CPU scaled_dot_product_attention (a library special case:
+  pinghaoyang.com.cn "GQA 完全拆解", section 工程实现 (engineering), names
+  PyTorch SDPA with fewer KV heads than query heads);
+* closed forms (softmax of known scores, one cached row, zero query, constant
+  values, prefix means, identical heads under mean pooling);
+* invariants the pages state (K = H is MHA and K = 1 is MQA; expanding each
+  KV head G times and running MHA gives GQA; incremental decode equals the
+  last row of causal attention; weight pooling commutes with projection).
+"""
+from __future__ import annotations
+
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import torch
+
+from oracle import bruteforce as BF
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _rand_decode(seed, B, H, K, d, lens, s_max=None, nan_tail=True):
+    r = _rng(seed)
+    s_max = s_max or (max(lens) + 1)
+    q = r.standard_normal((B, H, d))
+    kc = r.standard_normal((B, K, s_max, d))
+    vc = r.standard_normal((B, K, s_max, d))
+    if nan_tail:
+        for b, L in enumerate(lens):
+            kc[b, :, L:] = np.nan
+            vc[b, :, L:] = np.nan
+    return q, kc, vc, np.array(lens)
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# --------------------------------------------------------------------------
+# numbers printed on the pages
+# --------------------------------------------------------------------------
+def check_kv_bytes_golden(O):
+    data = json.loads((GOLDEN / "kv_cache_bytes.json").read_text())
+    for e in data["entries"]:
+        got = O.kv_cache_bytes(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"], e["tokens"])
+        if "exact_bytes" in e:
+            assert got == e["exact_bytes"], (e["what"], got)
+        else:
+            val = round(got / e["unit_bytes"], e["round_to"])
+            assert val == e["approx"], (e["what"], got, val)
+    for r in data["ratios"]:
+        full = O.kv_cache_bytes(80, r["mha_kv_heads"], 128, 2, 2048)
+        grp = O.kv_cache_bytes(80, r["gqa_kv_heads"], 128, 2, 2048)
+        assert grp / full == r["ratio"], r["what"]
+
+
+def check_kv_head_map(O):
+    for H, K in [(8, 2), (16, 4), (6, 3), (56, 8), (71, 1), (5, 5)]:
+        for h in range(H):
+            assert O.kv_head_of(h, H, K) == BF.group_of_head(h + 1, H, K) - 1, (H, K, h)
+
+
+# --------------------------------------------------------------------------
+# brute force on tiny inputs
+# --------------------------------------------------------------------------
+def check_bruteforce_decode(O):
+    for seed, (B, H, K, d, lens) in enumerate([
+            (2, 6, 3, 4, [5, 1]), (1, 8, 2, 3, [7]), (2, 4, 4, 5, [3, 0]),
+            (1, 5, 1, 4, [6]), (2, 9, 3, 2, [2, 9])]):
+        q, kc, vc, sl = _rand_decode(100 + seed, B, H, K, d, lens)
+        ref = BF.decode_bruteforce(q.tolist(), kc.tolist(), vc.tolist(), sl.tolist(), 0.37)
+        _close(O.decode_ref(q, kc, vc, sl, 0.37), ref, 1e-13, f"decode brute force {seed}")
+
+
+def check_bruteforce_prefill(O):
+    for seed, (B, H, K, S, d) in enumerate([(1, 4, 2, 5, 3), (2, 6, 3, 4, 2), (1, 3, 1, 6, 4)]):
+        r = _rng(200 + seed)
+        q = r.standard_normal((B, H, S, d))
+        k = r.standard_normal((B, K, S + 2, d))
+        v = r.standard_normal((B, K, S + 2, d))
+        k[:, :, S:] = np.nan
+        v[:, :, S:] = np.nan
+        ref = BF.prefill_bruteforce(q.tolist(), k[:, :, :S].tolist(), v[:, :, :S].tolist(), 0.6)
+        _close(O.prefill_causal_ref(q, k, v, 0.6), ref, 1e-13, f"prefill brute force {seed}")
+
+
+def check_bruteforce_meanpool(O):
+    for seed, (outer, H, K, inner) in enumerate([(2, 6, 3, 5), (1, 8, 2, 3), (3, 4, 4, 2), (1, 7, 1, 4)]):
+        src = _rng(300 + seed).standard_normal((outer, H, inner))
+        _close(O.meanpool_convert_ref(src, K), BF.meanpool_bruteforce(src.tolist(), K), 1e-14,
+               f"meanpool brute force {seed}")
+
+
+# --------------------------------------------------------------------------
+# library special case: torch fp64 CPU SDPA
+# --------------------------------------------------------------------------
+def _sdpa(q, k, v, scale, causal=False, gqa=True):
+    F = torch.nn.functional
+    return F.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        is_causal=causal, scale=scale, enable_gqa=gqa).numpy()
+
+
+def check_sdpa_decode(O):
+    for seed, (B, H, K, d, lens) in enumerate([(3, 32, 8, 16, [40, 1, 17]), (2, 12, 4, 8, [9, 33])]):
+        q, kc, vc, sl = _rand_decode(400 + seed, B, H, K, d, lens)
+        got = O.decode_ref(q, kc, vc, sl, 0.25)
+        for b, L in enumerate(lens):
+            ref = _sdpa(q[b][None, :, None, :], kc[b][None, :, :L], vc[b][None, :, :L], 0.25)
+            _close(got[b], ref[0, :, 0, :], 1e-12, f"SDPA decode b={b}")
+
+
+def check_sdpa_prefill(O):
+    r = _rng(500)
+    B, H, K, S, d = 2, 8, 2, 24, 8
+    q = r.standard_normal((B, H, S, d))
+    k = r.standard_normal((B, K, S, d))
+    v = r.standard_normal((B, K, S, d))
+    _close(O.prefill_causal_ref(q, k, v, 0.3), _sdpa(q, k, v, 0.3, causal=True), 1e-12, "SDPA prefill")
+    rows = [0, 5, 23]
+    _close(O.prefill_causal_ref(q, k, v, 0.3, rows=rows),
+           _sdpa(q, k, v, 0.3, causal=True)[:, :, rows], 1e-12, "SDPA prefill rows")
+
+
+def check_mha_special_case(O):
+    """K = H: every query head has its own KV head (plain multi-head)."""
+    q, kc, vc, sl = _rand_decode(600, 2, 6, 6, 8, [11, 4])
+    got = O.decode_ref(q, kc, vc, sl, 0.5)
+    for b, L in enumerate(sl):
+        ref = _sdpa(q[b][None, :, None, :], kc[b][None, :, :L], vc[b][None, :, :L], 0.5, gqa=False)
+        _close(got[b], ref[0, :, 0, :], 1e-12, "MHA special case")
+
+
+def check_mqa_special_case(O):
+    """K = 1: all query heads share one K/V head, which has no head axis
+    (pinghaoyang.com.cn 'GQA 完全拆解', MQA section: [b, n, d_k])."""
+    q, kc, vc, sl = _rand_decode(700, 2, 7, 1, 8, [13, 2])
+    got = O.decode_ref(q, kc, vc, sl, 0.5)
+    for b, L in enumerate(sl):
+        kk = np.broadcast_to(kc[b, 0, :L], (7, L, 8)).copy()[None]
+        vv = np.broadcast_to(vc[b, 0, :L], (7, L, 8)).copy()[None]
+        ref = _sdpa(q[b][None, :, None, :], kk, vv, 0.5, gqa=False)
+        _close(got[b], ref[0, :, 0, :], 1e-12, "MQA special case")
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+def check_expanded_kv_equivalence(O):
+    """GQA equals MHA on KV heads materialised G times each (the repeat_kv
+    route described in the engineering section), with explicit copies."""
+    B, H, K, d = 2, 12, 3, 8
+    q, kc, vc, sl = _rand_decode(800, B, H, K, d, [10, 6])
+    G = H // K
+    kx = np.empty((B, H) + kc.shape[2:])
+    vx = np.empty((B, H) + vc.shape[2:])
+    for h in range(H):
+        kx[:, h] = kc[:, h // G]
+        vx[:, h] = vc[:, h // G]
+    _close(O.decode_ref(q, kc, vc, sl, 0.4), O.decode_ref(q, kx, vx, sl, 0.4), 1e-13,
+           "expanded-KV equivalence")
+
+
+def check_identical_heads_meanpool(O):
+    """An MHA cache whose heads are identical within each group gives the
+    same outputs as GQA on the mean-pooled cache, and mean pooling returns
+    that shared head exactly."""
+    B, H, K, d, L = 2, 8, 2, 6, 9
+    r = _rng(900)
+    base_k = r.standard_normal((B, K, L, d))
+    base_v = r.standard_normal((B, K, L, d))
+    G = H // K
+    kx = np.repeat(base_k, G, axis=1)
+    vx = np.repeat(base_v, G, axis=1)
+    q = r.standard_normal((B, H, d))
+    pooled_k = O.meanpool_convert_ref(kx.transpose(0, 2, 1, 3).reshape(B * L, H, d), K)
+    pooled_k = pooled_k.reshape(B, L, K, d).transpose(0, 2, 1, 3)
+    pooled_v = O.meanpool_convert_ref(vx.transpose(0, 2, 1, 3).reshape(B * L, H, d), K)
+    pooled_v = pooled_v.reshape(B, L, K, d).transpose(0, 2, 1, 3)
+    assert np.array_equal(pooled_k, base_k) and np.array_equal(pooled_v, base_v)
+    sl = np.array([L, L - 3])
+    _close(O.decode_ref(q, pooled_k, pooled_v, sl, 0.3), O.decode_ref(q, kx, vx, sl, 0.3), 1e-13,
+           "identical heads vs MHA")
+
+
+def check_softmax_closed_form(O):
+    """Known scores: with q = e0, k_j = (ln(j+1)/scale) e0 the scores are
+    ln(j+1), so p_j = (j+1) / sum(1..L) exactly; one-hot value rows make the
+    output equal to p, which must also sum to one."""
+    L, d, scale = 7, 8, 0.125
+    q = np.zeros((1, 2, d))
+    q[0, :, 0] = 1.0
+    kc = np.zeros((1, 1, L, d))
+    vc = np.zeros((1, 1, L, d))
+    for j in range(L):
+        kc[0, 0, j, 0] = math.log(j + 1) / scale
+        vc[0, 0, j, j] = 1.0
+    want = np.array([(j + 1) / (L * (L + 1) / 2) for j in range(L)] + [0.0] * (d - L))
+    out = O.decode_ref(q, kc, vc, [L], scale)
+    _close(out[0, 0], want, 1e-15, "closed-form softmax")
+    _close(out[0, 1], want, 1e-15, "closed-form softmax head 1")
+    w = O.decode_weights_ref(q, kc, [L], scale)
+    _close(w[0][0], want[:L], 1e-15, "weights closed form")
+    assert abs(math.fsum(w[0][1]) - 1.0) < 1e-15
+
+
+def check_weights_sum_to_one(O):
+    q, kc, vc, sl = _rand_decode(1000, 2, 8, 2, 8, [12, 3])
+    for row in O.decode_weights_ref(q, kc, sl, 0.7):
+        for p in row:
+            assert np.all(p >= 0) and abs(math.fsum(p) - 1.0) < 1e-14
+
+
+def check_weights_sdpa(O):
+    """The weights equal SDPA's output when the value rows are the identity."""
+    q, kc, vc, sl = _rand_decode(1050, 2, 8, 4, 6, [5, 3])
+    w = O.decode_weights_ref(q, kc, sl, 0.6)
+    for b, L in enumerate(sl):
+        eye = np.broadcast_to(np.eye(L), (4, L, L)).copy()[None]
+        ref = _sdpa(q[b][None, :, None, :], kc[b][None, :, :L], eye, 0.6)[0, :, 0, :]
+        _close(np.stack(w[b]), ref, 1e-13, "weights vs SDPA")
+
+
+def check_single_row(O):
+    """L = 1: the softmax has one term, so the output is that value row exactly."""
+    q, kc, vc, sl = _rand_decode(1100, 3, 8, 4, 8, [1, 1, 1])
+    out = O.decode_ref(q, kc, vc, sl, 0.3)
+    for b in range(3):
+        for h in range(8):
+            assert np.array_equal(out[b, h], vc[b, h // 2, 0])
+
+
+def check_zero_query_mean(O):
+    """q = 0: all scores equal, so the output is the mean of rows [0, L)."""
+    q, kc, vc, sl = _rand_decode(1200, 2, 6, 3, 5, [17, 4], s_max=20)
+    q[:] = 0.0
+    out = O.decode_ref(q, kc, vc, sl, 0.9)
+    for b, L in enumerate(sl):
+        for h in range(6):
+            _close(out[b, h], vc[b, h // 2, :L].mean(axis=0), 1e-14, "zero-query mean")
+
+
+def check_constant_values(O):
+    q, kc, vc, sl = _rand_decode(1300, 2, 4, 2, 6, [9, 5])
+    c = _rng(1301).standard_normal(6)
+    for b, L in enumerate(sl):
+        vc[b, :, :L] = c
+    out = O.decode_ref(q, kc, vc, sl, 1.1)
+    _close(out, np.broadcast_to(c, out.shape), 1e-14, "constant values")
+
+
+def check_empty_length(O):
+    q, kc, vc, sl = _rand_decode(1400, 2, 4, 2, 4, [0, 3])
+    out = O.decode_ref(q, kc, vc, sl, 0.5)
+    assert np.array_equal(out[0], np.zeros((4, 4))) and np.all(np.isfinite(out[1]))
+
+
+def check_incremental_equals_causal(O):
+    """Appending token i and then decoding it reproduces causal row i."""
+    r = _rng(1500)
+    B, H, K, S, d = 2, 6, 2, 9, 4
+    q = r.standard_normal((B, H, S, d))
+    k = r.standard_normal((B, K, S, d))
+    v = r.standard_normal((B, K, S, d))
+    full = O.prefill_causal_ref(q, k, v, 0.45)
+    kc = np.full((B, K, S, d), np.nan)
+    vc = np.full((B, K, S, d), np.nan)
+    sl = np.zeros(B, dtype=np.int64)
+    for i in range(S):
+        kc, vc, sl = O.kv_append_ref(k[:, :, i], v[:, :, i], kc, vc, sl)
+        assert list(sl) == [i + 1] * B
+        _close(O.decode_ref(q[:, :, i], kc, vc, sl, 0.45), full[:, :, i], 1e-13,
+               f"incremental row {i}")
+
+
+def check_prefill_closed_forms(O):
+    r = _rng(1600)
+    B, H, K, S, d = 1, 4, 2, 8, 3
+    q = r.standard_normal((B, H, S, d))
+    k = r.standard_normal((B, K, S, d))
+    v = r.standard_normal((B, K, S, d))
+    out = O.prefill_causal_ref(q, k, v, 0.8)
+    for h in range(H):
+        assert np.array_equal(out[0, h, 0], v[0, h // 2, 0]), "row 0 must equal V_0"
+    out0 = O.prefill_causal_ref(np.zeros_like(q), k, v, 0.8)
+    for h in range(H):
+        for i in range(S):
+            _close(out0[0, h, i], v[0, h // 2, :i + 1].mean(axis=0), 1e-14, "prefix mean")
+
+
+def check_append_semantics(O):
+    r = _rng(1700)
+    B, K, S_max, d = 3, 2, 5, 4
+    kc = r.integers(-30000, 30000, (B, K, S_max, d), dtype=np.int16)
+    vc = r.integers(-30000, 30000, (B, K, S_max, d), dtype=np.int16)
+    kn = r.integers(-30000, 30000, (B, K, d), dtype=np.int16)
+    vn = r.integers(-30000, 30000, (B, K, d), dtype=np.int16)
+    sl = np.array([0, 3, S_max])
+    k2, v2, s2 = O.kv_append_ref(kn, vn, kc, vc, sl)
+    assert list(s2) == [1, 4, S_max]
+    for b, L in enumerate(sl):
+        for pos in range(S_max):
+            if pos == L:
+                assert np.array_equal(k2[b, :, pos], kn[b]) and np.array_equal(v2[b, :, pos], vn[b])
+            else:
+                assert np.array_equal(k2[b, :, pos], kc[b, :, pos])
+                assert np.array_equal(v2[b, :, pos], vc[b, :, pos])
+    assert list(sl) == [0, 3, S_max], "inputs must not be modified"
+
+
+def check_meanpool_linearity(O):
+    """Pooling the per-head key projections W_K [H, d_k, d_model] and then
+    projecting X equals projecting X with every head and pooling the results
+    (the einsum 'bd,hdk->bhk' form of the MQA section)."""
+    r = _rng(1800)
+    H, K, dk, dm, n = 8, 2, 5, 7, 3
+    W = r.standard_normal((H, dm, dk))
+    X = r.standard_normal((n, dm))
+    per_head = np.einsum("bd,hdk->bhk", X, W)                  # [n, H, dk]
+    pooled_after = O.meanpool_convert_ref(per_head, K)          # [n, K, dk]
+    Wp = O.meanpool_convert_ref(W.reshape(1, H, dm * dk), K).reshape(K, dm, dk)
+    pooled_before = np.einsum("bd,hdk->bhk", X, Wp)
+    _close(pooled_after, pooled_before, 1e-12, "meanpool linearity")
+
+
+def check_meanpool_identity_g1(O):
+    src = _rng(1900).standard_normal((3, 5, 4))
+    assert np.array_equal(O.meanpool_convert_ref(src, 5), src)
+
+
+ALL_CHECKS = [
+    check_kv_bytes_golden, check_kv_head_map,
+    check_bruteforce_decode, check_bruteforce_prefill, check_bruteforce_meanpool,
+    check_sdpa_decode, check_sdpa_prefill, check_mha_special_case, check_mqa_special_case,
+    check_expanded_kv_equivalence, check_identical_heads_meanpool,
+    check_softmax_closed_form, check_weights_sum_to_one, check_weights_sdpa, check_single_row,
+    check_zero_query_mean, check_constant_values, check_empty_length,
+    check_incremental_equals_causal, check_prefill_closed_forms, check_append_semantics,
+    check_meanpool_linearity, check_meanpool_identity_g1,
+]

@@ -1,0 +1,80 @@
+"""Each plausible mistake planted in a copy of the oracle must fail a pin.
+
+The mistakes are planted on the CPU, in a private copy of the oracle's source
+text; the real oracle module is never modified.  A mutation "fails a pin"
+when at least one check raises.
+"""
+import types
+from pathlib import Path
+
+import pytest
+
+from oracle_pins import ALL_CHECKS
+
+SRC = (Path(__file__).resolve().parent.parent / "oracle" / "gqa_oracle.py").read_text()
+
+MUTATIONS = {
+    "interleaved_group_map": [
+        ("Qg = q[b, k * G:(k + 1) * G, :]", "Qg = q[b, k::K, :]"),
+        ("out[b, k * G:(k + 1) * G, :] = p @ Vc", "out[b, k::K, :] = p @ Vc")],
+    "kv_head_of_modulo": [("return h // (H // K)", "return h % K")],
+    "weights_group_map": [("k_cache[b, h // G, :L, :]", "k_cache[b, h % K, :L, :]")],
+    "decode_length_short": [("k_cache[b, k, :L, :]", "k_cache[b, k, :max(L - 1, 1), :]"),
+                            ("v_cache[b, k, :L, :]", "v_cache[b, k, :max(L - 1, 1), :]")],
+    "decode_length_long": [("k_cache[b, k, :L, :]", "k_cache[b, k, :L + 1, :]"),
+                           ("v_cache[b, k, :L, :]", "v_cache[b, k, :L + 1, :]")],
+    "decode_scale_dropped": [("p = _softmax_rows(float(scale) * (Qg @ Kc.T))",
+                              "p = _softmax_rows(Qg @ Kc.T)")],
+    "decode_scale_sqrt": [("p = _softmax_rows(float(scale) * (Qg @ Kc.T))",
+                           "p = _softmax_rows(float(scale) ** 0.5 * (Qg @ Kc.T))")],
+    "decode_values_are_keys": [("out[b, k * G:(k + 1) * G, :] = p @ Vc",
+                                "out[b, k * G:(k + 1) * G, :] = p @ Kc")],
+    "softmax_wrong_axis": [("s = s - s.max(axis=-1, keepdims=True)", "s = s - s.max(axis=0, keepdims=True)"),
+                           ("return e / e.sum(axis=-1, keepdims=True)", "return e / e.sum(axis=0, keepdims=True)")],
+    "softmax_unnormalised": [("return e / e.sum(axis=-1, keepdims=True)", "return e")],
+    "softmax_sign_flip": [("e = np.exp(s)", "e = np.exp(-s)")],
+    "causal_strict": [("keep = np.arange(S)[None, :] <= rows[:, None]",
+                       "keep = np.arange(S)[None, :] < rows[:, None]")],
+    "causal_reversed": [("keep = np.arange(S)[None, :] <= rows[:, None]",
+                         "keep = np.arange(S)[None, :] >= rows[:, None]")],
+    "causal_no_mask": [("s = np.where(keep, s, -np.inf)", "s = s")],
+    "prefill_group_map": [("for h in range(g * G, (g + 1) * G):", "for h in range(g, H, K):")],
+    "prefill_values_are_keys": [("out[b, h] = _softmax_rows(s) @ Vc", "out[b, h] = _softmax_rows(s) @ Kc")],
+    "prefill_scale_dropped": [("s = float(scale) * (q[b, h, rows, :] @ Kc.T)", "s = q[b, h, rows, :] @ Kc.T")],
+    "meanpool_interleaved": [("return src.reshape(outer, K, G, inner).mean(axis=2)",
+                              "return src.reshape(outer, G, K, inner).mean(axis=1)")],
+    "meanpool_first_head": [("return src.reshape(outer, K, G, inner).mean(axis=2)",
+                             "return src.reshape(outer, K, G, inner)[:, :, 0, :]")],
+    "meanpool_sum": [("return src.reshape(outer, K, G, inner).mean(axis=2)",
+                      "return src.reshape(outer, K, G, inner).sum(axis=2)")],
+    "kv_bytes_no_factor_two": [("return 2 * int(layers)", "return int(layers)")],
+    "kv_bytes_query_heads": [("return 2 * int(layers) * int(kv_heads)", "return 2 * int(layers) * int(kv_heads) * 4")],
+    "append_wrong_row": [("kc[b, :, L, :] = k_new[b]", "kc[b, :, max(L - 1, 0), :] = k_new[b]")],
+    "append_no_increment": [("sl[b] = L + 1", "sl[b] = L")],
+    "append_v_from_k": [("vc[b, :, L, :] = v_new[b]", "vc[b, :, L, :] = k_new[b]")],
+    "append_full_cache": [("if L >= S_max:\n            continue", "if L > S_max:\n            continue")],
+    "empty_length_nan": [("        if L == 0:\n            continue\n        for k in range(K):",
+                          "        for k in range(K):")],
+}
+
+
+def _mutant(edits):
+    src = SRC
+    for old, new in edits:
+        assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+        src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    mod = _mutant(MUTATIONS[name])
+    caught = []
+    for check in ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as detection
+            caught.append(f"{check.__name__}: {type(e).__name__}")
+    assert caught, f"mutation {name} passed every pin"
