@@ -1,1 +1,23 @@
+"""Grouped-query attention over a KV cache on AMD Instinct MI355X (gfx950).
 
+The computation lives in libgqa.so (hand-written HIP kernels behind the C
+ABI declared in include/gqa.h); this package is its thin ctypes binding
+(``_binding``), the in-tree build script (``build``) and the seeded
+synthetic-input generator (``inputs``).
+"""
+from ._binding import (  # noqa: F401
+    GQA_BF16,
+    GQA_F32,
+    GQAError,
+    gqa_abi_version,
+    gqa_decode,
+    gqa_decode_workspace_bytes,
+    gqa_kv_append,
+    gqa_kv_cache_bytes,
+    gqa_last_error,
+    gqa_meanpool_convert,
+    gqa_prefill_causal,
+    gqa_set_timing_events,
+    header_symbols,
+    load_library,
+)

@@ -1,0 +1,206 @@
+"""ctypes binding of libgqa (include/gqa.h), one Python function per entry point.
+
+Argument marshalling only: the functions take torch tensors that live on the
+GPU, check dtype/shape/contiguity/device, derive the integer sizes the C ABI
+wants from the shapes, and pass raw device pointers plus the current HIP
+stream.  Every step of the computation runs in the HIP kernels of libgqa.so;
+if the library is missing the functions raise instead of computing anything
+another way.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import torch
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libgqa.so"
+HEADER = PKG.parent / "include" / "gqa.h"
+
+GQA_F32, GQA_BF16 = 0, 1
+GQA_OK, GQA_ERR_INVALID, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, -1, -2, -3, -4
+
+_DTYPE_CODE = {torch.float32: GQA_F32, torch.bfloat16: GQA_BF16}
+
+_c_void_p, _c_int, _c_int64, _c_size_t, _c_float = (
+    ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float)
+
+_SIGNATURES = {
+    "gqa_abi_version": (_c_int, []),
+    "gqa_last_error": (ctypes.c_char_p, []),
+    "gqa_set_timing_events": (_c_int, [_c_void_p, _c_void_p]),
+    "gqa_kv_cache_bytes": (ctypes.c_uint64, [_c_int, _c_int, _c_int, _c_int, ctypes.c_uint64]),
+    "gqa_kv_append": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 + [_c_void_p]),
+    "gqa_decode_workspace_bytes": (_c_size_t, [_c_int] * 5),
+    "gqa_decode": (_c_int, [_c_void_p] * 6 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_prefill_causal": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_meanpool_convert": (_c_int, [_c_void_p, _c_void_p, _c_int64, _c_int, _c_int, _c_int64, _c_int, _c_void_p]),
+}
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} returned {code}: {msg}")
+        self.code = code
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared in include/gqa.h."""
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*\s]+?)\b(gqa_\w+)\s*\(", text, flags=re.M)))
+
+
+def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgqa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = Path(path)
+    if not path.exists():
+        raise RuntimeError(
+            f"{path} is missing: build it first (python -m grouped_query_kv_amd.build); "
+            "there is no other implementation to fall back on")
+    lib = ctypes.CDLL(str(path))
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int) -> None:
+    if code != GQA_OK:
+        raise GQAError(fn, code, load_library().gqa_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _need(t: torch.Tensor, name: str, ndim: int, dtypes=(torch.float32, torch.bfloat16)):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not supported")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def gqa_abi_version() -> int:
+    return load_library().gqa_abi_version()
+
+
+def gqa_last_error() -> str:
+    return load_library().gqa_last_error().decode()
+
+
+def gqa_kv_cache_bytes(layers: int, K: int, d: int, elem_bytes: int, tokens: int) -> int:
+    return int(load_library().gqa_kv_cache_bytes(layers, K, d, elem_bytes, tokens))
+
+
+def gqa_set_timing_events(begin=None, end=None) -> None:
+    """Arm (or clear, with None) the begin/end events recorded around the
+    main kernel of gqa_decode / gqa_prefill_causal on this thread."""
+    b = None if begin is None else begin.cuda_event
+    e = None if end is None else end.cuda_event
+    _check("gqa_set_timing_events", load_library().gqa_set_timing_events(b, e))
+
+
+def gqa_kv_append(k_new, v_new, k_cache, v_cache, seq_lens, stream=None) -> None:
+    """Write k_new/v_new [B,K,d] at row seq_lens[b] of the caches [B,K,S_max,d]
+    and increment seq_lens (int32 [B]), all on the GPU."""
+    _need(k_cache, "k_cache", 4)
+    B, K, S_max, d = k_cache.shape
+    for t, nm in ((v_cache, "v_cache"),):
+        _need(t, nm, 4)
+        if t.shape != k_cache.shape or t.dtype != k_cache.dtype:
+            raise ValueError("v_cache must match k_cache")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, 3)
+        if tuple(t.shape) != (B, K, d) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{nm} must be [B,K,d] of the cache dtype")
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    lib = load_library()
+    _check("gqa_kv_append", lib.gqa_kv_append(
+        k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        seq_lens.data_ptr(), B, K, S_max, d, _DTYPE_CODE[k_cache.dtype], _stream(stream)))
+
+
+def gqa_decode_workspace_bytes(B: int, H: int, K: int, max_seq_len: int, d: int) -> int:
+    return int(load_library().gqa_decode_workspace_bytes(B, H, K, max_seq_len, d))
+
+
+def gqa_decode(q, k_cache, v_cache, seq_lens, out, workspace, max_seq_len: int,
+               scale: float | None = None, stream=None) -> None:
+    """One decode step: out [B,H,d] = GQA of q [B,H,d] over rows [0, seq_lens[b])
+    of the caches [B,K,S_max,d].  workspace: uint8 GPU tensor of at least
+    gqa_decode_workspace_bytes(...) bytes."""
+    _need(q, "q", 3)
+    _need(k_cache, "k_cache", 4)
+    _need(v_cache, "v_cache", 4)
+    _need(out, "out", 3)
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    _need(workspace, "workspace", 1, (torch.uint8,))
+    B, H, d = q.shape
+    Bk, K, S_max, dk = k_cache.shape
+    if Bk != B or dk != d or v_cache.shape != k_cache.shape or tuple(out.shape) != (B, H, d):
+        raise ValueError("shape mismatch between q, caches and out")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches must share a dtype")
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    _check("gqa_decode", lib.gqa_decode(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), B, H, K, S_max, int(max_seq_len), d, float(scale),
+        _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def gqa_prefill_causal(q, k, v, out, scale: float | None = None, stream=None) -> None:
+    """Causal GQA over a prefix: q/out [B,H,S,d], k/v [B,K,S_max,d] (rows < S used)."""
+    _need(q, "q", 4, (torch.bfloat16,))
+    _need(k, "k", 4, (torch.bfloat16,))
+    _need(v, "v", 4, (torch.bfloat16,))
+    _need(out, "out", 4)
+    B, H, S, d = q.shape
+    Bk, K, S_max, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape or tuple(out.shape) != (B, H, S, d):
+        raise ValueError("shape mismatch between q, k, v and out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    _check("gqa_prefill_causal", lib.gqa_prefill_causal(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, K, S, S_max, d,
+        float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def gqa_meanpool_convert(src, dst, stream=None) -> None:
+    """dst [outer,K,inner] = mean over each group of G consecutive heads of src [outer,H,inner]."""
+    _need(src, "src", 3)
+    _need(dst, "dst", 3)
+    outer, H, inner = src.shape
+    K = dst.shape[1]
+    if dst.shape[0] != outer or dst.shape[2] != inner or dst.dtype != src.dtype:
+        raise ValueError("dst must be [outer,K,inner] of the src dtype")
+    lib = load_library()
+    _check("gqa_meanpool_convert", lib.gqa_meanpool_convert(
+        src.data_ptr(), dst.data_ptr(), outer, H, K, inner, _DTYPE_CODE[src.dtype], _stream(stream)))

@@ -1,0 +1,227 @@
+// Decode partition pass for bf16 caches, on the gfx950 matrix cores.
+//
+// What it computes (compassingai.com "分組查詢注意力", section 技術原理: the
+// G query heads of group g attend to the one shared K_g, V_g with
+// softmax(Q_g K_g^T / sqrt(d_k)) V_g): for a partition [t0, t1) of the
+// positions of sequence b and KV head k, and every query head h of the
+// group, the un-normalised online-softmax state
+//     m_h   = max_j s_hj            (s_hj = scale * log2(e) * q_h . k_j)
+//     l_h   = sum_j 2^(s_hj - m_h)
+//     acc_h = sum_j 2^(s_hj - m_h) v_j
+// which the combine pass merges across partitions.  Working in base 2 with
+// log2(e) folded into the scale gives the same softmax.
+//
+// How (pinghaoyang.com.cn "GQA 完全拆解", section 工程实现 (engineering): the
+// group's shared KV block is loaded once and reused by all its query heads):
+// one wavefront owns one partition and streams it in chunks of 32 positions.
+// Each K row is read from HBM once, straight into matrix-core operand
+// registers, and multiplies all (up to 16) query heads of the group in one
+// v_mfma_f32_16x16x32_bf16:  S^T[32 x 16] = K_chunk[32 x d] . Q_g^T[d x 16].
+// Each V row is read from HBM once, staged through LDS to be re-laid out as
+// the matrix-core operand, and then serves all heads:
+//     O[16 x d] += P[16 x 32] . V_chunk[32 x d].
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 (wave64, lane l, n = l % 16,
+// g = l / 16): A row m = n holds 8 k-values selected by g; B column n holds
+// the same 8 k-values; C/D lane l holds D[4g + i][n], i = 0..3.  Because the
+// k-index of both operands is chosen by (g, element) in the same way, any
+// relabelling of the contraction index that is applied to both operands
+// gives the same product.  This kernel uses that freedom twice:
+//   * Q.K: lane (n, g) at k-step s carries head dimensions 32s + 8g .. +7, so
+//     every K operand is one 16-byte load from a K row;
+//   * P.V: the scores come out of the first product as lane (n = head, g)
+//     holding positions {4g+i, 16+4g+i}; those eight positions are used as
+//     that lane's contraction slots, so P needs no data movement and only V
+//     is gathered (from LDS) in the same position order.
+#include "common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kChunk = 32;   // positions per inner iteration
+constexpr int kVPad = 8;     // bf16 elements of padding per LDS row
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
+    float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
+    int head_blocks, float scale_log2) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int KSTEPS = D / 32;        // contraction steps of Q.K
+  constexpr int NTILES = D / 16;        // 16-wide output tiles of P.V
+  constexpr int LANES_PER_ROW = D / 8;  // 16-byte words per V row
+  constexpr int ROWS_PER_LOAD = 64 / LANES_PER_ROW;
+  constexpr int VLOADS = kChunk / ROWS_PER_LOAD;
+
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk][D + kVPad];
+
+  const int p = blockIdx.x;
+  const int k = blockIdx.y / head_blocks;
+  const int hb = blockIdx.y - k * head_blocks;
+  const int b = blockIdx.z;
+  const int G = H / K;
+  const int L = seq_lens[b];
+  const int t0 = p * part_tokens;
+  if (t0 >= L) return;  // partition beyond this sequence: nothing to do
+  const int t1 = min(t0 + part_tokens, L);
+
+  const int lane = threadIdx.x;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  // Q^T operand: lane (n, g) holds head hb*16+n, dims 32s+8g..+7.
+  const int hq = hb * 16 + n;
+  const bool hq_ok = hq < G;
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = as_bf16x8(hq_ok ? ld16(qrow + 32 * s + 8 * g) : zero_u32x4());
+  }
+
+  const size_t head_base = ((size_t)b * K + k) * (size_t)S_max * D;
+  const __bf16* kbase = kc + head_base;
+  const __bf16* vbase = vc + head_base;
+
+  float m_run = -INFINITY;  // running max of head n (replicated over g)
+  float l_run = 0.f;        // running sum of head n
+  f32x4 acc[NTILES];
+#pragma unroll
+  for (int t = 0; t < NTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int vrow = lane / LANES_PER_ROW;
+  const int vcol = (lane % LANES_PER_ROW) * 8;
+
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    // ---- issue all loads of the chunk: K into operand registers, V rows ----
+    u32x4 ka[2][KSTEPS];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int tok = c0 + 16 * mt + n;
+      const __bf16* krow = kbase + (size_t)tok * D + 8 * g;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = tok < t1 ? ld16(krow + 32 * s) : zero_u32x4();
+    }
+    u32x4 vr[VLOADS];
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int tok = c0 + i * ROWS_PER_LOAD + vrow;
+      vr[i] = tok < t1 ? ld16(vbase + (size_t)tok * D + vcol) : zero_u32x4();
+    }
+
+    // ---- S^T = K . Q^T for the two 16-position tiles ----
+    f32x4 st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[mt][s]), qf[s], st[mt], 0, 0, 0);
+    }
+
+    // ---- online softmax for head n over positions {16mt + 4g + i} ----
+    float sv[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = c0 + 16 * mt + 4 * g + i;
+        const float x = tok < t1 ? st[mt][i] * scale_log2 : -INFINITY;
+        sv[4 * mt + i] = x;
+        cmax = fmaxf(cmax, x);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);  // finite: the chunk has >= 1 position
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+    uint32_t pw[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float e0 = fast_exp2(sv[j] - m_new);
+      const float e1 = fast_exp2(sv[j + 1] - m_new);
+      psum += e0 + e1;
+      pw[j / 2] = pack_bf16x2(e0, e1);
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    // acc rows are heads 4g+i; their rescale factors live in lanes 4g+i.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
+    }
+
+    // ---- V chunk -> LDS, then gather the B operand in P's position order ----
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i)
+      *reinterpret_cast<u32x4*>(&vt[i * ROWS_PER_LOAD + vrow][vcol]) = vr[i];
+    __syncthreads();
+    const bf16x8 pa = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+    for (int t = 0; t < NTILES; ++t) {
+      const int col = 16 * t + n;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // contraction slots 2j, 2j+1 -> positions tok(g, 2j), tok(g, 2j+1)
+        const int i0 = 2 * j, i1 = 2 * j + 1;
+        const int r0 = (i0 < 4) ? 4 * g + i0 : 16 + 4 * g + (i0 - 4);
+        const int r1 = (i1 < 4) ? 4 * g + i1 : 16 + 4 * g + (i1 - 4);
+        w[j] = (uint32_t)vt[r0][col] | ((uint32_t)vt[r1][col] << 16);
+      }
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
+                                                       acc[t], 0, 0, 0);
+    }
+    __syncthreads();  // LDS reads done before the next chunk overwrites vt
+  }
+
+  // ---- write the partition's partial state ----
+  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * g + i;
+    if (hb * 16 + hl < G) {
+      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
+    }
+  }
+  if (g == 0 && hq_ok) {
+    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    ml[0] = m_run;
+    ml[1] = l_run;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_split_bf16(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
+                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
+                                    float scale_log2, hipStream_t stream) {
+  const dim3 grid(plan.parts, K * plan.head_blocks, B);
+  const dim3 block(64);
+  auto qp = static_cast<const __bf16*>(q);
+  auto kp = static_cast<const __bf16*>(k_cache);
+  auto vp = static_cast<const __bf16*>(v_cache);
+  if (d == 128)
+    hipLaunchKernelGGL(decode_split_bf16_kernel<128>, grid, block, 0, stream, qp, kp, vp, seq_lens,
+                       ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts,
+                       plan.head_blocks, scale_log2);
+  else
+    hipLaunchKernelGGL(decode_split_bf16_kernel<64>, grid, block, 0, stream, qp, kp, vp, seq_lens,
+                       ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts,
+                       plan.head_blocks, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,75 @@
+// Decode combine pass: merges the partitions' online-softmax states.
+//
+// For query head h of sequence b with n = ceil(L_b / part_tokens) partitions
+// holding (m_p, l_p, acc_p) in base-2 units:
+//     M = max_p m_p,  w_p = 2^(m_p - M),
+//     out = (sum_p w_p acc_p) / (sum_p w_p l_p),
+// which equals softmax-weighted sum over all L_b positions (the block-wise
+// computation with an online softmax that the foundit.cn GQA article and
+// pinghaoyang.com.cn "GQA 完全拆解" (section 质量与速度的实测权衡, on
+// FlashAttention being complementary to GQA) name; the merge rule follows
+// from exp(a) = exp(a - M) exp(M)).  L_b = 0 gives a zero row.
+//
+// One 64-thread workgroup per (b, h); thread c owns dims c, c+64.
+#include "common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(64) void decode_combine_kernel(
+    const float* __restrict__ part_acc, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ seq_lens, void* __restrict__ out, int H, int part_tokens,
+    int parts) {
+  constexpr int PER = D / 64;
+  const int bh = blockIdx.x;
+  const int b = bh / H;
+  const int L = seq_lens[b];
+  const int n = L > 0 ? min(parts, (L + part_tokens - 1) / part_tokens) : 0;
+  const float* ml = part_ml + (size_t)bh * parts * 2;
+  const float* pa = part_acc + (size_t)bh * parts * D;
+
+  float M = -INFINITY;
+  for (int p = 0; p < n; ++p) M = fmaxf(M, ml[2 * p]);
+  float num[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) num[j] = 0.f;
+  float den = 0.f;
+  for (int p = 0; p < n; ++p) {
+    const float w = fast_exp2(ml[2 * p] - M);
+    den = fmaf(w, ml[2 * p + 1], den);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) num[j] = fmaf(w, pa[(size_t)p * D + threadIdx.x + 64 * j], num[j]);
+  }
+  const float inv = n > 0 ? 1.f / den : 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const float o = n > 0 ? num[j] * inv : 0.f;
+    const size_t idx = (size_t)bh * D + threadIdx.x + 64 * j;
+    if (OUT_BF16)
+      static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(o);
+    else
+      static_cast<float*>(out)[idx] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_combine(const DecodeWorkspace& ws, const int32_t* seq_lens, void* out,
+                                 const DecodePlan& plan, int B, int H, int d, bool out_bf16,
+                                 hipStream_t stream) {
+  const dim3 grid(B * H), block(64);
+#define GQA_COMBINE(DD, OB)                                                                     \
+  hipLaunchKernelGGL((decode_combine_kernel<DD, OB>), grid, block, 0, stream, ws.part_acc,      \
+                     ws.part_ml, seq_lens, out, H, plan.part_tokens, plan.parts)
+  if (d == 128) {
+    if (out_bf16) GQA_COMBINE(128, true); else GQA_COMBINE(128, false);
+  } else {
+    if (out_bf16) GQA_COMBINE(64, true); else GQA_COMBINE(64, false);
+  }
+#undef GQA_COMBINE
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -1,0 +1,238 @@
+// C ABI of libgqa: argument validation, split planning and kernel launches.
+// The declarations and their contracts are in include/gqa.h.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "gqa.h"
+#include "gqa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_ev_begin = nullptr;
+thread_local hipEvent_t g_ev_end = nullptr;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return GQA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == GQA_F32 ? 4 : (dtype == GQA_BF16 ? 2 : 0); }
+
+int check_hip(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return GQA_OK;
+}
+
+// Partition length override for tuning (multiple of 64 positions); 0 = automatic.
+int part_tokens_override() {
+  static const int v = [] {
+    const char* s = std::getenv("GQA_DECODE_PART_TOKENS");
+    if (!s) return 0;
+    const int x = std::atoi(s);
+    return x >= 64 ? (x + 63) / 64 * 64 : 0;
+  }();
+  return v;
+}
+
+// Launch with optional timing events around the main kernel.
+struct TimedRegion {
+  hipStream_t s;
+  explicit TimedRegion(hipStream_t st) : s(st) {
+    if (g_ev_begin && g_ev_end) (void)hipEventRecord(g_ev_begin, s);
+  }
+  ~TimedRegion() {
+    if (g_ev_begin && g_ev_end) (void)hipEventRecord(g_ev_end, s);
+  }
+};
+
+}  // namespace
+
+namespace gqa {
+
+DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d) {
+  (void)d;
+  DecodePlan p{};
+  const int G = H / K;
+  p.head_blocks = (G + 15) / 16;
+  const long long units = (long long)B * K * p.head_blocks;
+  const int L = max_seq_len > 0 ? max_seq_len : 1;
+  int pt = part_tokens_override();
+  if (pt == 0) {
+    // Aim at roughly 4096 single-wave partitions in flight over 256 CUs; a
+    // partition never goes below 64 positions.
+    const long long target = 4096;
+    long long parts = target / (units > 0 ? units : 1);
+    if (parts < 1) parts = 1;
+    long long t = (L + parts - 1) / parts;
+    t = (t + 63) / 64 * 64;
+    pt = (int)(t < 64 ? 64 : t);
+  }
+  p.part_tokens = pt;
+  p.parts = (L + pt - 1) / pt;
+  return p;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d) {
+  const size_t rows = (size_t)B * H * p.parts;
+  return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d) {
+  const size_t rows = (size_t)B * H * p.parts;
+  DecodeWorkspace w;
+  w.part_acc = static_cast<float*>(base);
+  w.part_ml = reinterpret_cast<float*>(static_cast<char*>(base) + align256(rows * d * sizeof(float)));
+  return w;
+}
+
+}  // namespace gqa
+
+extern "C" {
+
+int gqa_abi_version(void) { return 1; }
+
+const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+int gqa_set_timing_events(void* begin_event, void* end_event) {
+  if ((begin_event == nullptr) != (end_event == nullptr))
+    return fail(GQA_ERR_INVALID, "gqa_set_timing_events: pass two events or two NULLs");
+  g_ev_begin = static_cast<hipEvent_t>(begin_event);
+  g_ev_end = static_cast<hipEvent_t>(end_event);
+  return ok();
+}
+
+uint64_t gqa_kv_cache_bytes(int layers, int K, int d, int elem_bytes_, uint64_t tokens) {
+  if (layers < 0 || K < 0 || d < 0 || elem_bytes_ < 0) return 0;
+  return 2ull * (uint64_t)layers * (uint64_t)K * (uint64_t)d * (uint64_t)elem_bytes_ * tokens;
+}
+
+int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  int32_t* seq_lens, int B, int K, int S_max, int d, int dtype, void* stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens)
+    return fail(GQA_ERR_INVALID, "gqa_kv_append: null pointer");
+  if (B < 1 || K < 1 || S_max < 1) return fail(GQA_ERR_INVALID, "gqa_kv_append: sizes must be >= 1");
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "gqa_kv_append: d=%d (64 or 128)", d);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(GQA_ERR_UNSUPPORTED, "gqa_kv_append: dtype %d", dtype);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(GQA_ERR_INVALID, "gqa_kv_append: misaligned pointer");
+  const int r = check_hip(gqa::launch_kv_append(k_new, v_new, k_cache, v_cache, seq_lens, B, K, S_max,
+                                                d * eb, static_cast<hipStream_t>(stream)),
+                          "gqa_kv_append launch");
+  return r ? r : ok();
+}
+
+static int validate_heads(const char* fn, int B, int H, int K, int d) {
+  if (B < 1 || H < 1 || K < 1) return fail(GQA_ERR_INVALID, "%s: B, H, K must be >= 1", fn);
+  if (K > H || H % K != 0) return fail(GQA_ERR_INVALID, "%s: H=%d not a multiple of K=%d", fn, H, K);
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", fn, d);
+  return GQA_OK;
+}
+
+size_t gqa_decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d) {
+  if (B < 1 || H < 1 || K < 1 || K > H || H % K || max_seq_len < 0 || (d != 64 && d != 128)) return 0;
+  const gqa::DecodePlan p = gqa::plan_decode(B, H, K, max_seq_len, d);
+  return gqa::decode_workspace_bytes(p, B, H, d);
+}
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+               void* out, void* workspace, size_t workspace_bytes, int B, int H, int K, int S_max,
+               int max_seq_len, int d, float scale, int dtype, int out_dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(GQA_ERR_INVALID, "gqa_decode: null pointer");
+  if (int r = validate_heads("gqa_decode", B, H, K, d)) return r;
+  if (S_max < 1 || max_seq_len < 0 || max_seq_len > S_max)
+    return fail(GQA_ERR_INVALID, "gqa_decode: need 0 <= max_seq_len <= S_max, S_max >= 1");
+  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID, "gqa_decode: scale not finite");
+  if (dtype == GQA_F32) {
+    if (out_dtype != GQA_F32) return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: f32 input needs f32 output");
+  } else if (dtype == GQA_BF16) {
+    if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
+      return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: out_dtype %d", out_dtype);
+  } else {
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: dtype %d", dtype);
+  }
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(GQA_ERR_INVALID, "gqa_decode: misaligned pointer");
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d);
+  const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(GQA_ERR_WORKSPACE, "gqa_decode: workspace needs %zu bytes (16-byte aligned), got %zu",
+                need, workspace ? workspace_bytes : (size_t)0);
+  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, H, d);
+  const float scale_log2 = scale * gqa::kLog2eHost;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r;
+  {
+    TimedRegion timed(s);
+    r = check_hip(dtype == GQA_BF16
+                      ? gqa::launch_decode_split_bf16(q, k_cache, v_cache, seq_lens, ws, plan, B, H,
+                                                      K, S_max, d, scale_log2, s)
+                      : gqa::launch_decode_split_f32(q, k_cache, v_cache, seq_lens, ws, plan, B, H,
+                                                     K, S_max, d, scale_log2, s),
+                  "gqa_decode partition launch");
+  }
+  if (r) return r;
+  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16, s),
+                "gqa_decode combine launch");
+  return r ? r : ok();
+}
+
+int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B, int H, int K,
+                       int S, int S_max, int d, float scale, int dtype, int out_dtype, void* stream) {
+  if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: null pointer");
+  if (int r = validate_heads("gqa_prefill_causal", B, H, K, d)) return r;
+  if (S < 1 || S_max < S) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: need 1 <= S <= S_max");
+  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: scale not finite");
+  if (dtype != GQA_BF16)
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_causal: only bf16 inputs (matrix-core path)");
+  if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
+    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_causal: out_dtype %d", out_dtype);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(GQA_ERR_INVALID, "gqa_prefill_causal: misaligned pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r;
+  {
+    TimedRegion timed(s);
+    r = check_hip(gqa::launch_prefill_causal_bf16(q, k, v, out, B, H, K, S, S_max, d,
+                                                  scale * gqa::kLog2eHost, out_dtype == GQA_BF16, s),
+                  "gqa_prefill_causal launch");
+  }
+  return r ? r : ok();
+}
+
+int gqa_meanpool_convert(const void* src, void* dst, int64_t outer, int H, int K, int64_t inner,
+                         int dtype, void* stream) {
+  if (!src || !dst) return fail(GQA_ERR_INVALID, "gqa_meanpool_convert: null pointer");
+  if (outer < 1 || inner < 1 || H < 1 || K < 1)
+    return fail(GQA_ERR_INVALID, "gqa_meanpool_convert: sizes must be >= 1");
+  if (K > H || H % K) return fail(GQA_ERR_INVALID, "gqa_meanpool_convert: H=%d not a multiple of K=%d", H, K);
+  if (!elem_bytes(dtype)) return fail(GQA_ERR_UNSUPPORTED, "gqa_meanpool_convert: dtype %d", dtype);
+  if (!aligned16(src) || !aligned16(dst)) return fail(GQA_ERR_INVALID, "gqa_meanpool_convert: misaligned pointer");
+  const int r = check_hip(gqa::launch_meanpool(src, dst, outer, H, K, inner, dtype == GQA_BF16,
+                                               static_cast<hipStream_t>(stream)),
+                          "gqa_meanpool_convert launch");
+  return r ? r : ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Internal declarations shared by the HIP translation units of libgqa.
+// Not part of the public ABI (include/gqa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr float kLog2eHost = 1.4426950408889634f;  // 1 / ln(2)
+
+// Split plan of one decode call: the cache positions [0, max_seq_len) are
+// cut into `parts` partitions of `part_tokens` positions; the query heads of
+// a group are handled in `head_blocks` blocks of at most 16 heads.
+struct DecodePlan {
+  int part_tokens;
+  int parts;
+  int head_blocks;
+};
+
+DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d);
+
+// Workspace layout of a decode call (all fp32):
+//   part_acc [B*H][parts][d]   un-normalised partial outputs
+//   part_ml  [B*H][parts][2]   running max (log2 units) and running sum
+struct DecodeWorkspace {
+  float* part_acc;
+  float* part_ml;
+};
+size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d);
+DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d);
+
+// ---- launchers (each returns the hipGetLastError() of its launch) ----
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            int32_t* seq_lens, int B, int K, int S_max, int row_bytes,
+                            hipStream_t stream);
+
+// Partition pass, bf16 inputs, matrix-core (MFMA) contraction.
+hipError_t launch_decode_split_bf16(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
+                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
+                                    float scale_log2, hipStream_t stream);
+
+// Partition pass, fp32 inputs, vector-ALU contraction.
+hipError_t launch_decode_split_f32(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* seq_lens, const DecodeWorkspace& ws,
+                                   const DecodePlan& plan, int B, int H, int K, int S_max, int d,
+                                   float scale_log2, hipStream_t stream);
+
+// Combine pass: partials -> out (fp32 or bf16).
+hipError_t launch_decode_combine(const DecodeWorkspace& ws, const int32_t* seq_lens, void* out,
+                                 const DecodePlan& plan, int B, int H, int d, bool out_bf16,
+                                 hipStream_t stream);
+
+hipError_t launch_prefill_causal_bf16(const void* q, const void* k, const void* v, void* out,
+                                      int B, int H, int K, int S, int S_max, int d,
+                                      float scale_log2, bool out_bf16, hipStream_t stream);
+
+hipError_t launch_meanpool(const void* src, void* dst, int64_t outer, int H, int K, int64_t inner,
+                           bool bf16, hipStream_t stream);
+
+}  // namespace gqa

@@ -1,0 +1,52 @@
+// Cache append: one new K row and one new V row per (sequence, KV head) are
+// written at position seq_lens[b], then seq_lens[b] grows by one.
+//
+// compassingai.com "分組查詢注意力", section 技術原理 (technical principle): a
+// generated token writes a [batch, 1, K, d_k] K and V row (K KV heads, not
+// H).  pinghaoyang.com.cn "GQA 完全拆解", section 解码推理的内存账本 (decode
+// memory ledger): the new row joins the cache at every decode step.
+//
+// One workgroup per sequence b.  Every thread reads seq_lens[b] before the
+// barrier and only thread 0 writes it after the barrier, so no thread can
+// see the incremented value.  Rows are moved as raw 16-byte words (bit
+// exact for any element type).  A full cache (L == S_max) is left as is.
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int32_t* __restrict__ seq_lens,
+    int K, int S_max, int row_words) {
+  const int b = blockIdx.x;
+  const int L = seq_lens[b];
+  __syncthreads();
+  if (L < 0 || L >= S_max) return;  // full (or corrupt) entry: write nothing
+  const int words = K * row_words;
+  for (int w = threadIdx.x; w < words; w += kAppendThreads) {
+    const int k = w / row_words;
+    const int o = w - k * row_words;
+    const size_t src = (size_t)(b * K + k) * row_words + o;
+    const size_t dst = ((size_t)(b * K + k) * S_max + L) * row_words + o;
+    k_cache[dst] = k_new[src];
+    v_cache[dst] = v_new[src];
+  }
+  if (threadIdx.x == 0) seq_lens[b] = L + 1;
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            int32_t* seq_lens, int B, int K, int S_max, int row_bytes,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(kv_append_kernel, dim3(B), dim3(kAppendThreads), 0, stream,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), seq_lens, K,
+                     S_max, row_bytes / 16);
+  return hipGetLastError();
+}
+
+}  // namespace gqa

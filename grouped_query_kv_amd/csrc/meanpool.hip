@@ -1,0 +1,112 @@
+// Mean-pool conversion of per-head weights into group weights:
+//   dst[o, g, i] = (sum_{r < G} src[o, g*G + r, i]) / G.
+//
+// pinghaoyang.com.cn "GQA 完全拆解", section Uptraining：把现成 MHA 检查点改造成
+// GQA (the key and value projections of a group are replaced by the mean of
+// its heads' projections); compassingai.com "分組查詢注意力", section 技術原理
+// (arithmetic mean over the H/K heads of a group; queries unchanged).
+//
+// Rounding rule: the sum runs in fp32 in head order r = 0..G-1 and is then
+// divided once by G with IEEE division, then rounded to the element type.
+// For G identical bf16 inputs every partial sum r*x is exact in fp32 (8
+// significant bits times r < 2^16), so the result is exactly x.
+//
+// Memory-bound elementwise pass: each thread handles one 16-byte word of
+// the output row (8 bf16 or 4 fp32 elements) and reads the G matching words.
+#include "common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void meanpool_vec_kernel(const u32x4* __restrict__ src,
+                                                           u32x4* __restrict__ dst, int64_t outer,
+                                                           int H, int K, int64_t words) {
+  constexpr int E = BF16 ? 8 : 4;  // elements per 16-byte word
+  const int G = H / K;
+  const float den = (float)G;
+  const int64_t total = outer * K * words;
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < total;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = w % words;
+    const int64_t og = w / words;
+    const int g = (int)(og % K);
+    const int64_t o = og / K;
+    float s[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = 0.f;
+    for (int r = 0; r < G; ++r) {
+      const u32x4 x = src[(o * H + (int64_t)g * G + r) * words + i];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float v;
+        if (BF16)
+          v = bf16_bits_to_f32((x[e / 2] >> (16 * (e & 1))) & 0xffffu);
+        else
+          v = __builtin_bit_cast(float, x[e]);
+        s[e] += v;
+      }
+    }
+    u32x4 y;
+    if (BF16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = pack_bf16x2(s[2 * j] / den, s[2 * j + 1] / den);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = __builtin_bit_cast(uint32_t, s[j] / den);
+    }
+    dst[w] = y;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void meanpool_scalar_kernel(const T* __restrict__ src,
+                                                              T* __restrict__ dst, int64_t outer,
+                                                              int H, int K, int64_t inner) {
+  const int G = H / K;
+  const int64_t total = outer * K * inner;
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < total;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = w % inner;
+    const int64_t og = w / inner;
+    const int g = (int)(og % K);
+    const int64_t o = og / K;
+    float s = 0.f;
+    for (int r = 0; r < G; ++r) s += static_cast<float>(src[(o * H + (int64_t)g * G + r) * inner + i]);
+    dst[w] = static_cast<T>(s / (float)G);
+  }
+}
+
+int grid_for(int64_t total) {
+  const int64_t blocks = (total + 255) / 256;
+  return (int)(blocks < 65536 ? (blocks > 0 ? blocks : 1) : 65536);
+}
+
+}  // namespace
+
+hipError_t launch_meanpool(const void* src, void* dst, int64_t outer, int H, int K, int64_t inner,
+                           bool bf16, hipStream_t stream) {
+  const int E = bf16 ? 8 : 4;
+  if (inner % E == 0) {
+    const int64_t words = inner / E;
+    const int grid = grid_for(outer * K * words);
+    if (bf16)
+      hipLaunchKernelGGL(meanpool_vec_kernel<true>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), outer, H, K, words);
+    else
+      hipLaunchKernelGGL(meanpool_vec_kernel<false>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), outer, H, K, words);
+  } else {
+    const int grid = grid_for(outer * K * inner);
+    if (bf16)
+      hipLaunchKernelGGL(meanpool_scalar_kernel<__bf16>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<const __bf16*>(src), static_cast<__bf16*>(dst), outer, H, K, inner);
+    else
+      hipLaunchKernelGGL(meanpool_scalar_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                         static_cast<const float*>(src), static_cast<float*>(dst), outer, H, K, inner);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gqa

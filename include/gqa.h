@@ -1,0 +1,155 @@
+/*
+ * gqa.h -- C ABI of the MI355X (gfx950) grouped-query-attention library.
+ *
+ * Grouped-query attention (GQA) splits H query heads into K groups of
+ * G = H / K consecutive heads; every head of group g attends to the one
+ * shared key head K_g and value head V_g with softmax(q K_g^T * scale) V_g.
+ *   - compassingai.com "分組查詢注意力", section 技術原理 (technical principle):
+ *     Q is regrouped [.., H, d] -> [.., K, H/K, d]; each generated token
+ *     writes one [batch, 1, K, d_k] K and V row.
+ *   - pinghaoyang.com.cn/aigc/posts/gqa "GQA 完全拆解", section
+ *     GQA：插值在 MHA 与 MQA 之间的分组共享 (GQA): group g is the consecutive
+ *     query heads (g-1)H/K+1 .. gH/K; K = 1 is MQA and K = H is MHA.
+ *   - same page, section 解码推理的内存账本 (decode memory ledger): at decode
+ *     step t the new query attends to all cached rows 1..t and the new K/V
+ *     row joins the cache; prefill processes the whole prefix at once.
+ *   - same page, section 工程实现 (engineering): the cache is laid out
+ *     layer x KV head x position and a group-aware kernel loads each shared
+ *     KV block once for all query heads of its group.
+ *
+ * Conventions for every entry point
+ *   - Layouts are contiguous row-major:
+ *       q (decode)        [B, H, d]
+ *       k_cache, v_cache  [B, K, S_max, d]      (position rows, d innermost)
+ *       k_new, v_new      [B, K, d]
+ *       seq_lens          [B] int32             (valid rows per sequence)
+ *       q, out (prefill)  [B, H, S, d]
+ *     Query head h uses KV head h / G (integer division).
+ *   - All pointers are device memory owned by the caller (hipMalloc or a
+ *     framework allocator); the library never frees or retains them after
+ *     the call returns.  Base pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work and never synchronises the device.
+ *   - Element types: GQA_F32 (float) and GQA_BF16 (bfloat16, RNE on output).
+ *     Supported head dimensions: d = 64 and d = 128.
+ *   - Return value: GQA_OK, or a negative code.  Argument errors are found
+ *     on the host before anything is enqueued; the text of the last error of
+ *     the calling thread is returned by gqa_last_error().
+ *   - Device-side contract (cannot be checked without a synchronisation):
+ *     0 <= seq_lens[b] <= S_max, and for decode seq_lens[b] <= max_seq_len.
+ *     Cache rows at positions >= seq_lens[b] are never read.
+ */
+#ifndef GQA_H_
+#define GQA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { GQA_F32 = 0, GQA_BF16 = 1 };
+
+enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID = -1,     /* null pointer, bad size, H % K != 0, misalignment */
+  GQA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}, unsupported dtype pair       */
+  GQA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required      */
+  GQA_ERR_HIP = -4          /* a HIP runtime call or launch failed             */
+};
+
+/* Version of this ABI (bumped on any incompatible change). */
+int gqa_abi_version(void);
+
+/*
+ * Append one token per sequence: for every b with L = seq_lens[b] < S_max
+ *   k_cache[b, k, L, :] = k_new[b, k, :],  v_cache[b, k, L, :] = v_new[b, k, :]
+ * for all k, then seq_lens[b] = L + 1.  A sequence whose cache is full
+ * (L == S_max) is left untouched, so nothing is ever written out of bounds.
+ * The copy is bit-exact.  (compassingai.com, technical principle: a token
+ * writes a [batch, 1, K, d_k] row; pinghaoyang.com.cn, decode memory ledger.)
+ * Arguments: B, K >= 1; S_max >= 1; d in {64, 128}; dtype GQA_F32 or GQA_BF16.
+ */
+int gqa_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  int32_t* seq_lens, int B, int K, int S_max, int d, int dtype,
+                  void* stream);
+
+/*
+ * Bytes of device workspace gqa_decode needs for these sizes (0 on invalid
+ * sizes).  The workspace holds per-partition partial results and is fully
+ * overwritten by every call; its content on entry does not matter.
+ */
+size_t gqa_decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d);
+
+/*
+ * One decode step of GQA over the KV cache:
+ *   out[b, h, :] = sum_{j < L_b} p_j v_cache[b, h/G, j, :],
+ *   p = softmax_j(scale * q[b, h, :] . k_cache[b, h/G, j, :]),  L_b = seq_lens[b]
+ * and out[b, h, :] = 0 when L_b == 0.  Call gqa_kv_append first to attend
+ * to the new token as well (pinghaoyang.com.cn, decode memory ledger: the
+ * step-t query sees rows 1..t).
+ *
+ * The cache is split along positions into partitions that are reduced with
+ * an online softmax (fp32 running max and sum) and combined in a second
+ * pass; each partition streams its K/V rows once for all G heads.
+ *
+ * max_seq_len: host-side upper bound of every seq_lens[b] (sizes the split).
+ * dtype: element type of q and the caches; out_dtype: GQA_F32, or GQA_BF16
+ * when dtype is GQA_BF16.  scale: usually 1/sqrt(d).
+ * workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes.
+ */
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
+               int B, int H, int K, int S_max, int max_seq_len, int d, float scale,
+               int dtype, int out_dtype, void* stream);
+
+/*
+ * Causal GQA attention over a whole prefix (prefill):
+ *   out[b, h, i, :] = sum_{j <= i} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
+ * for i in [0, S).  k and v are [B, K, S_max, d] with S <= S_max; rows >= S
+ * are never read.  (pinghaoyang.com.cn, decode memory ledger: prefill
+ * computes the whole prefix in parallel; row i equals decode step i.)
+ * dtype must be GQA_BF16 (bf16 matrix-core path, fp32 accumulation);
+ * out_dtype GQA_BF16 or GQA_F32.
+ */
+int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
+                       int B, int H, int K, int S, int S_max, int d, float scale,
+                       int dtype, int out_dtype, void* stream);
+
+/*
+ * Mean-pool conversion of per-head weights into group weights:
+ *   dst[o, g, i] = (sum_{r < G} src[o, g*G + r, i]) / G
+ * with src [outer, H, inner] and dst [outer, K, inner], both of `dtype`.
+ * The sum runs in fp32 in head order and is divided once by G (IEEE
+ * division), then rounded to dtype.  (pinghaoyang.com.cn, section
+ * Uptraining：把现成 MHA 检查点改造成 GQA (mean-pooling conversion);
+ * compassingai.com, technical principle.)
+ */
+int gqa_meanpool_convert(const void* src, void* dst, int64_t outer, int H, int K,
+                         int64_t inner, int dtype, void* stream);
+
+/*
+ * KV-cache size in bytes: 2 * layers * K * d * elem_bytes * tokens
+ * (pinghaoyang.com.cn, decode memory ledger and GQA section).  Host only.
+ * Returns 0 if any argument is negative.
+ */
+uint64_t gqa_kv_cache_bytes(int layers, int K, int d, int elem_bytes, uint64_t tokens);
+
+/*
+ * Benchmark timing hook.  While set (both non-NULL), gqa_decode and
+ * gqa_prefill_causal record `begin_event` on their stream immediately before
+ * launching their main kernel and `end_event` immediately after it; the
+ * events are hipEvent_t handles passed as void*, owned by the caller.
+ * Applies to calls from the calling thread only; pass NULLs to clear.
+ */
+int gqa_set_timing_events(void* begin_event, void* end_event);
+
+/* Text of the last error returned on the calling thread ("" if none). */
+const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H_ */

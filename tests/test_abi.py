@@ -1,0 +1,137 @@
+"""The C-ABI library: it loads, exports what include/gqa.h declares, and its
+host-side logic (sizes, validation, error codes) behaves -- all without a GPU.
+
+Every call here fails validation (or is host-only), so nothing is enqueued.
+"""
+import ctypes
+import json
+from pathlib import Path
+
+import pytest
+
+import grouped_query_kv_amd as gqa
+from grouped_query_kv_amd import _binding as B
+
+GOLDEN = Path(__file__).resolve().parent / "golden" / "kv_cache_bytes.json"
+FAKE = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gqa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = gqa.header_symbols()
+    assert {"gqa_kv_append", "gqa_decode", "gqa_prefill_causal", "gqa_meanpool_convert"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), f"libgqa.so does not export {name}"
+
+
+def test_abi_version(lib):
+    assert lib.gqa_abi_version() == 1
+
+
+def test_kv_cache_bytes_matches_pages(lib):
+    for e in json.loads(GOLDEN.read_text())["entries"]:
+        got = gqa.gqa_kv_cache_bytes(e["layers"], e["kv_heads"], e["head_dim"], e["elem_bytes"], e["tokens"])
+        if "exact_bytes" in e:
+            assert got == e["exact_bytes"], e["what"]
+        else:
+            assert round(got / e["unit_bytes"], e["round_to"]) == e["approx"], e["what"]
+    assert gqa.gqa_kv_cache_bytes(-1, 8, 128, 2, 1) == 0
+
+
+def test_workspace_bytes(lib):
+    assert gqa.gqa_decode_workspace_bytes(16, 32, 8, 8193, 128) > 0
+    # invalid shapes -> 0
+    assert gqa.gqa_decode_workspace_bytes(16, 30, 8, 8193, 128) == 0
+    assert gqa.gqa_decode_workspace_bytes(16, 32, 8, 8193, 96) == 0
+    assert gqa.gqa_decode_workspace_bytes(0, 32, 8, 8193, 128) == 0
+    # grows with the context
+    assert gqa.gqa_decode_workspace_bytes(4, 32, 8, 131072, 128) >= gqa.gqa_decode_workspace_bytes(4, 32, 8, 1024, 128)
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30, B=2, H=8, K=2,
+             S_max=64, max_seq_len=64, d=128, scale=0.088, dtype=B.GQA_BF16, out_dtype=B.GQA_BF16)
+    a.update(kw)
+    return lib.gqa_decode(a["q"], a["k"], a["v"], a["sl"], a["out"], a["ws"], a["wsb"], a["B"], a["H"],
+                          a["K"], a["S_max"], a["max_seq_len"], a["d"], a["scale"], a["dtype"],
+                          a["out_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), B.GQA_ERR_INVALID),
+    (dict(out=None), B.GQA_ERR_INVALID),
+    (dict(H=9, K=2), B.GQA_ERR_INVALID),
+    (dict(H=2, K=4), B.GQA_ERR_INVALID),
+    (dict(B=0), B.GQA_ERR_INVALID),
+    (dict(d=96), B.GQA_ERR_UNSUPPORTED),
+    (dict(dtype=7), B.GQA_ERR_UNSUPPORTED),
+    (dict(dtype=B.GQA_F32, out_dtype=B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    (dict(max_seq_len=65), B.GQA_ERR_INVALID),
+    (dict(scale=float("nan")), B.GQA_ERR_INVALID),
+    (dict(q=FAKE + 2), B.GQA_ERR_INVALID),
+    (dict(wsb=16), B.GQA_ERR_WORKSPACE),
+    (dict(ws=None), B.GQA_ERR_WORKSPACE),
+])
+def test_decode_rejects(lib, kw, code):
+    assert _decode(lib, **kw) == code
+    assert lib.gqa_last_error().decode().startswith("gqa_decode")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, FAKE, FAKE, 2, 8, 16, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 16, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 16, 80, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 16, 128, 5), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE + 8, FAKE, FAKE, 2, 8, 16, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE + 2, 2, 8, 16, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+])
+def test_append_rejects(lib, args, code):
+    assert lib.gqa_kv_append(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 8, 16, 128, 0.1, B.GQA_F32, B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 16, 8, 128, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 3, 16, 16, 128, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, None, 1, 8, 2, 16, 16, 128, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 16, 16, 32, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 0, 16, 128, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_INVALID),
+])
+def test_prefill_rejects(lib, args, code):
+    assert lib.gqa_prefill_causal(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, 4, 8, 2, 16, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, 0, 8, 2, 16, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, 4, 8, 3, 16, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, 4, 8, 2, 16, 9), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE + 4, 4, 8, 2, 16, B.GQA_F32), B.GQA_ERR_INVALID),
+])
+def test_meanpool_rejects(lib, args, code):
+    assert lib.gqa_meanpool_convert(*args, None) == code
+
+
+def test_timing_events_need_both(lib):
+    assert lib.gqa_set_timing_events(FAKE, None) == B.GQA_ERR_INVALID
+    assert lib.gqa_set_timing_events(None, None) == B.GQA_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gqa.gqa_meanpool_convert(torch.zeros(2, 8, 4), torch.zeros(2, 2, 4))
+    with pytest.raises(ValueError):
+        gqa.gqa_decode(x, x[:, None], x[:, None], torch.zeros(2, dtype=torch.int32), x,
+                       torch.zeros(16, dtype=torch.uint8), 8)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load_library(tmp_path / "nope.so")

@@ -1,0 +1,123 @@
+"""GPU parity of the decode path (gqa_decode) against the fp64 CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_kv_amd as gqa
+from grouped_query_kv_amd.inputs import WORKLOADS, decode_inputs, workload_inputs
+from gpu_util import DEV, TOL, f64, guarded, guards_intact, note, report, run_decode, scale_of
+from oracle import decode_ref, kv_append_ref
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, append=False):
+    q = f64(inp["q"])
+    kc, vc, sl = inp["k_cache"], inp["v_cache"], inp["seq_lens"].numpy()
+    d = q.shape[-1]
+    if append:
+        kc_n = kc.float().numpy()
+        vc_n = vc.float().numpy()
+        kc_n, vc_n, sl = kv_append_ref(inp["k_new"].float().numpy(), inp["v_new"].float().numpy(),
+                                       kc_n, vc_n, sl)
+        return decode_ref(q, kc_n, vc_n, sl, scale_of(d))
+    return decode_ref(q, kc.float().numpy(), vc.float().numpy(), sl, scale_of(d))
+
+
+# ---- the tiny fp32 workload and its MHA / MQA variants ----------------------
+@pytest.mark.parametrize("K", [4, 16, 1])
+def test_decode_tiny_f32(K):
+    w = WORKLOADS["decode_tiny_f32"]
+    inp = decode_inputs(w.B, w.H, K, w.d, "f32", seed=0, L=w.L)
+    note(f"decode tiny f32 K={K}")
+    out, _ = run_decode(inp)
+    r = report(f"tiny f32 K={K}", f64(out), _oracle(inp))
+    assert r["finite"] and r["max_abs"] <= TOL["f32"]
+
+
+# ---- bf16 (and fp32) shape sweep: group sizes, head dims, ragged lengths ----
+CASES = [
+    # B, H, K, d, lens, dtype
+    (3, 32, 8, 128, [1, 33, 1000], "bf16"),
+    (2, 16, 4, 64, [31, 32], "bf16"),
+    (2, 56, 8, 128, [300, 5], "bf16"),         # G = 7
+    (1, 71, 1, 64, [257], "bf16"),             # G = 71: five head blocks
+    (2, 8, 8, 128, [2, 97], "bf16"),           # K = H (MHA)
+    (2, 32, 1, 128, [129, 64], "bf16"),        # K = 1 (MQA), G = 32
+    (4, 64, 8, 128, [0, 1, 640, 641], "bf16"),  # empty sequence, partition edges
+    (2, 12, 4, 128, [70, 3], "f32"),
+    (1, 71, 1, 128, [200], "f32"),
+]
+
+
+@pytest.mark.parametrize("B,H,K,d,lens,dtype", CASES)
+def test_decode_shapes(B, H, K, d, lens, dtype):
+    note(f"decode B={B} H={H} K={K} d={d} lens={lens} {dtype}")
+    inp = decode_inputs(B, H, K, d, dtype, seed=11, lens=lens)
+    out, _ = run_decode(inp)
+    r = report("shape", f64(out), _oracle(inp))
+    assert r["finite"] and r["max_abs"] <= TOL[dtype]
+    zero = [b for b, L in enumerate(lens) if L == 0]
+    for b in zero:
+        assert torch.count_nonzero(out[b]).item() == 0
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_decode_out_dtype_and_guards(out_dtype):
+    """Output written exactly in place (guard bands intact), fp32 or bf16."""
+    B, H, K, d = 2, 32, 8, 128
+    inp = decode_inputs(B, H, K, d, "bf16", seed=5, lens=[500, 77])
+    q, kc, vc = inp["q"].to(DEV), inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    sl = inp["seq_lens"].to(DEV)
+    out, buf, guard = guarded((B, H, d), out_dtype)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, 500, d), dtype=torch.uint8, device=DEV)
+    note(f"decode guards out={out_dtype}")
+    gqa.gqa_decode(q, kc, vc, sl, out, ws, 500, scale=scale_of(d))
+    torch.cuda.synchronize()
+    assert guards_intact(buf, guard, out_dtype)
+    r = report("guards", f64(out), _oracle(inp))
+    assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+
+
+def test_decode_is_deterministic():
+    inp = decode_inputs(2, 32, 8, 128, "bf16", seed=9, lens=[3000, 1234])
+    a, _ = run_decode(inp)
+    b, _ = run_decode(inp)
+    assert torch.equal(a, b)
+
+
+def test_decode_timing_events():
+    inp = decode_inputs(2, 32, 8, 128, "bf16", seed=9, lens=[3000, 1234])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gqa.gqa_set_timing_events(e0, e1)
+    try:
+        run_decode(inp)
+    finally:
+        gqa.gqa_set_timing_events(None, None)
+    assert e0.elapsed_time(e1) > 0.0
+
+
+# ---- the full-size workloads, in the launch configuration the bench uses ----
+@pytest.mark.parametrize("name", ["decode_llama3_8b", "decode_70b_ragged", "decode_long_131k"])
+def test_decode_full_workload(name):
+    w = WORKLOADS[name]
+    note(f"full workload {name}: generating inputs")
+    inp = workload_inputs(w, seed=0)
+    note(f"full workload {name}: GPU")
+    out, dev = run_decode(inp, append=w.append)
+    if w.append:
+        # the appended rows and the lengths must match the oracle bit for bit
+        sl_ref = inp["seq_lens"].numpy() + 1
+        assert np.array_equal(dev["seq_lens"].cpu().numpy(), sl_ref)
+        for b in range(w.B):
+            L = int(inp["seq_lens"][b])
+            assert torch.equal(dev["k_cache"][b, :, L].cpu(), inp["k_new"][b])
+            assert torch.equal(dev["v_cache"][b, :, L].cpu(), inp["v_new"][b])
+    note(f"full workload {name}: oracle")
+    ref = np.zeros(tuple(out.shape))
+    got = f64(out)
+    for b in range(w.B):  # per sequence to bound host memory
+        sub = {k: (v[b:b + 1] if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        ref[b] = _oracle(sub, append=w.append)[0]
+    r = report(name, got, ref)
+    assert r["finite"] and r["max_abs"] <= TOL["bf16"]
