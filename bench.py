@@ -1,0 +1,192 @@
+"""Benchmark of the GQA decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole decode hot path over one batch: append the
+new token's K/V rows of every sequence (gqa_kv_append), then attend over the
+cache (gqa_decode: partition pass + combine pass).  The default workload is
+the Llama-3-8B-shaped layer: B=16 sequences at 8192 cached tokens, 32 query
+heads over 8 KV heads, d=128, bf16 (synthetic N(0,1) data).
+
+The caches are kept in several copies that the steps rotate through, so no
+step finds the previous step's cache lines in the 256 MB Infinity Cache; each
+step appends one more token, so the context grows by one per visit of a copy
+and the algorithmic bytes are counted from the actual lengths.
+
+Prints one JSON line.  `value` is the KV-cache read rate of the whole step
+(algorithmic KV bytes / step time); tokens/s (B tokens per step) and the
+fraction of the 8 TB/s HBM peak are reported beside it.  `roofline` covers
+the dominant kernel (the decode partition pass), timed live with HIP events
+recorded on its stream around each launch.  `cpu_baseline` is the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_llama3_8b")
+    ap.add_argument("--copies", type=int, default=4, help="cache copies rotated over the steps")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline time budget")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kv_bytes(lens, K, d, elem):
+    return int(sum(2 * K * int(L) * d * elem for L in lens))
+
+
+def cpu_baseline_decode(inp, w, budget_s):
+    """Time the fp64 oracle (unchanged) on whole sequences of the workload,
+    one BLAS thread, until about `budget_s` seconds have been spent."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import decode_ref, kv_append_ref
+
+    d = w.d
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    done_bytes, done_seqs, t_used = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        b = 0
+        while t_used < budget_s and done_seqs < 4 * w.B:
+            sl = inp["seq_lens"][b:b + 1].numpy()
+            q = inp["q"][b:b + 1].double().numpy()
+            kc = inp["k_cache"][b:b + 1].float().numpy()
+            vc = inp["v_cache"][b:b + 1].float().numpy()
+            kn = inp["k_new"][b:b + 1].float().numpy()
+            vn = inp["v_new"][b:b + 1].float().numpy()
+            t0 = time.perf_counter()
+            if w.append:
+                kc, vc, sl = kv_append_ref(kn, vn, kc, vc, sl)
+            decode_ref(q, kc, vc, sl, scale)
+            t_used += time.perf_counter() - t0
+            done_bytes += kv_bytes(sl, w.K, d, 2)
+            done_seqs += 1
+            b = (b + 1) % w.B
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": done_seqs / t_used,
+            "sample": f"{done_seqs} whole sequences of the workload (append + decode over "
+                      f"{int(inp['seq_lens'][0]) + (1 if w.append else 0)} positions, all 32 heads), "
+                      f"{t_used:.1f} s of fp64 NumPy on 1 thread"}
+
+
+def bench_decode(args, w):
+    import grouped_query_kv_amd as gqa
+    from grouped_query_kv_amd.inputs import workload_inputs
+
+    dev = torch.device("cuda:0")
+    R = max(1, args.copies)
+    visits = math.ceil((args.warmup + args.steps) / R)
+    base_len = int(w.L) if w.ragged is None else w.ragged[1]
+    s_max = base_len + visits + 2
+    t_gen = time.perf_counter()
+    inp = workload_inputs(w, seed=args.seed, s_max=s_max)
+    t_gen = time.perf_counter() - t_gen
+    B, H, K, d = w.B, w.H, w.K, w.d
+    q = inp["q"].to(dev)
+    kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
+    copies = []
+    kc0, vc0 = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    for r in range(R):
+        copies.append({"k": kc0 if r == 0 else kc0.clone(), "v": vc0 if r == 0 else vc0.clone(),
+                       "sl": inp["seq_lens"].to(dev).clone()})
+    host_lens = [inp["seq_lens"].clone() for _ in range(R)]
+    max_len = int(inp["seq_lens"].max()) + visits + 1
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, max_len, d), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = copies[i % R]
+        if w.append:
+            gqa.gqa_kv_append(kn, vn, c["k"], c["v"], c["sl"], stream=stream)
+            host_lens[i % R] += 1
+        if ev is not None:
+            gqa.gqa_set_timing_events(ev[0], ev[1])
+        gqa.gqa_decode(q, c["k"], c["v"], c["sl"], out, ws, max_len, scale=scale, stream=stream)
+        if ev is not None:
+            gqa.gqa_set_timing_events(None, None)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # algorithmic KV bytes of each timed step (lengths after that step's append)
+    step_bytes = []
+    sim = [h.clone() for h in host_lens]
+    for i in range(args.warmup, args.warmup + args.steps):
+        if w.append:
+            sim[i % R] += 1
+        step_bytes.append(kv_bytes(sim[i % R].tolist(), K, d, 2))
+    events = [(gqa.HipEvent(), gqa.HipEvent()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j, i in enumerate(range(args.warmup, args.warmup + args.steps)):
+        step(i, events[j])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = [a.elapsed_ms(b) for a, b in events]
+    total_bytes = sum(step_bytes)
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = total_bytes / elapsed / 1e9
+    kern_avg_ms = float(np.mean(kern_ms))
+    achieved = (total_bytes / args.steps) / (kern_avg_ms * 1e-3) / 1e9
+    res = {
+        "metric": "GQA decode KV-read GB/s (% of HBM peak) + attention tokens/s, 1xMI355X",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "K": K, "d": d,
+                   "context": (int(w.L) if w.ragged is None else list(w.ragged)),
+                   "append_per_step": bool(w.append), "cache_copies": R,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": int(total_bytes / args.steps),
+        "roofline": {"kernel": "decode partition pass (decode_split_bf16_kernel)", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_kernel_us": round(kern_avg_ms * 1e3, 3)},
+        "input_gen_s": round(t_gen, 1),
+    }
+    return res, inp
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    from grouped_query_kv_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    if w.kind != "decode":
+        print(f"workload {w.name} is not a decode workload; the bench times the decode step", file=sys.stderr)
+        sys.exit(2)
+    res, inp = bench_decode(args, w)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(inp, w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     GQA_BF16,
     GQA_F32,
     GQAError,
+    HipEvent,
     gqa_abi_version,
     gqa_decode,
     gqa_decode_workspace_bytes,

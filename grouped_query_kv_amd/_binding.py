@@ -113,11 +113,53 @@ def gqa_kv_cache_bytes(layers: int, K: int, d: int, elem_bytes: int, tokens: int
     return int(load_library().gqa_kv_cache_bytes(layers, K, d, elem_bytes, tokens))
 
 
-def gqa_set_timing_events(begin=None, end=None) -> None:
+_hip = None
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime already loaded in this process (the one torch and
+    libgqa share), for raw event handles."""
+    global _hip
+    if _hip is None:
+        load_library()
+        h = ctypes.CDLL("libamdhip64.so.7")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _c_void_p, _c_void_p]
+        h.hipEventSynchronize.argtypes = [_c_void_p]
+        h.hipEventDestroy.argtypes = [_c_void_p]
+        _hip = h
+    return _hip
+
+
+class HipEvent:
+    """A raw timing hipEvent_t, recorded by the library's timing hook."""
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        if _hip_runtime().hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        """Milliseconds between this event and `end` (waits for `end`)."""
+        h = _hip_runtime()
+        if h.hipEventSynchronize(end.handle) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if h.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed (event not recorded?)")
+        return float(ms.value)
+
+    def __del__(self):
+        if _hip is not None and self.handle:
+            _hip.hipEventDestroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+
+def gqa_set_timing_events(begin: HipEvent | None = None, end: HipEvent | None = None) -> None:
     """Arm (or clear, with None) the begin/end events recorded around the
     main kernel of gqa_decode / gqa_prefill_causal on this thread."""
-    b = None if begin is None else begin.cuda_event
-    e = None if end is None else end.cuda_event
+    b = None if begin is None else begin.handle
+    e = None if end is None else end.handle
     _check("gqa_set_timing_events", load_library().gqa_set_timing_events(b, e))
 
 

@@ -38,14 +38,15 @@ __global__ __launch_bounds__(256) void meanpool_vec_kernel(const u32x4* __restri
     for (int e = 0; e < E; ++e) s[e] = 0.f;
     for (int r = 0; r < G; ++r) {
       const u32x4 x = src[(o * H + (int64_t)g * G + r) * words + i];
+      if (BF16) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float v;
-        if (BF16)
-          v = bf16_bits_to_f32((x[e / 2] >> (16 * (e & 1))) & 0xffffu);
-        else
-          v = __builtin_bit_cast(float, x[e]);
-        s[e] += v;
+        for (int e = 0; e < E; ++e) s[e] += bf16_bits_to_f32((x[e / 2] >> (16 * (e & 1))) & 0xffffu);
+      } else {
+        // whole-vector reinterpretation (a per-element bit_cast of a vector
+        // subscript is not used: it has been seen to read element 0 only)
+        const f32x4 xf = __builtin_bit_cast(f32x4, x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[e] += xf[e];
       }
     }
     u32x4 y;
@@ -53,8 +54,7 @@ __global__ __launch_bounds__(256) void meanpool_vec_kernel(const u32x4* __restri
 #pragma unroll
       for (int j = 0; j < 4; ++j) y[j] = pack_bf16x2(s[2 * j] / den, s[2 * j + 1] / den);
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = __builtin_bit_cast(uint32_t, s[j] / den);
+      y = __builtin_bit_cast(u32x4, f32x4{s[0] / den, s[1] / den, s[2] / den, s[3] / den});
     }
     dst[w] = y;
   }

@@ -88,13 +88,13 @@ def test_decode_is_deterministic():
 
 def test_decode_timing_events():
     inp = decode_inputs(2, 32, 8, 128, "bf16", seed=9, lens=[3000, 1234])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = gqa.HipEvent(), gqa.HipEvent()
     gqa.gqa_set_timing_events(e0, e1)
     try:
         run_decode(inp)
     finally:
         gqa.gqa_set_timing_events(None, None)
-    assert e0.elapsed_time(e1) > 0.0
+    assert e0.elapsed_ms(e1) > 0.0
 
 
 # ---- the full-size workloads, in the launch configuration the bench uses ----
