@@ -123,7 +123,7 @@ def _hip_runtime() -> ctypes.CDLL:
     if _hip is None:
         load_library()
         h = ctypes.CDLL("libamdhip64.so.7")
-        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _c_void_p, _c_void_p]
         h.hipEventSynchronize.argtypes = [_c_void_p]
         h.hipEventDestroy.argtypes = [_c_void_p]
@@ -132,12 +132,17 @@ def _hip_runtime() -> ctypes.CDLL:
 
 
 class HipEvent:
-    """A raw timing hipEvent_t, recorded by the library's timing hook."""
+    """A raw timing hipEvent_t, recorded by the library's timing hook.  It is
+    created without the system-scope fence on record (a timing-only event),
+    so recording it does not write back and invalidate the caches between
+    the kernels it brackets."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self):
         self.handle = ctypes.c_void_p()
-        if _hip_runtime().hipEventCreate(ctypes.byref(self.handle)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if _hip_runtime().hipEventCreateWithFlags(ctypes.byref(self.handle), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
 
     def elapsed_ms(self, end: "HipEvent") -> float:
         """Milliseconds between this event and `end` (waits for `end`)."""

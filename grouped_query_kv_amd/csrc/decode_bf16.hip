@@ -31,8 +31,16 @@
 //     every K operand is one 16-byte load from a K row;
 //   * P.V: the scores come out of the first product as lane (n = head, g)
 //     holding positions {4g+i, 16+4g+i}; those eight positions are used as
-//     that lane's contraction slots, so P needs no data movement and only V
-//     is gathered (from LDS) in the same position order.
+//     that lane's contraction slots, so P needs no data movement.
+// V is staged row-major in LDS and read back transposed with
+// ds_read_b64_tr_b16: within each 16-lane group, the 64-bit reads of lanes
+// 4r..4r+3 form row r of a 4 x 16 block of bf16 and lane i receives column i.
+// Pointing the four lanes of row r at V[position r][16t .. 16t+15] gives lane
+// (n, g) the values V[p][16t + n] of four positions p, which is exactly half
+// of its B operand; two such reads give the eight contraction slots.
+//
+// Loads of chunk c+1 are issued before the arithmetic of chunk c so the
+// wavefront always has a chunk of K and V in flight.
 #include "common.h"
 #include "gqa_internal.h"
 
@@ -41,6 +49,16 @@ namespace {
 
 constexpr int kChunk = 32;   // positions per inner iteration
 constexpr int kVPad = 8;     // bf16 elements of padding per LDS row
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposed 64-bit LDS read (see the layout note above).
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
 
 template <int D>
 __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
@@ -54,8 +72,9 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   constexpr int LANES_PER_ROW = D / 8;  // 16-byte words per V row
   constexpr int ROWS_PER_LOAD = 64 / LANES_PER_ROW;
   constexpr int VLOADS = kChunk / ROWS_PER_LOAD;
+  constexpr int LDS_ROW = D + kVPad;
 
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk][D + kVPad];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * LDS_ROW];
 
   const int p = blockIdx.x;
   const int k = blockIdx.y / head_blocks;
@@ -94,10 +113,13 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 
   const int vrow = lane / LANES_PER_ROW;
   const int vcol = (lane % LANES_PER_ROW) * 8;
+  // transposed-read source of this lane: row 4g + (n/4) (+16 for slots 4..7),
+  // dims 16t + 4*(n%4)
+  const uint16_t* tr_src = &vt[(4 * g + (n >> 2)) * LDS_ROW + 4 * (n & 3)];
 
-  for (int c0 = t0; c0 < t1; c0 += kChunk) {
-    // ---- issue all loads of the chunk: K into operand registers, V rows ----
-    u32x4 ka[2][KSTEPS];
+  u32x4 ka[2][KSTEPS];
+  u32x4 vr[VLOADS];
+  auto load_k = [&](int c0) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int tok = c0 + 16 * mt + n;
@@ -105,13 +127,19 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = tok < t1 ? ld16(krow + 32 * s) : zero_u32x4();
     }
-    u32x4 vr[VLOADS];
+  };
+  auto load_v = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int tok = c0 + i * ROWS_PER_LOAD + vrow;
       vr[i] = tok < t1 ? ld16(vbase + (size_t)tok * D + vcol) : zero_u32x4();
     }
+  };
+  load_k(t0);
+  load_v(t0);
 
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    const bool more = c0 + kChunk < t1;
     // ---- S^T = K . Q^T for the two 16-position tiles ----
     f32x4 st[2];
 #pragma unroll
@@ -121,6 +149,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       for (int s = 0; s < KSTEPS; ++s)
         st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[mt][s]), qf[s], st[mt], 0, 0, 0);
     }
+    if (more) load_k(c0 + kChunk);  // next chunk's K streams during this chunk
 
     // ---- online softmax for head n over positions {16mt + 4g + i} ----
     float sv[8];
@@ -160,25 +189,18 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
     }
 
-    // ---- V chunk -> LDS, then gather the B operand in P's position order ----
+    // ---- V chunk -> LDS (row-major), then transposed reads as B operand ----
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i)
-      *reinterpret_cast<u32x4*>(&vt[i * ROWS_PER_LOAD + vrow][vcol]) = vr[i];
+      *reinterpret_cast<u32x4*>(&vt[(i * ROWS_PER_LOAD + vrow) * LDS_ROW + vcol]) = vr[i];
     __syncthreads();
+    if (more) load_v(c0 + kChunk);  // next chunk's V streams during P.V
     const bf16x8 pa = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
     for (int t = 0; t < NTILES; ++t) {
-      const int col = 16 * t + n;
-      uint32_t w[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // contraction slots 2j, 2j+1 -> positions tok(g, 2j), tok(g, 2j+1)
-        const int i0 = 2 * j, i1 = 2 * j + 1;
-        const int r0 = (i0 < 4) ? 4 * g + i0 : 16 + 4 * g + (i0 - 4);
-        const int r1 = (i1 < 4) ? 4 * g + i1 : 16 + 4 * g + (i1 - 4);
-        w[j] = (uint32_t)vt[r0][col] | ((uint32_t)vt[r1][col] << 16);
-      }
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u32x4{w[0], w[1], w[2], w[3]}),
+      const uint2 lo = lds_read_tr16(tr_src + 16 * t);
+      const uint2 hi = lds_read_tr16(tr_src + 16 * LDS_ROW + 16 * t);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}),
                                                        acc[t], 0, 0, 0);
     }
     __syncthreads();  // LDS reads done before the next chunk overwrites vt

@@ -10,7 +10,7 @@
 // FlashAttention being complementary to GQA) name; the merge rule follows
 // from exp(a) = exp(a - M) exp(M)).  L_b = 0 gives a zero row.
 //
-// One 64-thread workgroup per (b, h); thread c owns dims c, c+64.
+// One 64-thread workgroup per (b, h); lane c owns dims [c*D/64, (c+1)*D/64).
 #include "common.h"
 #include "gqa_internal.h"
 
@@ -22,31 +22,60 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
     const int32_t* __restrict__ seq_lens, void* __restrict__ out, int H, int part_tokens,
     int parts) {
-  constexpr int PER = D / 64;
+  constexpr int PER = D / 64;  // dims per lane
+  __shared__ float wsh[64];
   const int bh = blockIdx.x;
   const int b = bh / H;
+  const int lane = threadIdx.x;
   const int L = seq_lens[b];
   const int n = L > 0 ? min(parts, (L + part_tokens - 1) / part_tokens) : 0;
-  const float* ml = part_ml + (size_t)bh * parts * 2;
-  const float* pa = part_acc + (size_t)bh * parts * D;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)bh * parts;
+  const float* pa = part_acc + (size_t)bh * parts * D + lane * PER;
 
+  // pass 1: global max over the partitions (lane-parallel loads)
   float M = -INFINITY;
-  for (int p = 0; p < n; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p].x);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  // pass 2: weights of up to 64 partitions at a time, shared through LDS;
+  // every lane then sums its dims over those partitions with independent loads
   float num[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) num[j] = 0.f;
   float den = 0.f;
-  for (int p = 0; p < n; ++p) {
-    const float w = fast_exp2(ml[2 * p] - M);
-    den = fmaf(w, ml[2 * p + 1], den);
-#pragma unroll
-    for (int j = 0; j < PER; ++j) num[j] = fmaf(w, pa[(size_t)p * D + threadIdx.x + 64 * j], num[j]);
+  for (int p0 = 0; p0 < n; p0 += 64) {
+    const int p = p0 + lane;
+    float w = 0.f;
+    if (p < n) {
+      const float2 x = ml[p];
+      w = fast_exp2(x.x - M);
+      den = fmaf(w, x.y, den);
+    }
+    wsh[lane] = w;
+    __syncthreads();
+    const int cnt = min(64, n - p0);
+#pragma unroll 8
+    for (int j = 0; j < cnt; ++j) {
+      const float wj = wsh[j];
+      const float* src = pa + (size_t)(p0 + j) * D;
+      if (PER == 2) {
+        const float2 a = *reinterpret_cast<const float2*>(src);
+        num[0] = fmaf(wj, a.x, num[0]);
+        num[PER - 1] = fmaf(wj, a.y, num[PER - 1]);
+      } else {
+        num[0] = fmaf(wj, src[0], num[0]);
+      }
+    }
+    __syncthreads();
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
   const float inv = n > 0 ? 1.f / den : 0.f;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const float o = n > 0 ? num[j] * inv : 0.f;
-    const size_t idx = (size_t)bh * D + threadIdx.x + 64 * j;
+    const size_t idx = (size_t)bh * D + lane * PER + j;
     if (OUT_BF16)
       static_cast<__bf16*>(out)[idx] = static_cast<__bf16>(o);
     else

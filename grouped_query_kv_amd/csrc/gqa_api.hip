@@ -39,13 +39,14 @@ int check_hip(hipError_t e, const char* what) {
   return GQA_OK;
 }
 
-// Partition length override for tuning (multiple of 64 positions); 0 = automatic.
+// Partition length override for tuning (rounded up to a multiple of 32
+// positions, at least 64); 0 = automatic.
 int part_tokens_override() {
   static const int v = [] {
     const char* s = std::getenv("GQA_DECODE_PART_TOKENS");
     if (!s) return 0;
     const int x = std::atoi(s);
-    return x >= 64 ? (x + 63) / 64 * 64 : 0;
+    return x >= 64 ? (x + 31) / 32 * 32 : 0;
   }();
   return v;
 }
@@ -74,13 +75,14 @@ DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d) {
   const int L = max_seq_len > 0 ? max_seq_len : 1;
   int pt = part_tokens_override();
   if (pt == 0) {
-    // Aim at roughly 4096 single-wave partitions in flight over 256 CUs; a
-    // partition never goes below 64 positions.
-    const long long target = 4096;
+    // One single-wave workgroup per partition.  Aim at about one full round
+    // of resident waves over the 256 CUs (3 per SIMD at the partition pass's
+    // register budget), with equal partitions of a multiple of 32 positions.
+    const long long target = 256LL * 4 * 3;
     long long parts = target / (units > 0 ? units : 1);
     if (parts < 1) parts = 1;
     long long t = (L + parts - 1) / parts;
-    t = (t + 63) / 64 * 64;
+    t = (t + 31) / 32 * 32;
     pt = (int)(t < 64 ? 64 : t);
   }
   p.part_tokens = pt;
