@@ -2,6 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+With --workload prefill_causal_4k it times the causal prefill instead (one
+step = one prefill of the whole batch; value in TFLOP/s of unmasked work).
+
 A step is one pass of the whole decode hot path over one batch: append the
 new token's K/V rows of every sequence (gqa_kv_append), then attend over the
 cache (gqa_decode: partition pass + combine pass).  The default workload is
@@ -170,6 +173,77 @@ def bench_decode(args, w):
     return res, inp
 
 
+def cpu_baseline_prefill(inp, w, budget_s):
+    """Time the fp64 oracle (unchanged) on whole (sequence, head) slices of
+    the prefill workload, one BLAS thread, until about `budget_s` seconds."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import prefill_causal_ref
+
+    scale = float(np.float32(1.0 / math.sqrt(w.d)))
+    G = w.H // w.K
+    done, t_used, heads = 0.0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s and heads < w.B * w.H:
+            b, h = divmod(heads, w.H)
+            q = inp["q"][b:b + 1, h:h + 1].double().numpy()
+            k = inp["k"][b:b + 1, h // G:h // G + 1].float().numpy()
+            v = inp["v"][b:b + 1, h // G:h // G + 1].float().numpy()
+            t0 = time.perf_counter()
+            prefill_causal_ref(q, k, v, scale)
+            t_used += time.perf_counter() - t0
+            done += 2.0 * w.d * w.L * (w.L + 1)
+            heads += 1
+    return {"value": done / t_used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{heads} whole (sequence, head) slices of the workload ({w.L} causal rows each), "
+                      f"{t_used:.1f} s of fp64 NumPy on 1 thread"}
+
+
+def bench_prefill(args, w):
+    import grouped_query_kv_amd as gqa
+    from grouped_query_kv_amd.inputs import workload_inputs
+
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = workload_inputs(w, seed=args.seed)
+    t_gen = time.perf_counter() - t_gen
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    out = torch.empty_like(q)
+    scale = float(np.float32(1.0 / math.sqrt(w.d)))
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        gqa.gqa_prefill_causal(q, k, v, out, scale=scale, stream=stream)
+    events = [(gqa.HipEvent(), gqa.HipEvent()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ev in events:
+        gqa.gqa_set_timing_events(*ev)
+        gqa.gqa_prefill_causal(q, k, v, out, scale=scale, stream=stream)
+        gqa.gqa_set_timing_events(None, None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = float(np.mean([a.elapsed_ms(b) for a, b in events]))
+    flops = 2.0 * w.B * w.H * w.d * w.L * (w.L + 1)   # unmasked (j <= i) score entries only
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res = {
+        "metric": "GQA causal prefill TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "K": w.K, "d": w.d, "S": w.L,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(w.B * w.L / (ms_per_step * 1e-3), 1),
+        "roofline": {"kernel": "causal prefill (prefill_causal_kernel)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_kernel_us": round(kern_ms * 1e3, 3)},
+        "input_gen_s": round(t_gen, 1),
+    }
+    return res, inp
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -179,12 +253,14 @@ def main():
     from grouped_query_kv_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    if w.kind != "decode":
-        print(f"workload {w.name} is not a decode workload; the bench times the decode step", file=sys.stderr)
-        sys.exit(2)
-    res, inp = bench_decode(args, w)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_decode(inp, w, args.cpu_seconds)
+    if w.kind == "prefill":
+        res, inp = bench_prefill(args, w)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_prefill(inp, w, args.cpu_seconds)
+    else:
+        res, inp = bench_decode(args, w)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_decode(inp, w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

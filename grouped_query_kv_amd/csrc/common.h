@@ -18,11 +18,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast
 // 16-byte global load (the address must be 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
 
-// Round-to-nearest-even fp32 -> bf16, two values packed low|high.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Round-to-nearest-even fp32 -> bf16, two values packed low|high (one
+// v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

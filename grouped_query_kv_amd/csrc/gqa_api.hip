@@ -164,7 +164,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
   if (int r = validate_heads("gqa_decode", B, H, K, d)) return r;
   if (S_max < 1 || max_seq_len < 0 || max_seq_len > S_max)
     return fail(GQA_ERR_INVALID, "gqa_decode: need 0 <= max_seq_len <= S_max, S_max >= 1");
-  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID, "gqa_decode: scale not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(GQA_ERR_INVALID, "gqa_decode: scale must be finite and > 0");
   if (dtype == GQA_F32) {
     if (out_dtype != GQA_F32) return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: f32 input needs f32 output");
   } else if (dtype == GQA_BF16) {
@@ -205,7 +205,8 @@ int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, i
   if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: null pointer");
   if (int r = validate_heads("gqa_prefill_causal", B, H, K, d)) return r;
   if (S < 1 || S_max < S) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: need 1 <= S <= S_max");
-  if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: scale not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(GQA_ERR_INVALID, "gqa_prefill_causal: scale must be finite and > 0");
   if (dtype != GQA_BF16)
     return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_causal: only bf16 inputs (matrix-core path)");
   if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)

@@ -12,16 +12,18 @@
 // block of 16 query positions, chunk of up to 8 heads of the group).  Each of
 // the 4 wavefronts owns two (head, 16 positions) row tiles, so one workgroup
 // covers 8 heads x 16 positions = 128 rows that all read the same K/V tiles.
-// The key loop walks 64-key tiles of [0, q0 + 16), staged in LDS:
-//   K tile [64][D]  row-major, 16-byte chunks XOR-swizzled by key,
-//   V tile [D][64]  transposed while being written, with the keys of every
-//                   32-key step permuted into the order the second product
-//                   consumes them, 16-byte chunks XOR-swizzled by dimension.
-// Per tile and row tile:  S^T[64 x 16] = K_tile . Q^T  (v_mfma_f32_16x16x32_bf16),
-// causal mask on the diagonal tile, base-2 online softmax in fp32,
-// O[16 x D] += P[16 x 64] . V_tile.  The score layout of the first product is
-// used directly as the P operand of the second (see decode_bf16.hip for the
-// operand layouts and the contraction-slot argument).
+// The key loop walks 64-key tiles of [0, q0 + 16), staged in LDS with rows
+// padded by 16 bytes (conflict-free 16-byte and transposed 8-byte reads):
+//   K tile [64][D]  read as the A operand of S^T = K . Q^T (ds_read_b128),
+//   V tile [64][D]  read transposed as the B operand of O += P . V
+//                   (ds_read_b64_tr_b16, see decode_bf16.hip for the layout).
+// The tiles are double-buffered: the global loads of tile j+1 are in flight
+// while tile j is multiplied, and one barrier per tile orders the buffers.
+// Per tile and row tile: S^T[64 x 16] = K_tile . Q^T (v_mfma_f32_16x16x32_bf16),
+// causal mask on the diagonal tile only, base-2 online softmax in fp32 with
+// lazy rescaling, O[16 x D] += P[16 x 64] . V_tile, where the score layout of
+// the first product is used directly as the P operand of the second, and the
+// softmax denominators come from the same product against a block of ones.
 // Blocks are issued last-position-first so the longest causal rows start
 // earliest.
 #include "common.h"
@@ -34,22 +36,27 @@ constexpr int kBN = 64;      // keys per tile
 constexpr int kBQ = 16;      // query positions per workgroup
 constexpr int kHeadsWG = 8;  // heads of the group per workgroup
 
-__device__ __forceinline__ int vt_slot(int key) {  // key in [0, 64)
-  const int ks = key >> 5, kk = key & 31;
-  return ks * 32 + ((kk & 15) >> 2) * 8 + ((kk >> 4) << 2) + (kk & 3);
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
 }
-__device__ __forceinline__ int vt_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void prefill_causal_kernel(
+__global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kg, const __bf16* __restrict__ vg,
     void* __restrict__ out, int H, int K, int S, int S_max, int head_chunks, float scale_log2) {
   constexpr int KSTEPS = D / 32;
   constexpr int DT = D / 16;
-  constexpr int CPR = D / 8;  // 16-byte chunks per K row
+  constexpr int ROW = D + 8;                // padded LDS row (elements)
+  constexpr int TILE = kBN * ROW;           // elements per staged tile
+  constexpr int CPR = D / 8;                // 16-byte chunks per global row
+  constexpr int LD_PER_THREAD = kBN * CPR / 256;
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vts[D * kBN];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [stage][K|V]
 
   const int nqb = (S + kBQ - 1) / kBQ;
   const int qb = nqb - 1 - (int)blockIdx.x;
@@ -65,7 +72,6 @@ __global__ __launch_bounds__(256) void prefill_causal_kernel(
   const int n = lane & 15;
   const int g = lane >> 4;
 
-  // the wave's two row tiles: heads hl0, hl0+1 of the group
   int hglob[2];
   bool hok[2];
 #pragma unroll
@@ -84,138 +90,174 @@ __global__ __launch_bounds__(256) void prefill_causal_kernel(
     for (int s = 0; s < KSTEPS; ++s) qf[j][s] = as_bf16x8(ld ? ld16(qrow + 32 * s + 8 * g) : zero_u32x4());
   }
 
+  // acc[jj][t]: O rows 4g+i, dims 16t+n.  lsum[jj]: the same rows' softmax
+  // denominators, produced by one extra P.V column block whose V is all ones
+  // (so the denominator sums exactly the bf16 weights the numerator uses).
   f32x4 acc[2][DT];
-  float m_run[2], l_run[2];
+  f32x4 lsum[2];
+  float m_run[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
+    lsum[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < DT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8 ones = as_bf16x8(u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 
   const size_t kv_base = ((size_t)b * K + k) * (size_t)S_max * D;
   const __bf16* kbase = kg + kv_base;
   const __bf16* vbase = vg + kv_base;
   const int kend = min(q0 + kBQ, S);
+  const int ntiles = (kend + kBN - 1) / kBN;
   const bool any_head = hok[0];
 
-  for (int kb0 = 0; kb0 < kend; kb0 += kBN) {
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage K and V tiles ----
+  // staging registers of one tile: this thread's share of K and V rows
+  u32x4 kr[LD_PER_THREAD], vr[LD_PER_THREAD];
+  auto load_tile = [&](int kb0) {
+    const bool full = kb0 + kBN <= kend;  // uniform: only the last tile is ragged
 #pragma unroll
-    for (int r = 0; r < kBN * CPR / 256; ++r) {
+    for (int r = 0; r < LD_PER_THREAD; ++r) {
       const int c = tid + 256 * r;
       const int key = c / CPR, cc = c - key * CPR;
-      const bool ld = kb0 + key < kend;
       const size_t off = (size_t)(kb0 + key) * D + cc * 8;
-      const u32x4 kw = ld ? ld16(kbase + off) : zero_u32x4();
-      const u32x4 vw = ld ? ld16(vbase + off) : zero_u32x4();
-      *reinterpret_cast<u32x4*>(&ks[key * D + ((cc ^ (key & (CPR - 1))) * 8)]) = kw;
-      const int slot = vt_slot(key);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = cc * 8 + e;
-        const int phys = ((slot >> 3) ^ vt_swz(row)) * 8 + (slot & 7);
-        vts[row * kBN + phys] = (uint16_t)(vw[e >> 1] >> (16 * (e & 1)));
+      if (full || kb0 + key < kend) {
+        kr[r] = ld16(kbase + off);
+        vr[r] = ld16(vbase + off);
+      } else {
+        kr[r] = zero_u32x4();
+        vr[r] = zero_u32x4();
       }
     }
-    __syncthreads();
-    if (!any_head) continue;
-
-    // ---- S^T = K_tile . Q^T for both row tiles ----
-    f32x4 st[2][4];
+  };
+  auto store_tile = [&](int stage) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) st[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int key = 16 * mt + n;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const int cc = 4 * s + g;
-        const bf16x8 a =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(&ks[key * D + ((cc ^ (key & (CPR - 1))) * 8)]));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          st[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], st[j][mt], 0, 0, 0);
-      }
+    for (int r = 0; r < LD_PER_THREAD; ++r) {
+      const int c = tid + 256 * r;
+      const int key = c / CPR, cc = c - key * CPR;
+      *reinterpret_cast<u32x4*>(&lds[stage][0][key * ROW + cc * 8]) = kr[r];
+      *reinterpret_cast<u32x4*>(&lds[stage][1][key * ROW + cc * 8]) = vr[r];
     }
+  };
 
-    // ---- online softmax per row tile ----
-    const bool diag = kb0 + kBN > q0;  // tile may hold keys beyond some rows
-    bf16x8 pa[2][2];
+  load_tile(0);
+  store_tile(0);
+  // transposed-read source of this lane inside a V tile (see decode_bf16.hip)
+  const int tr_off = (4 * g + (n >> 2)) * ROW + 4 * (n & 3);
+  // A row's running max is only raised (and its accumulators rescaled) when
+  // a tile's scores exceed it by more than 2^kLazy; otherwise the stale max
+  // is kept, the weights stay <= 2^kLazy, and numerator and denominator
+  // share it, so the quotient is unchanged.
+  constexpr float kLazy = 8.f;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int kb0 = j * kBN;
+    const int stage = j & 1;
+    const bool more = j + 1 < ntiles;
+    if (more) load_tile(kb0 + kBN);  // next tile streams during this one
+    __syncthreads();                 // tile j staged; tile j-1 fully consumed
+
+    if (any_head) {
+      const uint16_t* kt = lds[stage][0];
+      const uint16_t* vt = lds[stage][1];
+      // ---- S^T = K_tile . Q^T for both row tiles (raw q.k) ----
+      f32x4 st[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float sv[16];
-      float cmax = -INFINITY;
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) st[jj][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb0 + 16 * mt + 4 * g + i;
-          float x = st[j][mt][i] * scale_log2;
-          if (diag && key > pos_n) x = -INFINITY;
-          sv[4 * mt + i] = x;
-          cmax = fmaxf(cmax, x);
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const bf16x8 a =
+              as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[(16 * mt + n) * ROW + 32 * s + 8 * g]));
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            st[jj][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[jj][s], st[jj][mt], 0, 0, 0);
         }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run[j], cmax);
-      const float alpha = fast_exp2(m_run[j] - m_new);
-      float psum = 0.f;
-      uint32_t pw[8];
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float e0 = fast_exp2(sv[e] - m_new);
-        const float e1 = fast_exp2(sv[e + 1] - m_new);
-        psum += e0 + e1;
-        pw[e / 2] = pack_bf16x2(e0, e1);
       }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      l_run[j] = l_run[j] * alpha + psum;
-      m_run[j] = m_new;
-      // P operand of 32-key step ks: score tiles mt = 2ks, 2ks+1
-      pa[j][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-      pa[j][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
+      if (kb0 + kBN > q0) {  // diagonal tile: drop keys after the row's position
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = __shfl(alpha, 4 * g + i);
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int t = 0; t < DT; ++t) acc[j][t][i] *= a;
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (kb0 + 16 * mt + 4 * g + i > pos_n) st[jj][mt][i] = -INFINITY;
+      }
+
+      // ---- online softmax per row tile ----
+      bf16x8 pa[2][2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        float cmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, st[jj][mt][i]);
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        const float cand = cmax * scale_log2;  // scale > 0
+        if (__any(cand > m_run[jj] + kLazy)) {
+          const float m_new = fmaxf(m_run[jj], cand);
+          const float alpha = fast_exp2(m_run[jj] - m_new);
+          m_run[jj] = m_new;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = __shfl(alpha, 4 * g + i);
+            lsum[jj][i] *= a;
+#pragma unroll
+            for (int t = 0; t < DT; ++t) acc[jj][t][i] *= a;
+          }
+        }
+        const float mneg = -m_run[jj];
+        uint32_t pw[8];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2)
+            pw[2 * mt + i / 2] = pack_bf16x2(fast_exp2(fmaf(st[jj][mt][i], scale_log2, mneg)),
+                                             fast_exp2(fmaf(st[jj][mt][i + 1], scale_log2, mneg)));
+        // P operand of 32-key step kk: score tiles mt = 2kk, 2kk+1
+        pa[jj][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+        pa[jj][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
+      }
+
+      // ---- O += P . V_tile, and the denominators via the all-ones block ----
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const uint16_t* src = vt + tr_off + kk * 32 * ROW + 16 * t;
+          const uint2 lo = lds_read_tr16(src);
+          const uint2 hi = lds_read_tr16(src + 16 * ROW);
+          const bf16x8 vb = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            acc[jj][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[jj][kk], vb, acc[jj][t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          lsum[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[jj][kk], ones, lsum[jj], 0, 0, 0);
       }
     }
-
-    // ---- O += P . V_tile ----
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const int row = 16 * t + n;
-        const int phys = ((4 * kk + g) ^ vt_swz(row)) * 8;
-        const bf16x8 vb = as_bf16x8(*reinterpret_cast<const u32x4*>(&vts[row * kBN + phys]));
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[j][kk], vb, acc[j][t], 0, 0, 0);
-      }
+    if (more) store_tile(stage ^ 1);
   }
 
   // ---- normalise and store rows 4g+i of each row tile ----
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (!hok[j]) continue;
+  for (int jj = 0; jj < 2; ++jj) {
+    if (!hok[jj]) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float l = __shfl(l_run[j], 4 * g + i);
       const int pos = q0 + 4 * g + i;
       if (pos >= S) continue;
-      const float inv = 1.f / l;
-      const size_t orow = (((size_t)b * H + hglob[j]) * S + pos) * D;
+      const float inv = 1.f / lsum[jj][i];
+      const size_t orow = (((size_t)b * H + hglob[jj]) * S + pos) * D;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const float o = acc[j][t][i] * inv;
+        const float o = acc[jj][t][i] * inv;
         if (OUT_BF16)
           static_cast<__bf16*>(out)[orow + 16 * t + n] = static_cast<__bf16>(o);
         else

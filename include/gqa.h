@@ -96,7 +96,7 @@ size_t gqa_decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d);
  *
  * max_seq_len: host-side upper bound of every seq_lens[b] (sizes the split).
  * dtype: element type of q and the caches; out_dtype: GQA_F32, or GQA_BF16
- * when dtype is GQA_BF16.  scale: usually 1/sqrt(d).
+ * when dtype is GQA_BF16.  scale: finite and > 0, usually 1/sqrt(d).
  * workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes.
  */
 int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -111,7 +111,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
  * are never read.  (pinghaoyang.com.cn, decode memory ledger: prefill
  * computes the whole prefix in parallel; row i equals decode step i.)
  * dtype must be GQA_BF16 (bf16 matrix-core path, fp32 accumulation);
- * out_dtype GQA_BF16 or GQA_F32.
+ * out_dtype GQA_BF16 or GQA_F32; scale finite and > 0.
  */
 int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
                        int B, int H, int K, int S, int S_max, int d, float scale,

@@ -72,6 +72,8 @@ def _decode(lib, **kw):
     (dict(dtype=B.GQA_F32, out_dtype=B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
     (dict(max_seq_len=65), B.GQA_ERR_INVALID),
     (dict(scale=float("nan")), B.GQA_ERR_INVALID),
+    (dict(scale=-0.5), B.GQA_ERR_INVALID),
+    (dict(scale=0.0), B.GQA_ERR_INVALID),
     (dict(q=FAKE + 2), B.GQA_ERR_INVALID),
     (dict(wsb=16), B.GQA_ERR_WORKSPACE),
     (dict(ws=None), B.GQA_ERR_WORKSPACE),
