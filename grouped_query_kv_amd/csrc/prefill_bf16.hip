@@ -12,13 +12,17 @@
 // block of 16 query positions, chunk of up to 8 heads of the group).  Each of
 // the 4 wavefronts owns two (head, 16 positions) row tiles, so one workgroup
 // covers 8 heads x 16 positions = 128 rows that all read the same K/V tiles.
-// The key loop walks 64-key tiles of [0, q0 + 16), staged in LDS with rows
-// padded by 16 bytes (conflict-free 16-byte and transposed 8-byte reads):
+// The key loop walks 64-key tiles of [0, q0 + 16), copied from global memory
+// straight into LDS (global_load_lds_dwordx4: lane i of a wavefront lands
+// its 16 bytes at LDS base + 16 i, with no register staging).  Rows are kept
+// whole and their 16-byte chunks XOR-swizzled by row, which each lane
+// realises by fetching the global chunk that belongs in its LDS slot; the
+// swizzle makes the 16-byte and the transposed 8-byte reads conflict-free:
 //   K tile [64][D]  read as the A operand of S^T = K . Q^T (ds_read_b128),
 //   V tile [64][D]  read transposed as the B operand of O += P . V
 //                   (ds_read_b64_tr_b16, see decode_bf16.hip for the layout).
-// The tiles are double-buffered: the global loads of tile j+1 are in flight
-// while tile j is multiplied, and one barrier per tile orders the buffers.
+// The tiles are double-buffered: the copies of tile j+1 are in flight while
+// tile j is multiplied, and one barrier per tile orders the buffers.
 // Per tile and row tile: S^T[64 x 16] = K_tile . Q^T (v_mfma_f32_16x16x32_bf16),
 // causal mask on the diagonal tile only, base-2 online softmax in fp32 with
 // lazy rescaling, O[16 x D] += P[16 x 64] . V_tile, where the score layout of
@@ -51,10 +55,9 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
     void* __restrict__ out, int H, int K, int S, int S_max, int head_chunks, float scale_log2) {
   constexpr int KSTEPS = D / 32;
   constexpr int DT = D / 16;
-  constexpr int ROW = D + 8;                // padded LDS row (elements)
-  constexpr int TILE = kBN * ROW;           // elements per staged tile
-  constexpr int CPR = D / 8;                // 16-byte chunks per global row
-  constexpr int LD_PER_THREAD = kBN * CPR / 256;
+  constexpr int CPR = D / 8;                // 16-byte chunks per row
+  constexpr int TILE = kBN * D;             // elements per staged tile
+  constexpr int COPIES = kBN * CPR / 64 / 4;  // 1 KB copies per wave per tile and tensor
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [stage][K|V]
 
@@ -112,38 +115,30 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
   const int ntiles = (kend + kBN - 1) / kBN;
   const bool any_head = hok[0];
 
-  // staging registers of one tile: this thread's share of K and V rows
-  u32x4 kr[LD_PER_THREAD], vr[LD_PER_THREAD];
-  auto load_tile = [&](int kb0) {
-    const bool full = kb0 + kBN <= kend;  // uniform: only the last tile is ragged
+  // Copy tile kb0 of K and V into `stage`.  Copy ii of a tensor fills LDS
+  // chunks [64 ii, 64 ii + 64); lane l's chunk is row r = (64 ii + l) / CPR,
+  // physical chunk l % CPR, which holds logical chunk (l % CPR) ^ (r % CPR).
+  // Rows past the last key are fetched from the last key instead (finite
+  // values; the causal mask gives them zero weight).
+  auto copy_tile = [&](int kb0, int stage) {
 #pragma unroll
-    for (int r = 0; r < LD_PER_THREAD; ++r) {
-      const int c = tid + 256 * r;
-      const int key = c / CPR, cc = c - key * CPR;
-      const size_t off = (size_t)(kb0 + key) * D + cc * 8;
-      if (full || kb0 + key < kend) {
-        kr[r] = ld16(kbase + off);
-        vr[r] = ld16(vbase + off);
-      } else {
-        kr[r] = zero_u32x4();
-        vr[r] = zero_u32x4();
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int r = 0; r < LD_PER_THREAD; ++r) {
-      const int c = tid + 256 * r;
-      const int key = c / CPR, cc = c - key * CPR;
-      *reinterpret_cast<u32x4*>(&lds[stage][0][key * ROW + cc * 8]) = kr[r];
-      *reinterpret_cast<u32x4*>(&lds[stage][1][key * ROW + cc * 8]) = vr[r];
+    for (int r = 0; r < COPIES; ++r) {
+      const int ii = wave + 4 * r;
+      const int c = 64 * ii + lane;
+      const int row = c / CPR, cp = c - row * CPR;
+      const int key = min(kb0 + row, kend - 1);
+      const size_t off = (size_t)key * D + (size_t)((cp ^ (row & (CPR - 1))) * 8);
+      __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)&lds[stage][0][ii * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)&lds[stage][1][ii * 512], 16, 0, 0);
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  // transposed-read source of this lane inside a V tile (see decode_bf16.hip)
-  const int tr_off = (4 * g + (n >> 2)) * ROW + 4 * (n & 3);
+  copy_tile(0, 0);
+  // transposed-read source of this lane inside a V tile: row 4g + n/4 of each
+  // 16-row block, dims 16t + 4(n % 4), i.e. logical chunk 2t + (n % 4) / 2
+  const int tr_row = 4 * g + (n >> 2);
+  const int tr_sub = 4 * (n & 1);
+  const int tr_c = (n & 3) >> 1;
   // A row's running max is only raised (and its accumulators rescaled) when
   // a tile's scores exceed it by more than 2^kLazy; otherwise the stale max
   // is kept, the weights stay <= 2^kLazy, and numerator and denominator
@@ -154,8 +149,9 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
     const int kb0 = j * kBN;
     const int stage = j & 1;
     const bool more = j + 1 < ntiles;
-    if (more) load_tile(kb0 + kBN);  // next tile streams during this one
-    __syncthreads();                 // tile j staged; tile j-1 fully consumed
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies of tile j landed
+    __syncthreads();                     // tile j staged; tile j-1 fully consumed
+    if (more) copy_tile(kb0 + kBN, stage ^ 1);  // next tile streams during this one
 
     if (any_head) {
       const uint16_t* kt = lds[stage][0];
@@ -170,8 +166,9 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const bf16x8 a =
-              as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[(16 * mt + n) * ROW + 32 * s + 8 * g]));
+          const int row = 16 * mt + n;
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              &kt[row * D + (((4 * s + g) ^ (row & (CPR - 1))) * 8)]));
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
             st[jj][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[jj][s], st[jj][mt], 0, 0, 0);
@@ -229,9 +226,10 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          const uint16_t* src = vt + tr_off + kk * 32 * ROW + 16 * t;
-          const uint2 lo = lds_read_tr16(src);
-          const uint2 hi = lds_read_tr16(src + 16 * ROW);
+          const int r0 = 32 * kk + tr_row, r1 = r0 + 16;
+          const int cl = 2 * t + tr_c;
+          const uint2 lo = lds_read_tr16(vt + r0 * D + ((cl ^ (r0 & (CPR - 1))) * 8) + tr_sub);
+          const uint2 hi = lds_read_tr16(vt + r1 * D + ((cl ^ (r1 & (CPR - 1))) * 8) + tr_sub);
           const bf16x8 vb = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
@@ -242,7 +240,6 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
           lsum[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[jj][kk], ones, lsum[jj], 0, 0, 0);
       }
     }
-    if (more) store_tile(stage ^ 1);
   }
 
   // ---- normalise and store rows 4g+i of each row tile ----
