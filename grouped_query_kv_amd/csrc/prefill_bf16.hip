@@ -30,6 +30,8 @@
 // softmax denominators come from the same product against a block of ones.
 // Blocks are issued last-position-first so the longest causal rows start
 // earliest.
+#include <type_traits>
+
 #include "common.h"
 #include "gqa_internal.h"
 
@@ -115,131 +117,167 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
   const int ntiles = (kend + kBN - 1) / kBN;
   const bool any_head = hok[0];
 
-  // Copy tile kb0 of K and V into `stage`.  Copy ii of a tensor fills LDS
-  // chunks [64 ii, 64 ii + 64); lane l's chunk is row r = (64 ii + l) / CPR,
-  // physical chunk l % CPR, which holds logical chunk (l % CPR) ^ (r % CPR).
-  // Rows past the last key are fetched from the last key instead (finite
-  // values; the causal mask gives them zero weight).
-  auto copy_tile = [&](int kb0, int stage) {
+  // LDS layout of a staged tile: whole rows of D bf16, their 16-byte chunks
+  // XOR-swizzled by row -- K: chunk ^ (row % CPR), which spreads the eight
+  // rows of a 16-byte operand read over distinct banks; V: chunk ^
+  // 2 (row % (CPR/2)), which keeps the two chunks of a 32-byte transposed
+  // read adjacent and puts consecutive rows in distinct 32-byte bank groups.
+  // Copy ii of a tensor fills LDS chunks [64 ii, 64 ii + 64); lane l's chunk
+  // is row (64 ii + l) / CPR, physical chunk l % CPR, so the lane fetches the
+  // global chunk that belongs there.  Rows past the last key are fetched from
+  // the last key instead (finite values; the causal mask gives them zero
+  // weight).
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  int crow[COPIES], koff[COPIES], voff[COPIES];
+#pragma unroll
+  for (int r = 0; r < COPIES; ++r) {
+    const int c = 64 * (wave_s + 4 * r) + lane;
+    const int row = c / CPR, cp = c - row * CPR;
+    crow[r] = row;
+    koff[r] = row * D + (cp ^ (row & (CPR - 1))) * 8;
+    voff[r] = row * D + (cp ^ ((row & (CPR / 2 - 1)) << 1)) * 8;
+  }
+  auto copy_tile = [&](int kb0, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
+    const char* k0 = reinterpret_cast<const char*>(kbase + (size_t)kb0 * D);
+    const char* v0 = reinterpret_cast<const char*>(vbase + (size_t)kb0 * D);
+    const bool full = kb0 + kBN <= kend;  // uniform: only the last tile is ragged
 #pragma unroll
     for (int r = 0; r < COPIES; ++r) {
-      const int ii = wave + 4 * r;
-      const int c = 64 * ii + lane;
-      const int row = c / CPR, cp = c - row * CPR;
-      const int key = min(kb0 + row, kend - 1);
-      const size_t off = (size_t)key * D + (size_t)((cp ^ (row & (CPR - 1))) * 8);
-      __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)&lds[stage][0][ii * 512], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)&lds[stage][1][ii * 512], 16, 0, 0);
+      int ko = koff[r], vo = voff[r];
+      if (!full) {
+        const int past = kb0 + crow[r] - (kend - 1);
+        if (past > 0) {
+          ko -= past * D;
+          vo -= past * D;
+        }
+      }
+      // uniform base + 32-bit byte offset: the scalar-base addressing form
+      __builtin_amdgcn_global_load_lds(k0 + (uint32_t)(2 * ko), (__attribute__((address_space(3))) void*)&lds[ST][0][(wave_s + 4 * r) * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(v0 + (uint32_t)(2 * vo), (__attribute__((address_space(3))) void*)&lds[ST][1][(wave_s + 4 * r) * 512], 16, 0, 0);
     }
   };
 
-  copy_tile(0, 0);
-  // transposed-read source of this lane inside a V tile: row 4g + n/4 of each
-  // 16-row block, dims 16t + 4(n % 4), i.e. logical chunk 2t + (n % 4) / 2
-  const int tr_row = 4 * g + (n >> 2);
-  const int tr_sub = 4 * (n & 1);
-  const int tr_c = (n & 3) >> 1;
+  // Loop-invariant LDS read offsets (elements).  K operand of k-step s: row
+  // 16mt + n, logical chunk 4s + g.  V transposed read for dim block t: row
+  // 32kk + 16hi + 4g + n/4, logical chunk 2t + (n%4)/2, half (n%2).
+  int ka_off[KSTEPS], vb_off[DT];
+#pragma unroll
+  for (int s2 = 0; s2 < KSTEPS; ++s2) ka_off[s2] = n * D + (((4 * s2 + g) ^ (n & (CPR - 1))) * 8);
+  {
+    const int tr_row = 4 * g + (n >> 2);
+    const int swz = (tr_row & (CPR / 2 - 1)) << 1;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+      vb_off[t] = tr_row * D + (((2 * t + ((n & 3) >> 1)) ^ swz) * 8) + 4 * (n & 1);
+  }
   // A row's running max is only raised (and its accumulators rescaled) when
   // a tile's scores exceed it by more than 2^kLazy; otherwise the stale max
   // is kept, the weights stay <= 2^kLazy, and numerator and denominator
   // share it, so the quotient is unchanged.
   constexpr float kLazy = 8.f;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int kb0 = j * kBN;
-    const int stage = j & 1;
-    const bool more = j + 1 < ntiles;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies of tile j landed
-    __syncthreads();                     // tile j staged; tile j-1 fully consumed
-    if (more) copy_tile(kb0 + kBN, stage ^ 1);  // next tile streams during this one
-
-    if (any_head) {
-      const uint16_t* kt = lds[stage][0];
-      const uint16_t* vt = lds[stage][1];
-      // ---- S^T = K_tile . Q^T for both row tiles (raw q.k) ----
-      f32x4 st[2][4];
+  auto tile = [&](int kb0, auto stage_c) {
+    constexpr int ST = decltype(stage_c)::value;
+    const uint16_t* kt = lds[ST][0];
+    const uint16_t* vt = lds[ST][1];
+    // ---- S^T = K_tile . Q^T for both row tiles (raw q.k) ----
+    f32x4 st[2][4];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) st[jj][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int s2 = 0; s2 < KSTEPS; ++s2) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&kt[ka_off[s2] + 16 * mt * D]));
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          st[jj][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[jj][s2], st[jj][mt], 0, 0, 0);
+      }
+    }
+    if (kb0 + kBN > q0) {  // diagonal tile: drop keys after the row's position
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) st[jj][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          const int row = 16 * mt + n;
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              &kt[row * D + (((4 * s + g) ^ (row & (CPR - 1))) * 8)]));
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            st[jj][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[jj][s], st[jj][mt], 0, 0, 0);
-        }
-      }
-      if (kb0 + kBN > q0) {  // diagonal tile: drop keys after the row's position
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (kb0 + 16 * mt + 4 * g + i > pos_n) st[jj][mt][i] = -INFINITY;
-      }
-
-      // ---- online softmax per row tile ----
-      bf16x8 pa[2][2];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        float cmax = -INFINITY;
-#pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, st[jj][mt][i]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float cand = cmax * scale_log2;  // scale > 0
-        if (__any(cand > m_run[jj] + kLazy)) {
-          const float m_new = fmaxf(m_run[jj], cand);
-          const float alpha = fast_exp2(m_run[jj] - m_new);
-          m_run[jj] = m_new;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = __shfl(alpha, 4 * g + i);
-            lsum[jj][i] *= a;
-#pragma unroll
-            for (int t = 0; t < DT; ++t) acc[jj][t][i] *= a;
-          }
-        }
-        const float mneg = -m_run[jj];
-        uint32_t pw[8];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; i += 2)
-            pw[2 * mt + i / 2] = pack_bf16x2(fast_exp2(fmaf(st[jj][mt][i], scale_log2, mneg)),
-                                             fast_exp2(fmaf(st[jj][mt][i + 1], scale_log2, mneg)));
-        // P operand of 32-key step kk: score tiles mt = 2kk, 2kk+1
-        pa[jj][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
-        pa[jj][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
-      }
-
-      // ---- O += P . V_tile, and the denominators via the all-ones block ----
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const int r0 = 32 * kk + tr_row, r1 = r0 + 16;
-          const int cl = 2 * t + tr_c;
-          const uint2 lo = lds_read_tr16(vt + r0 * D + ((cl ^ (r0 & (CPR - 1))) * 8) + tr_sub);
-          const uint2 hi = lds_read_tr16(vt + r1 * D + ((cl ^ (r1 & (CPR - 1))) * 8) + tr_sub);
-          const bf16x8 vb = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            acc[jj][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[jj][kk], vb, acc[jj][t], 0, 0, 0);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          lsum[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[jj][kk], ones, lsum[jj], 0, 0, 0);
-      }
+          for (int i = 0; i < 4; ++i)
+            if (kb0 + 16 * mt + 4 * g + i > pos_n) st[jj][mt][i] = -INFINITY;
     }
+
+    // ---- online softmax per row tile ----
+    bf16x8 pa[2][2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, st[jj][mt][i]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float cand = cmax * scale_log2;  // scale > 0
+      if (__any(cand > m_run[jj] + kLazy)) {
+        const float m_new = fmaxf(m_run[jj], cand);
+        const float alpha = fast_exp2(m_run[jj] - m_new);
+        m_run[jj] = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = __shfl(alpha, 4 * g + i);
+          lsum[jj][i] *= a;
+#pragma unroll
+          for (int t = 0; t < DT; ++t) acc[jj][t][i] *= a;
+        }
+      }
+      const float mneg = -m_run[jj];
+      uint32_t pw[8];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2)
+          pw[2 * mt + i / 2] = pack_bf16x2(fast_exp2(fmaf(st[jj][mt][i], scale_log2, mneg)),
+                                           fast_exp2(fmaf(st[jj][mt][i + 1], scale_log2, mneg)));
+      // P operand of 32-key step kk: score tiles mt = 2kk, 2kk+1
+      pa[jj][0] = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+      pa[jj][1] = as_bf16x8(u32x4{pw[4], pw[5], pw[6], pw[7]});
+    }
+
+    // ---- O += P . V_tile, and the denominators via the all-ones block ----
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const uint2 lo = lds_read_tr16(vt + vb_off[t] + 32 * kk * D);
+        const uint2 hi = lds_read_tr16(vt + vb_off[t] + (32 * kk + 16) * D);
+        const bf16x8 vb = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          acc[jj][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[jj][kk], vb, acc[jj][t], 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        lsum[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[jj][kk], ones, lsum[jj], 0, 0, 0);
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  copy_tile(0, S0{});
+  // Tiles alternate between the two LDS stages; the loop is unrolled by two
+  // so each stage's addresses are compile-time offsets.
+  for (int j = 0; j < ntiles; j += 2) {
+    const int kb0 = j * kBN;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies of tile j landed
+    __syncthreads();                     // tile j staged; tile j-1 fully consumed
+    if (j + 1 < ntiles) copy_tile(kb0 + kBN, S1{});  // next tile streams during this one
+    if (any_head) tile(kb0, S0{});
+    if (j + 1 >= ntiles) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (j + 2 < ntiles) copy_tile(kb0 + 2 * kBN, S0{});
+    if (any_head) tile(kb0 + kBN, S1{});
   }
 
   // ---- normalise and store rows 4g+i of each row tile ----
