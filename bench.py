@@ -52,6 +52,29 @@ def parse():
     return ap.parse_args()
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch recorded from rocprofv3 counters for `kernel`
+    (profiles/traffic.json), or None when the kernel's sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(rec["read_bytes"] + rec["write_bytes"])
+
+
 def kv_bytes(lens, K, d, elem):
     return int(sum(2 * K * int(L) * d * elem for L in lens))
 
@@ -166,7 +189,8 @@ def bench_decode(args, w):
         "kv_bytes_per_step": int(total_bytes / args.steps),
         "roofline": {"kernel": "decode partition pass (decode_split_bf16_kernel)", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("decode_split_bf16_kernel"),
                      "avg_kernel_us": round(kern_avg_ms * 1e3, 3)},
         "input_gen_s": round(t_gen, 1),
     }
@@ -237,7 +261,8 @@ def bench_prefill(args, w):
         "tokens_per_s": round(w.B * w.L / (ms_per_step * 1e-3), 1),
         "roofline": {"kernel": "causal prefill (prefill_causal_kernel)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic("prefill_causal_kernel"),
                      "avg_kernel_us": round(kern_ms * 1e3, 3)},
         "input_gen_s": round(t_gen, 1),
     }

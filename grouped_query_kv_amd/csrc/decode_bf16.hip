@@ -48,7 +48,9 @@ namespace gqa {
 namespace {
 
 constexpr int kChunk = 32;   // positions per inner iteration
-constexpr int kVPad = 8;     // bf16 elements of padding per LDS row
+// bf16 elements of padding per LDS row: a 32-byte shift per row puts the
+// four rows of one 16-lane transposed read in distinct 32-byte bank groups
+constexpr int kVPad = 16;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;

@@ -46,6 +46,16 @@ def guards_intact(buf: torch.Tensor, guard: int, dtype) -> bool:
     return bool(torch.isnan(head).all() and torch.isnan(tail).all())
 
 
+def bf16_bound(ref: np.ndarray, v_absmax: float, weights_in_denominator: bool = False) -> float:
+    """Arithmetic error bound of a bf16 attention output.  Each softmax weight
+    is rounded to bf16 once (relative 2^-9) before multiplying V, and the
+    output is rounded once more (2^-9 |out|).  When the denominator also sums
+    the rounded weights (prefill) the weighted mean can move by up to twice
+    the weight error.  fp32 accumulation error is orders smaller."""
+    w = 2.0 ** -8 if weights_in_denominator else 2.0 ** -9
+    return w * v_absmax + 2.0 ** -9 * float(np.abs(ref).max()) + 1e-6
+
+
 def report(name: str, got: np.ndarray, ref: np.ndarray) -> dict:
     err = np.abs(got - ref)
     rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0

@@ -5,7 +5,7 @@ import torch
 
 import grouped_query_kv_amd as gqa
 from grouped_query_kv_amd.inputs import WORKLOADS, decode_inputs, workload_inputs
-from gpu_util import DEV, TOL, f64, guarded, guards_intact, note, report, run_decode, scale_of
+from gpu_util import DEV, TOL, bf16_bound, f64, guarded, guards_intact, note, report, run_decode, scale_of
 from oracle import decode_ref, kv_append_ref
 
 pytestmark = pytest.mark.gpu
@@ -22,6 +22,14 @@ def _oracle(inp, append=False):
                                        kc_n, vc_n, sl)
         return decode_ref(q, kc_n, vc_n, sl, scale_of(d))
     return decode_ref(q, kc.float().numpy(), vc.float().numpy(), sl, scale_of(d))
+
+
+def _vmax(inp):
+    """max |v| over the valid cache rows (and the appended rows)."""
+    v = inp["v_cache"]
+    m = max(float(v[b, :, :int(L)].float().abs().max()) if int(L) > 0 else 0.0
+            for b, L in enumerate(inp["seq_lens"].tolist()))
+    return max(m, float(inp["v_new"].float().abs().max()))
 
 
 # ---- the tiny fp32 workload and its MHA / MQA variants ----------------------
@@ -55,8 +63,11 @@ def test_decode_shapes(B, H, K, d, lens, dtype):
     note(f"decode B={B} H={H} K={K} d={d} lens={lens} {dtype}")
     inp = decode_inputs(B, H, K, d, dtype, seed=11, lens=lens)
     out, _ = run_decode(inp)
-    r = report("shape", f64(out), _oracle(inp))
+    ref = _oracle(inp)
+    r = report("shape", f64(out), ref)
     assert r["finite"] and r["max_abs"] <= TOL[dtype]
+    if dtype == "bf16":
+        assert r["max_abs"] <= bf16_bound(ref, _vmax(inp))
     zero = [b for b, L in enumerate(lens) if L == 0]
     for b in zero:
         assert torch.count_nonzero(out[b]).item() == 0
@@ -75,8 +86,10 @@ def test_decode_out_dtype_and_guards(out_dtype):
     gqa.gqa_decode(q, kc, vc, sl, out, ws, 500, scale=scale_of(d))
     torch.cuda.synchronize()
     assert guards_intact(buf, guard, out_dtype)
-    r = report("guards", f64(out), _oracle(inp))
+    ref = _oracle(inp)
+    r = report("guards", f64(out), ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+    assert r["max_abs"] <= bf16_bound(ref, _vmax(inp))
 
 
 def test_decode_is_deterministic():
@@ -121,3 +134,4 @@ def test_decode_full_workload(name):
         ref[b] = _oracle(sub, append=w.append)[0]
     r = report(name, got, ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+    assert r["max_abs"] <= bf16_bound(ref, _vmax(inp))

@@ -5,7 +5,7 @@ import torch
 
 import grouped_query_kv_amd as gqa
 from grouped_query_kv_amd.inputs import WORKLOADS, decode_inputs, prefill_inputs, workload_inputs
-from gpu_util import DEV, TOL, f64, guarded, guards_intact, note, report, run_decode, scale_of
+from gpu_util import DEV, TOL, bf16_bound, f64, guarded, guards_intact, note, report, run_decode, scale_of
 from oracle import prefill_causal_ref
 
 pytestmark = pytest.mark.gpu
@@ -17,6 +17,10 @@ def _run(inp, out_dtype=torch.bfloat16):
     gqa.gqa_prefill_causal(q, k, v, out, scale=scale_of(q.shape[-1]))
     torch.cuda.synchronize()
     return out
+
+
+def _vmax(inp, S):
+    return float(inp["v"][:, :, :S].float().abs().max())
 
 
 CASES = [
@@ -39,6 +43,7 @@ def test_prefill_shapes(B, H, K, S, d, S_max):
     ref = prefill_causal_ref(f64(inp["q"]), inp["k"].float().numpy(), inp["v"].float().numpy(), scale_of(d))
     r = report("prefill", f64(out), ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+    assert r["max_abs"] <= bf16_bound(ref, _vmax(inp, S), weights_in_denominator=True)
 
 
 def test_prefill_fp32_out_and_guards():
@@ -92,4 +97,5 @@ def test_prefill_full_workload_sampled_rows():
                              inp["k"].float().numpy(), inp["v"].float().numpy(), scale_of(w.d), rows=rows)
     r = report("prefill 4k sampled", out[:, :, rows], ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+    assert r["max_abs"] <= bf16_bound(ref, _vmax(inp, w.L), weights_in_denominator=True)
     assert np.all(np.isfinite(out))
