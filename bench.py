@@ -6,8 +6,9 @@ With --workload prefill_causal_4k it times the causal prefill instead (one
 step = one prefill of the whole batch; value in TFLOP/s of unmasked work).
 
 A step is one pass of the whole decode hot path over one batch: append the
-new token's K/V rows of every sequence (gqa_kv_append), then attend over the
-cache (gqa_decode: partition pass + combine pass).  The default workload is
+new token's K/V rows of every sequence and attend over the cache including
+them (gqa_decode_append: the append fused into the partition pass, then the
+combine pass -- the same work as gqa_kv_append followed by gqa_decode).  The default workload is
 the Llama-3-8B-shaped layer: B=16 sequences at 8192 cached tokens, 32 query
 heads over 8 KV heads, d=128, bf16 (synthetic N(0,1) data).
 
@@ -142,12 +143,15 @@ def bench_decode(args, w):
 
     def step(i, ev=None):
         c = copies[i % R]
-        if w.append:
-            gqa.gqa_kv_append(kn, vn, c["k"], c["v"], c["sl"], stream=stream)
-            host_lens[i % R] += 1
         if ev is not None:
             gqa.gqa_set_timing_events(ev[0], ev[1])
-        gqa.gqa_decode(q, c["k"], c["v"], c["sl"], out, ws, max_len, scale=scale, stream=stream)
+        if w.append:
+            # append + decode as one fused call (two kernel launches)
+            gqa.gqa_decode_append(q, kn, vn, c["k"], c["v"], c["sl"], out, ws, max_len,
+                                  scale=scale, stream=stream)
+            host_lens[i % R] += 1
+        else:
+            gqa.gqa_decode(q, c["k"], c["v"], c["sl"], out, ws, max_len, scale=scale, stream=stream)
         if ev is not None:
             gqa.gqa_set_timing_events(None, None)
 
@@ -187,7 +191,7 @@ def bench_decode(args, w):
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(total_bytes / args.steps),
-        "roofline": {"kernel": "decode partition pass (decode_split_bf16_kernel)", "bound": "hbm",
+        "roofline": {"kernel": "decode partition pass with fused append (decode_split_bf16_kernel)", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("decode_split_bf16_kernel"),

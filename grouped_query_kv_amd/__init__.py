@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     HipEvent,
     gqa_abi_version,
     gqa_decode,
+    gqa_decode_append,
     gqa_decode_workspace_bytes,
     gqa_kv_append,
     gqa_kv_cache_bytes,

@@ -62,12 +62,19 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-template <int D>
+// APPEND: fused cache append.  The step's new K/V rows (k_new, v_new) sit at
+// position L_in = seq_lens[b] (when the cache has room): the partition that
+// covers it reads that row from k_new/v_new and writes it into the cache
+// (head block 0 only; nothing else reads that row in this launch), and the
+// lengths after the append go to `lens_out` for the combine pass, which
+// publishes them to seq_lens.
+template <int D, bool APPEND>
 __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
+    const __bf16* __restrict__ q, __bf16* __restrict__ kc, __bf16* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
-    int head_blocks, float scale_log2) {
+    int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;        // contraction steps of Q.K
   constexpr int NTILES = D / 16;        // 16-wide output tiles of P.V
@@ -83,7 +90,15 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   const int hb = blockIdx.y - k * head_blocks;
   const int b = blockIdx.z;
   const int G = H / K;
-  const int L = seq_lens[b];
+  const int L_in = seq_lens[b];
+  int L = L_in, newpos = -1;
+  if (APPEND) {
+    if (L_in < S_max) {
+      newpos = L_in;
+      L = L_in + 1;
+    }
+    if (p == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens_out[b] = L;
+  }
   const int t0 = p * part_tokens;
   if (t0 >= L) return;  // partition beyond this sequence: nothing to do
   const int t1 = min(t0 + part_tokens, L);
@@ -104,8 +119,10 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   }
 
   const size_t head_base = ((size_t)b * K + k) * (size_t)S_max * D;
-  const __bf16* kbase = kc + head_base;
-  const __bf16* vbase = vc + head_base;
+  __bf16* kbase = kc + head_base;
+  __bf16* vbase = vc + head_base;
+  const __bf16* knew_row = APPEND ? k_new + ((size_t)b * K + k) * D : nullptr;
+  const __bf16* vnew_row = APPEND ? v_new + ((size_t)b * K + k) * D : nullptr;
 
   float m_run = -INFINITY;  // running max of head n (replicated over g)
   float l_run = 0.f;        // running sum of head n
@@ -125,7 +142,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int tok = c0 + 16 * mt + n;
-      const __bf16* krow = kbase + (size_t)tok * D + 8 * g;
+      const __bf16* krow = (APPEND && tok == newpos ? knew_row : kbase + (size_t)tok * D) + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = tok < t1 ? ld16(krow + 32 * s) : zero_u32x4();
     }
@@ -134,7 +151,8 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int tok = c0 + i * ROWS_PER_LOAD + vrow;
-      vr[i] = tok < t1 ? ld16(vbase + (size_t)tok * D + vcol) : zero_u32x4();
+      const __bf16* vrow_p = APPEND && tok == newpos ? vnew_row : vbase + (size_t)tok * D;
+      vr[i] = tok < t1 ? ld16(vrow_p + vcol) : zero_u32x4();
     }
   };
   load_k(t0);
@@ -208,6 +226,12 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
     __syncthreads();  // LDS reads done before the next chunk overwrites vt
   }
 
+  if (APPEND && hb == 0 && newpos >= t0 && newpos < t1 && lane < LANES_PER_ROW) {
+    // the appended rows join the cache (bit copy)
+    *reinterpret_cast<u32x4*>(kbase + (size_t)newpos * D + 8 * lane) = ld16(knew_row + 8 * lane);
+    *reinterpret_cast<u32x4*>(vbase + (size_t)newpos * D + 8 * lane) = ld16(vnew_row + 8 * lane);
+  }
+
   // ---- write the partition's partial state ----
   const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
 #pragma unroll
@@ -228,23 +252,29 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 
 }  // namespace
 
-hipError_t launch_decode_split_bf16(const void* q, const void* k_cache, const void* v_cache,
+hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const int32_t* seq_lens, const DecodeWorkspace& ws,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
-                                    float scale_log2, hipStream_t stream) {
+                                    float scale_log2, const void* k_new, const void* v_new,
+                                    hipStream_t stream) {
   const dim3 grid(plan.parts, K * plan.head_blocks, B);
   const dim3 block(64);
   auto qp = static_cast<const __bf16*>(q);
-  auto kp = static_cast<const __bf16*>(k_cache);
-  auto vp = static_cast<const __bf16*>(v_cache);
-  if (d == 128)
-    hipLaunchKernelGGL(decode_split_bf16_kernel<128>, grid, block, 0, stream, qp, kp, vp, seq_lens,
-                       ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts,
-                       plan.head_blocks, scale_log2);
-  else
-    hipLaunchKernelGGL(decode_split_bf16_kernel<64>, grid, block, 0, stream, qp, kp, vp, seq_lens,
-                       ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts,
-                       plan.head_blocks, scale_log2);
+  auto kp = static_cast<__bf16*>(k_cache);
+  auto vp = static_cast<__bf16*>(v_cache);
+  auto kn = static_cast<const __bf16*>(k_new);
+  auto vn = static_cast<const __bf16*>(v_new);
+  const bool app = k_new != nullptr;
+#define GQA_SPLIT(DD, AP)                                                                         \
+  hipLaunchKernelGGL((decode_split_bf16_kernel<DD, AP>), grid, block, 0, stream, qp, kp, vp,      \
+                     seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts, \
+                     plan.head_blocks, scale_log2, kn, vn, ws.lens)
+  if (d == 128) {
+    if (app) GQA_SPLIT(128, true); else GQA_SPLIT(128, false);
+  } else {
+    if (app) GQA_SPLIT(64, true); else GQA_SPLIT(64, false);
+  }
+#undef GQA_SPLIT
   return hipGetLastError();
 }
 

@@ -17,17 +17,20 @@
 namespace gqa {
 namespace {
 
-template <int D, bool OUT_BF16>
+// LENS_FROM_WS: after a fused append the lengths come from the workspace
+// (written by the partition pass), and the (b, h = 0) workgroup publishes them
+// to seq_lens -- no workgroup of this pass reads seq_lens, so there is no race.
+template <int D, bool OUT_BF16, bool LENS_FROM_WS>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ seq_lens, void* __restrict__ out, int H, int part_tokens,
-    int parts) {
+    int32_t* __restrict__ seq_lens, const int32_t* __restrict__ ws_lens, void* __restrict__ out,
+    int H, int part_tokens, int parts) {
   constexpr int PER = D / 64;  // dims per lane
   __shared__ float wsh[64];
   const int bh = blockIdx.x;
   const int b = bh / H;
   const int lane = threadIdx.x;
-  const int L = seq_lens[b];
+  const int L = LENS_FROM_WS ? ws_lens[b] : seq_lens[b];
   const int n = L > 0 ? min(parts, (L + part_tokens - 1) / part_tokens) : 0;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)bh * parts;
   const float* pa = part_acc + (size_t)bh * parts * D + lane * PER;
@@ -72,6 +75,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
   const float inv = n > 0 ? 1.f / den : 0.f;
+  if (LENS_FROM_WS && bh - b * H == 0 && lane == 0) seq_lens[b] = L;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const float o = n > 0 ? num[j] * inv : 0.f;
@@ -85,18 +89,25 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 
 }  // namespace
 
-hipError_t launch_decode_combine(const DecodeWorkspace& ws, const int32_t* seq_lens, void* out,
+hipError_t launch_decode_combine(const DecodeWorkspace& ws, int32_t* seq_lens, void* out,
                                  const DecodePlan& plan, int B, int H, int d, bool out_bf16,
-                                 hipStream_t stream) {
+                                 bool lens_from_ws, hipStream_t stream) {
   const dim3 grid(B * H), block(64);
-#define GQA_COMBINE(DD, OB)                                                                     \
-  hipLaunchKernelGGL((decode_combine_kernel<DD, OB>), grid, block, 0, stream, ws.part_acc,      \
-                     ws.part_ml, seq_lens, out, H, plan.part_tokens, plan.parts)
-  if (d == 128) {
-    if (out_bf16) GQA_COMBINE(128, true); else GQA_COMBINE(128, false);
-  } else {
-    if (out_bf16) GQA_COMBINE(64, true); else GQA_COMBINE(64, false);
+#define GQA_COMBINE(DD, OB, LW)                                                                  \
+  hipLaunchKernelGGL((decode_combine_kernel<DD, OB, LW>), grid, block, 0, stream, ws.part_acc,   \
+                     ws.part_ml, seq_lens, ws.lens, out, H, plan.part_tokens, plan.parts)
+#define GQA_COMBINE_D(DD)                                                                        \
+  if (out_bf16) {                                                                                \
+    if (lens_from_ws) GQA_COMBINE(DD, true, true); else GQA_COMBINE(DD, true, false);            \
+  } else {                                                                                       \
+    if (lens_from_ws) GQA_COMBINE(DD, false, true); else GQA_COMBINE(DD, false, false);          \
   }
+  if (d == 128) {
+    GQA_COMBINE_D(128)
+  } else {
+    GQA_COMBINE_D(64)
+  }
+#undef GQA_COMBINE_D
 #undef GQA_COMBINE
   return hipGetLastError();
 }

@@ -27,12 +27,14 @@ constexpr int kThreads = 256;
 constexpr int kChunkF = 64;
 constexpr int kHB = 16;  // heads per block
 
-template <int D>
+// APPEND: fused cache append, as in decode_bf16.hip.
+template <int D, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
-    const float* __restrict__ q, const float* __restrict__ kc, const float* __restrict__ vc,
+    const float* __restrict__ q, float* __restrict__ kc, float* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
-    int head_blocks, float scale_log2) {
+    int head_blocks, float scale_log2, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, int32_t* __restrict__ lens_out) {
   constexpr int HEADS_PER_THREAD = kHB * D / kThreads;  // 8 (D=128) or 4 (D=64)
 
   __shared__ float qs[kHB][D];
@@ -46,7 +48,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
   const int hb = blockIdx.y - k * head_blocks;
   const int b = blockIdx.z;
   const int G = H / K;
-  const int L = seq_lens[b];
+  const int L_in = seq_lens[b];
+  int L = L_in, newpos = -1;
+  if (APPEND) {
+    if (L_in < S_max) {
+      newpos = L_in;
+      L = L_in + 1;
+    }
+    if (p == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens_out[b] = L;
+  }
   const int t0 = p * part_tokens;
   if (t0 >= L) return;
   const int t1 = min(t0 + part_tokens, L);
@@ -66,8 +76,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
     l_s[tid] = 0.f;
   }
   const size_t head_base = ((size_t)b * K + k) * (size_t)S_max * D;
-  const float* kbase = kc + head_base;
-  const float* vbase = vc + head_base;
+  float* kbase = kc + head_base;
+  float* vbase = vc + head_base;
+  const float* knew_row = APPEND ? k_new + ((size_t)b * K + k) * D : nullptr;
+  const float* vnew_row = APPEND ? v_new + ((size_t)b * K + k) * D : nullptr;
 
   const int c_own = tid % D;            // value dimension owned in phase 3
   const int slice = tid / D;            // head slice owned in phase 3
@@ -84,7 +96,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
       const int h0 = tid / kChunkF;  // 0..3
       float s[4] = {0.f, 0.f, 0.f, 0.f};
       if (t < n_tok) {
-        const float4* krow = reinterpret_cast<const float4*>(kbase + (size_t)(c0 + t) * D);
+        const float* krow_p = APPEND && c0 + t == newpos ? knew_row : kbase + (size_t)(c0 + t) * D;
+        const float4* krow = reinterpret_cast<const float4*>(krow_p);
 #pragma unroll 4
         for (int c4 = 0; c4 < D / 4; ++c4) {
           const float4 kv = krow[c4];
@@ -130,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
 #pragma unroll
     for (int j = 0; j < HEADS_PER_THREAD; ++j) acc[j] *= alpha_s[slice * HEADS_PER_THREAD + j];
     for (int t = 0; t < n_tok; ++t) {
-      const float v = vbase[(size_t)(c0 + t) * D + c_own];
+      const float v = APPEND && c0 + t == newpos ? vnew_row[c_own] : vbase[(size_t)(c0 + t) * D + c_own];
 #pragma unroll
       for (int j = 0; j < HEADS_PER_THREAD; ++j)
         acc[j] = fmaf(ps[slice * HEADS_PER_THREAD + j][t], v, acc[j]);
@@ -138,6 +151,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
     __syncthreads();
   }
 
+  if (APPEND && hb == 0 && newpos >= t0 && newpos < t1 && tid < D) {
+    // the appended rows join the cache
+    kbase[(size_t)newpos * D + tid] = knew_row[tid];
+    vbase[(size_t)newpos * D + tid] = vnew_row[tid];
+  }
 #pragma unroll
   for (int j = 0; j < HEADS_PER_THREAD; ++j) {
     const int h = slice * HEADS_PER_THREAD + j;
@@ -152,23 +170,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_decode_split_f32(const void* q, const void* k_cache, const void* v_cache,
+hipError_t launch_decode_split_f32(const void* q, void* k_cache, void* v_cache,
                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
-                                   float scale_log2, hipStream_t stream) {
+                                   float scale_log2, const void* k_new, const void* v_new,
+                                   hipStream_t stream) {
   const dim3 grid(plan.parts, K * plan.head_blocks, B);
   const dim3 block(kThreads);
   auto qp = static_cast<const float*>(q);
-  auto kp = static_cast<const float*>(k_cache);
-  auto vp = static_cast<const float*>(v_cache);
-  if (d == 128)
-    hipLaunchKernelGGL(decode_split_f32_kernel<128>, grid, block, 0, stream, qp, kp, vp, seq_lens,
-                       ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts,
-                       plan.head_blocks, scale_log2);
-  else
-    hipLaunchKernelGGL(decode_split_f32_kernel<64>, grid, block, 0, stream, qp, kp, vp, seq_lens,
-                       ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts,
-                       plan.head_blocks, scale_log2);
+  auto kp = static_cast<float*>(k_cache);
+  auto vp = static_cast<float*>(v_cache);
+  auto kn = static_cast<const float*>(k_new);
+  auto vn = static_cast<const float*>(v_new);
+  const bool app = k_new != nullptr;
+#define GQA_SPLIT(DD, AP)                                                                         \
+  hipLaunchKernelGGL((decode_split_f32_kernel<DD, AP>), grid, block, 0, stream, qp, kp, vp,       \
+                     seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts, \
+                     plan.head_blocks, scale_log2, kn, vn, ws.lens)
+  if (d == 128) {
+    if (app) GQA_SPLIT(128, true); else GQA_SPLIT(128, false);
+  } else {
+    if (app) GQA_SPLIT(64, true); else GQA_SPLIT(64, false);
+  }
+#undef GQA_SPLIT
   return hipGetLastError();
 }
 

@@ -94,14 +94,19 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d) {
   const size_t rows = (size_t)B * H * p.parts;
-  return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float));
+  return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float)) +
+         align256((size_t)B * sizeof(int32_t));
 }
 
 DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d) {
   const size_t rows = (size_t)B * H * p.parts;
+  char* c = static_cast<char*>(base);
   DecodeWorkspace w;
-  w.part_acc = static_cast<float*>(base);
-  w.part_ml = reinterpret_cast<float*>(static_cast<char*>(base) + align256(rows * d * sizeof(float)));
+  w.part_acc = reinterpret_cast<float*>(c);
+  c += align256(rows * d * sizeof(float));
+  w.part_ml = reinterpret_cast<float*>(c);
+  c += align256(rows * 2 * sizeof(float));
+  w.lens = reinterpret_cast<int32_t*>(c);
   return w;
 }
 
@@ -156,30 +161,33 @@ size_t gqa_decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d) {
   return gqa::decode_workspace_bytes(p, B, H, d);
 }
 
-int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-               void* out, void* workspace, size_t workspace_bytes, int B, int H, int K, int S_max,
-               int max_seq_len, int d, float scale, int dtype, int out_dtype, void* stream) {
-  if (!q || !k_cache || !v_cache || !seq_lens || !out)
-    return fail(GQA_ERR_INVALID, "gqa_decode: null pointer");
-  if (int r = validate_heads("gqa_decode", B, H, K, d)) return r;
+// Shared body of gqa_decode and gqa_decode_append (k_new == nullptr: no append).
+static int decode_impl(const char* fn, const void* q, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, int32_t* seq_lens, void* out, void* workspace,
+                       size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len,
+                       int d, float scale, int dtype, int out_dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !out) return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (int r = validate_heads(fn, B, H, K, d)) return r;
   if (S_max < 1 || max_seq_len < 0 || max_seq_len > S_max)
-    return fail(GQA_ERR_INVALID, "gqa_decode: need 0 <= max_seq_len <= S_max, S_max >= 1");
-  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(GQA_ERR_INVALID, "gqa_decode: scale must be finite and > 0");
+    return fail(GQA_ERR_INVALID, "%s: need 0 <= max_seq_len <= S_max, S_max >= 1", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(GQA_ERR_INVALID, "%s: scale must be finite and > 0", fn);
   if (dtype == GQA_F32) {
-    if (out_dtype != GQA_F32) return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: f32 input needs f32 output");
+    if (out_dtype != GQA_F32) return fail(GQA_ERR_UNSUPPORTED, "%s: f32 input needs f32 output", fn);
   } else if (dtype == GQA_BF16) {
     if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
-      return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: out_dtype %d", out_dtype);
+      return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
   } else {
-    return fail(GQA_ERR_UNSUPPORTED, "gqa_decode: dtype %d", dtype);
+    return fail(GQA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
   }
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
-    return fail(GQA_ERR_INVALID, "gqa_decode: misaligned pointer");
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
   const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d);
   const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
-    return fail(GQA_ERR_WORKSPACE, "gqa_decode: workspace needs %zu bytes (16-byte aligned), got %zu",
+    return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
                 need, workspace ? workspace_bytes : (size_t)0);
   const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, H, d);
   const float scale_log2 = scale * gqa::kLog2eHost;
@@ -189,15 +197,35 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
     TimedRegion timed(s);
     r = check_hip(dtype == GQA_BF16
                       ? gqa::launch_decode_split_bf16(q, k_cache, v_cache, seq_lens, ws, plan, B, H,
-                                                      K, S_max, d, scale_log2, s)
+                                                      K, S_max, d, scale_log2, k_new, v_new, s)
                       : gqa::launch_decode_split_f32(q, k_cache, v_cache, seq_lens, ws, plan, B, H,
-                                                     K, S_max, d, scale_log2, s),
-                  "gqa_decode partition launch");
+                                                     K, S_max, d, scale_log2, k_new, v_new, s),
+                  "partition-pass launch");
   }
   if (r) return r;
-  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16, s),
-                "gqa_decode combine launch");
+  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16,
+                                           k_new != nullptr, s),
+                "combine-pass launch");
   return r ? r : ok();
+}
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+               void* out, void* workspace, size_t workspace_bytes, int B, int H, int K, int S_max,
+               int max_seq_len, int d, float scale, int dtype, int out_dtype, void* stream) {
+  // read-only use of the caches and lengths (no append)
+  return decode_impl("gqa_decode", q, nullptr, nullptr, const_cast<void*>(k_cache),
+                     const_cast<void*>(v_cache), const_cast<int32_t*>(seq_lens), out, workspace,
+                     workspace_bytes, B, H, K, S_max, max_seq_len, d, scale, dtype, out_dtype, stream);
+}
+
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, int32_t* seq_lens, void* out, void* workspace,
+                      size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len, int d,
+                      float scale, int dtype, int out_dtype, void* stream) {
+  if (!k_new || !v_new) return fail(GQA_ERR_INVALID, "gqa_decode_append: null pointer");
+  return decode_impl("gqa_decode_append", q, k_new, v_new, k_cache, v_cache, seq_lens, out,
+                     workspace, workspace_bytes, B, H, K, S_max, max_seq_len, d, scale, dtype,
+                     out_dtype, stream);
 }
 
 int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B, int H, int K,

@@ -21,14 +21,17 @@ struct DecodePlan {
 
 DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d);
 
-// Workspace layout of a decode call (all fp32):
-//   part_acc [B*H][parts][d]   un-normalised partial outputs
-//   part_ml  [B*H][parts][2]   running max (log2 units) and running sum
+// Workspace layout of a decode call:
+//   part_acc [B*H][parts][d]   fp32 un-normalised partial outputs
+//   part_ml  [B*H][parts][2]   fp32 running max (log2 units) and running sum
+//   lens     [B]               int32 lengths after a fused append
 struct DecodeWorkspace {
   float* part_acc;
   float* part_ml;
+  int32_t* lens;
 };
 size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d);
+// (the workspace holds part_acc, part_ml and lens, each 256-byte aligned)
 DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d);
 
 // ---- launchers (each returns the hipGetLastError() of its launch) ----
@@ -37,22 +40,26 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                             int32_t* seq_lens, int B, int K, int S_max, int row_bytes,
                             hipStream_t stream);
 
-// Partition pass, bf16 inputs, matrix-core (MFMA) contraction.
-hipError_t launch_decode_split_bf16(const void* q, const void* k_cache, const void* v_cache,
+// Partition pass, bf16 inputs, matrix-core (MFMA) contraction.  With
+// k_new/v_new non-null the step's append is fused in (caches are written).
+hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const int32_t* seq_lens, const DecodeWorkspace& ws,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
-                                    float scale_log2, hipStream_t stream);
+                                    float scale_log2, const void* k_new, const void* v_new,
+                                    hipStream_t stream);
 
-// Partition pass, fp32 inputs, vector-ALU contraction.
-hipError_t launch_decode_split_f32(const void* q, const void* k_cache, const void* v_cache,
+// Partition pass, fp32 inputs, vector-ALU contraction (same append option).
+hipError_t launch_decode_split_f32(const void* q, void* k_cache, void* v_cache,
                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
-                                   float scale_log2, hipStream_t stream);
+                                   float scale_log2, const void* k_new, const void* v_new,
+                                   hipStream_t stream);
 
-// Combine pass: partials -> out (fp32 or bf16).
-hipError_t launch_decode_combine(const DecodeWorkspace& ws, const int32_t* seq_lens, void* out,
+// Combine pass: partials -> out (fp32 or bf16).  lens_from_ws: lengths come
+// from the workspace (fused append) and are published to seq_lens.
+hipError_t launch_decode_combine(const DecodeWorkspace& ws, int32_t* seq_lens, void* out,
                                  const DecodePlan& plan, int B, int H, int d, bool out_bf16,
-                                 hipStream_t stream);
+                                 bool lens_from_ws, hipStream_t stream);
 
 hipError_t launch_prefill_causal_bf16(const void* q, const void* k, const void* v, void* out,
                                       int B, int H, int K, int S, int S_max, int d,

@@ -105,6 +105,25 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                int dtype, int out_dtype, void* stream);
 
 /*
+ * One decode step with the cache append fused in: the same result as
+ * gqa_kv_append(k_new, v_new, k_cache, v_cache, seq_lens, ...) followed by
+ * gqa_decode(q, k_cache, v_cache, seq_lens, out, ...) -- caches and
+ * seq_lens end up bit-identical, out within the decode tolerance -- in two
+ * kernel launches instead of three: the partition holding the new position
+ * takes that row from k_new/v_new and writes it into the cache.  A sequence
+ * whose cache is full (seq_lens[b] == S_max) gets no append and attends over
+ * its S_max rows.  max_seq_len bounds the lengths *after* the append.
+ * (pinghaoyang.com.cn, decode memory ledger: each step appends the new K/V
+ * row and the new query attends to every cached row including it.)
+ * Arguments as gqa_kv_append and gqa_decode; workspace sized by
+ * gqa_decode_workspace_bytes(B, H, K, max_seq_len, d).
+ */
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, int32_t* seq_lens, void* out, void* workspace,
+                      size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len,
+                      int d, float scale, int dtype, int out_dtype, void* stream);
+
+/*
  * Causal GQA attention over a whole prefix (prefill):
  *   out[b, h, i, :] = sum_{j <= i} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
  * for i in [0, S).  k and v are [B, K, S_max, d] with S <= S_max; rows >= S
@@ -137,8 +156,8 @@ int gqa_meanpool_convert(const void* src, void* dst, int64_t outer, int H, int K
 uint64_t gqa_kv_cache_bytes(int layers, int K, int d, int elem_bytes, uint64_t tokens);
 
 /*
- * Benchmark timing hook.  While set (both non-NULL), gqa_decode and
- * gqa_prefill_causal record `begin_event` on their stream immediately before
+ * Benchmark timing hook.  While set (both non-NULL), gqa_decode,
+ * gqa_decode_append and gqa_prefill_causal record `begin_event` on their stream immediately before
  * launching their main kernel and `end_event` immediately after it; the
  * events are hipEvent_t handles passed as void*, owned by the caller.
  * Applies to calls from the calling thread only; pass NULLs to clear.

@@ -23,7 +23,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = gqa.header_symbols()
-    assert {"gqa_kv_append", "gqa_decode", "gqa_prefill_causal", "gqa_meanpool_convert"} <= set(declared)
+    assert {"gqa_kv_append", "gqa_decode", "gqa_decode_append", "gqa_prefill_causal",
+            "gqa_meanpool_convert"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), f"libgqa.so does not export {name}"
 
@@ -81,6 +82,14 @@ def _decode(lib, **kw):
 def test_decode_rejects(lib, kw, code):
     assert _decode(lib, **kw) == code
     assert lib.gqa_last_error().decode().startswith("gqa_decode")
+
+
+@pytest.mark.parametrize("kn,vn,code", [(None, FAKE, B.GQA_ERR_INVALID), (FAKE, None, B.GQA_ERR_INVALID),
+                                         (FAKE + 4, FAKE, B.GQA_ERR_INVALID)])
+def test_decode_append_rejects(lib, kn, vn, code):
+    rc = lib.gqa_decode_append(FAKE, kn, vn, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 8, 2, 64, 64, 128,
+                               0.088, B.GQA_BF16, B.GQA_BF16, None)
+    assert rc == code and lib.gqa_last_error().decode().startswith("gqa_decode_append")
 
 
 @pytest.mark.parametrize("args,code", [

@@ -1,0 +1,93 @@
+"""GPU parity of the fused step gqa_decode_append (append + decode in two launches)."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_kv_amd as gqa
+from grouped_query_kv_amd.inputs import WORKLOADS, decode_inputs, workload_inputs
+from gpu_util import DEV, TOL, bf16_bound, f64, note, report, scale_of
+from oracle import decode_ref, kv_append_ref
+
+pytestmark = pytest.mark.gpu
+
+_INT = {torch.bfloat16: torch.int16, torch.float32: torch.int32}
+
+
+def _fused(inp, max_seq_len, out_dtype=None):
+    q, kc, vc = inp["q"].to(DEV), inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    sl = inp["seq_lens"].to(DEV)
+    B, H, d = q.shape
+    K = kc.shape[1]
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, max_seq_len, d), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, H, d), dtype=out_dtype or q.dtype, device=DEV)
+    gqa.gqa_decode_append(q, inp["k_new"].to(DEV), inp["v_new"].to(DEV), kc, vc, sl, out, ws,
+                          max_seq_len, scale=scale_of(d))
+    torch.cuda.synchronize()
+    return out, kc, vc, sl
+
+
+def _unfused(inp, max_seq_len, out_dtype=None):
+    q, kc, vc = inp["q"].to(DEV), inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    sl = inp["seq_lens"].to(DEV)
+    B, H, d = q.shape
+    K = kc.shape[1]
+    gqa.gqa_kv_append(inp["k_new"].to(DEV), inp["v_new"].to(DEV), kc, vc, sl)
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, max_seq_len, d), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, H, d), dtype=out_dtype or q.dtype, device=DEV)
+    gqa.gqa_decode(q, kc, vc, sl, out, ws, max_seq_len, scale=scale_of(d))
+    torch.cuda.synchronize()
+    return out, kc, vc, sl
+
+
+CASES = [
+    # B, H, K, d, lens, S_max, dtype
+    (4, 32, 8, 128, [0, 1, 700, 4095], 4096, "bf16"),   # empty, one row, middle, last free row
+    (3, 16, 4, 64, [31, 32, 33], 40, "bf16"),
+    (2, 64, 8, 128, [511, 2048], 2049, "bf16"),
+    (2, 56, 8, 128, [300, 300], 300, "bf16"),           # full caches: no append
+    (2, 71, 1, 64, [100, 257], 300, "bf16"),
+    (3, 12, 4, 128, [0, 63, 200], 256, "f32"),
+    (2, 16, 16, 64, [64, 64], 64, "f32"),               # full caches, fp32
+]
+
+
+@pytest.mark.parametrize("B,H,K,d,lens,S_max,dtype", CASES)
+def test_fused_step_vs_oracle_and_unfused(B, H, K, d, lens, S_max, dtype):
+    note(f"fused step B={B} H={H} K={K} d={d} lens={lens} S_max={S_max} {dtype}")
+    inp = decode_inputs(B, H, K, d, dtype, seed=17, lens=lens, s_max=S_max)
+    msl = min(max(lens) + 1, S_max)
+    out, kc, vc, sl = _fused(inp, msl)
+    out2, kc2, vc2, sl2 = _unfused(inp, msl)
+    # caches and lengths: bit-identical to the oracle's append and to the unfused path
+    it = _INT[inp["k_cache"].dtype]
+    k_ref, v_ref, s_ref = kv_append_ref(inp["k_new"].view(it).numpy(), inp["v_new"].view(it).numpy(),
+                                        inp["k_cache"].view(it).numpy(), inp["v_cache"].view(it).numpy(),
+                                        inp["seq_lens"].numpy())
+    assert np.array_equal(sl.cpu().numpy(), s_ref)
+    assert np.array_equal(kc.cpu().view(it).numpy(), k_ref) and np.array_equal(vc.cpu().view(it).numpy(), v_ref)
+    # same plan, same arithmetic: the fused output equals the unfused one bit for bit
+    assert torch.equal(out, out2) and torch.equal(sl, sl2)
+    # oracle decode over the oracle-appended caches (bit-identical to kc, vc)
+    ref = decode_ref(f64(inp["q"]), kc.cpu().float().numpy(), vc.cpu().float().numpy(), s_ref, scale_of(d))
+    r = report("fused", f64(out), ref)
+    assert r["finite"] and r["max_abs"] <= TOL[dtype]
+    if dtype == "bf16":
+        vmax = float(vc.cpu().float().nan_to_num(0.0).abs().max())
+        assert r["max_abs"] <= bf16_bound(ref, vmax)
+
+
+def test_fused_step_full_workload():
+    w = WORKLOADS["decode_llama3_8b"]
+    inp = workload_inputs(w, seed=0)
+    note("fused step on the Llama-3-8B layer")
+    out, kc, vc, sl = _fused(inp, w.L + 1)
+    assert sl.cpu().tolist() == [w.L + 1] * w.B
+    ref = np.zeros(tuple(out.shape))
+    for b in range(w.B):
+        k2, v2, s2 = kv_append_ref(inp["k_new"][b:b + 1].float().numpy(), inp["v_new"][b:b + 1].float().numpy(),
+                                   inp["k_cache"][b:b + 1].float().numpy(), inp["v_cache"][b:b + 1].float().numpy(),
+                                   inp["seq_lens"][b:b + 1].numpy())
+        ref[b] = decode_ref(f64(inp["q"][b:b + 1]), k2, v2, s2, scale_of(w.d))[0]
+        assert torch.equal(kc[b, :, w.L].cpu(), inp["k_new"][b]) and torch.equal(vc[b, :, w.L].cpu(), inp["v_new"][b])
+    r = report("fused llama3_8b", f64(out), ref)
+    assert r["finite"] and r["max_abs"] <= TOL["bf16"]
