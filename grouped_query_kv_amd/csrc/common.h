@@ -18,6 +18,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast
 // 16-byte global load (the address must be 16-byte aligned).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
 
+// 16-byte streaming load for data read exactly once (non-temporal hint:
+// the line is not kept in the caches for reuse).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 

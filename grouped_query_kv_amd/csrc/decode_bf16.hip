@@ -40,7 +40,8 @@
 // of its B operand; two such reads give the eight contraction slots.
 //
 // Loads of chunk c+1 are issued before the arithmetic of chunk c so the
-// wavefront always has a chunk of K and V in flight.
+// wavefront always has a chunk of K and V in flight.  The cache is streamed
+// with non-temporal loads (every byte is read once per step).
 #include "common.h"
 #include "gqa_internal.h"
 
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       const int tok = c0 + 16 * mt + n;
       const __bf16* krow = (APPEND && tok == newpos ? knew_row : kbase + (size_t)tok * D) + 8 * g;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = tok < t1 ? ld16(krow + 32 * s) : zero_u32x4();
+      for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = tok < t1 ? ld16_stream(krow + 32 * s) : zero_u32x4();
     }
   };
   auto load_v = [&](int c0) {
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
     for (int i = 0; i < VLOADS; ++i) {
       const int tok = c0 + i * ROWS_PER_LOAD + vrow;
       const __bf16* vrow_p = APPEND && tok == newpos ? vnew_row : vbase + (size_t)tok * D;
-      vr[i] = tok < t1 ? ld16(vrow_p + vcol) : zero_u32x4();
+      vr[i] = tok < t1 ? ld16_stream(vrow_p + vcol) : zero_u32x4();
     }
   };
   load_k(t0);

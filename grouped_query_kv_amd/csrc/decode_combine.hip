@@ -35,14 +35,24 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)bh * parts;
   const float* pa = part_acc + (size_t)bh * parts * D + lane * PER;
 
-  // pass 1: global max over the partitions (lane-parallel loads)
+  // The first kEarly partitions' numerators are loaded up front, together
+  // with the (max, sum) pairs, so the common case costs one memory round
+  // trip after the length; any further partitions are streamed below.
+  constexpr int kEarly = 32;
+  float early[kEarly][PER];
+#pragma unroll
+  for (int p = 0; p < kEarly; ++p)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) early[p][j] = p < n ? pa[(size_t)p * D + j] : 0.f;
+
+  // global max over the partitions (lane-parallel loads)
   float M = -INFINITY;
   for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p].x);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
-  // pass 2: weights of up to 64 partitions at a time, shared through LDS;
-  // every lane then sums its dims over those partitions with independent loads
+  // weights of up to 64 partitions at a time, shared through LDS; every lane
+  // then sums its dims over those partitions
   float num[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) num[j] = 0.f;
@@ -58,17 +68,19 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     wsh[lane] = w;
     __syncthreads();
     const int cnt = min(64, n - p0);
-#pragma unroll 8
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = wsh[j];
-      const float* src = pa + (size_t)(p0 + j) * D;
-      if (PER == 2) {
-        const float2 a = *reinterpret_cast<const float2*>(src);
-        num[0] = fmaf(wj, a.x, num[0]);
-        num[PER - 1] = fmaf(wj, a.y, num[PER - 1]);
-      } else {
-        num[0] = fmaf(wj, src[0], num[0]);
+    if (p0 == 0) {
+#pragma unroll
+      for (int q = 0; q < kEarly; ++q) {
+        const float wq = wsh[q];  // zero beyond n
+#pragma unroll
+        for (int j = 0; j < PER; ++j) num[j] = fmaf(wq, early[q][j], num[j]);
       }
+    }
+    for (int j2 = p0 == 0 ? kEarly : 0; j2 < cnt; ++j2) {
+      const float wj = wsh[j2];
+      const float* src = pa + (size_t)(p0 + j2) * D;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) num[j] = fmaf(wj, src[j], num[j]);
     }
     __syncthreads();
   }
