@@ -211,16 +211,18 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
     bf16x8 pa[2][2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      float cmax = -INFINITY;
+      // lane-local max of this lane's 16 scores of row n; the wave only
+      // needs the row's exact max (a cross-lane reduction) when some score
+      // exceeds the stale max by more than 2^kLazy
+      float lmax = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, st[jj][mt][i]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float cand = cmax * scale_log2;  // scale > 0
-      if (__any(cand > m_run[jj] + kLazy)) {
-        const float m_new = fmaxf(m_run[jj], cand);
+        for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, st[jj][mt][i]);
+      if (__any(lmax * scale_log2 > m_run[jj] + kLazy)) {  // scale > 0
+        float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        const float m_new = fmaxf(m_run[jj], cmax * scale_log2);
         const float alpha = fast_exp2(m_run[jj] - m_new);
         m_run[jj] = m_new;
 #pragma unroll
