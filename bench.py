@@ -8,7 +8,9 @@ step = one prefill of the whole batch; value in TFLOP/s of unmasked work).
 A step is one pass of the whole decode hot path over one batch: append the
 new token's K/V rows of every sequence and attend over the cache including
 them (gqa_decode_append: the append fused into the partition pass, then the
-combine pass -- the same work as gqa_kv_append followed by gqa_decode).  The default workload is
+combine pass -- the same work as gqa_kv_append followed by gqa_decode).  A
+paged workload (decode_paged_llama3_8b) runs gqa_kv_append_paged and then
+gqa_decode_paged over 16-row blocks in shuffled physical order.  The default workload is
 the Llama-3-8B-shaped layer: B=16 sequences at 8192 cached tokens, 32 query
 heads over 8 KV heads, d=128, bf16 (synthetic N(0,1) data).
 
@@ -85,8 +87,10 @@ def cpu_baseline_decode(inp, w, budget_s):
     one BLAS thread, until about `budget_s` seconds have been spent."""
     from threadpoolctl import threadpool_limits
 
-    from oracle import decode_ref, kv_append_ref
+    from grouped_query_kv_amd.inputs import paged_layout
+    from oracle import decode_paged_ref, decode_ref, kv_append_paged_ref, kv_append_ref
 
+    paged = "block_size" in w.extra
     d = w.d
     scale = float(np.float32(1.0 / math.sqrt(d)))
     done_bytes, done_seqs, t_used = 0, 0, 0.0
@@ -99,24 +103,35 @@ def cpu_baseline_decode(inp, w, budget_s):
             vc = inp["v_cache"][b:b + 1].float().numpy()
             kn = inp["k_new"][b:b + 1].float().numpy()
             vn = inp["v_new"][b:b + 1].float().numpy()
-            t0 = time.perf_counter()
-            if w.append:
-                kc, vc, sl = kv_append_ref(kn, vn, kc, vc, sl)
-            decode_ref(q, kc, vc, sl, scale)
-            t_used += time.perf_counter() - t0
+            if paged:
+                pg = paged_layout({"k_cache": inp["k_cache"][b:b + 1], "v_cache": inp["v_cache"][b:b + 1]},
+                                  w.extra["block_size"], seed=b)
+                kp, vp = pg["k_pool"].float().numpy(), pg["v_pool"].float().numpy()
+                bt = pg["block_table"].numpy()
+                t0 = time.perf_counter()
+                if w.append:
+                    kp, vp, sl = kv_append_paged_ref(kn, vn, kp, vp, bt, sl)
+                decode_paged_ref(q, kp, vp, bt, sl, scale)
+                t_used += time.perf_counter() - t0
+            else:
+                t0 = time.perf_counter()
+                if w.append:
+                    kc, vc, sl = kv_append_ref(kn, vn, kc, vc, sl)
+                decode_ref(q, kc, vc, sl, scale)
+                t_used += time.perf_counter() - t0
             done_bytes += kv_bytes(sl, w.K, d, 2)
             done_seqs += 1
             b = (b + 1) % w.B
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tokens_per_s": done_seqs / t_used,
-            "sample": f"{done_seqs} whole sequences of the workload (append + decode over "
+            "sample": f"{done_seqs} whole sequences of the workload ({'paged ' if paged else ''}append + decode over "
                       f"{int(inp['seq_lens'][0]) + (1 if w.append else 0)} positions, all 32 heads), "
                       f"{t_used:.1f} s of fp64 NumPy on 1 thread"}
 
 
 def bench_decode(args, w):
     import grouped_query_kv_amd as gqa
-    from grouped_query_kv_amd.inputs import workload_inputs
+    from grouped_query_kv_amd.inputs import paged_layout, workload_inputs
 
     dev = torch.device("cuda:0")
     R = max(1, args.copies)
@@ -129,14 +144,25 @@ def bench_decode(args, w):
     B, H, K, d = w.B, w.H, w.K, w.d
     q = inp["q"].to(dev)
     kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
+    paged = "block_size" in w.extra
     copies = []
-    kc0, vc0 = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    if paged:
+        pg = paged_layout(inp, w.extra["block_size"], seed=args.seed + 1)
+        kc0, vc0 = pg["k_pool"].to(dev), pg["v_pool"].to(dev)
+        bt = pg["block_table"].to(dev)
+    else:
+        kc0, vc0 = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
     for r in range(R):
         copies.append({"k": kc0 if r == 0 else kc0.clone(), "v": vc0 if r == 0 else vc0.clone(),
                        "sl": inp["seq_lens"].to(dev).clone()})
     host_lens = [inp["seq_lens"].clone() for _ in range(R)]
     max_len = int(inp["seq_lens"].max()) + visits + 1
-    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, max_len, d), dtype=torch.uint8, device=dev)
+    if paged:
+        bs = w.extra["block_size"]
+        ws = torch.empty(gqa.gqa_decode_paged_workspace_bytes(B, H, K, max_len, d, bs),
+                         dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, max_len, d), dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
     scale = float(np.float32(1.0 / math.sqrt(d)))
     stream = torch.cuda.current_stream()
@@ -145,7 +171,14 @@ def bench_decode(args, w):
         c = copies[i % R]
         if ev is not None:
             gqa.gqa_set_timing_events(ev[0], ev[1])
-        if w.append:
+        if paged:
+            # append through the block table, then decode (three kernel launches)
+            if w.append:
+                gqa.gqa_kv_append_paged(kn, vn, c["k"], c["v"], bt, c["sl"], stream=stream)
+                host_lens[i % R] += 1
+            gqa.gqa_decode_paged(q, c["k"], c["v"], bt, c["sl"], out, ws, max_len, scale=scale,
+                                 stream=stream)
+        elif w.append:
             # append + decode as one fused call (two kernel launches)
             gqa.gqa_decode_append(q, kn, vn, c["k"], c["v"], c["sl"], out, ws, max_len,
                                   scale=scale, stream=stream)
@@ -191,14 +224,17 @@ def bench_decode(args, w):
         "config": {"workload": w.name, "B": B, "H": H, "K": K, "d": d,
                    "context": (int(w.L) if w.ragged is None else list(w.ragged)),
                    "append_per_step": bool(w.append), "cache_copies": R,
+                   **({"block_size": w.extra["block_size"], "block_order": "shuffled"} if paged else {}),
                    "parallelism": "single GPU"},
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(total_bytes / args.steps),
-        "roofline": {"kernel": "decode partition pass with fused append (decode_split_bf16_kernel)", "bound": "hbm",
+        "roofline": {"kernel": ("paged decode partition pass (decode_split_bf16_kernel, paged)" if paged else
+                                "decode partition pass with fused append (decode_split_bf16_kernel)"),
+                     "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("decode_split_bf16_kernel"),
+                     "traffic": recorded_traffic("decode_split_bf16_kernel" + ("_paged" if paged else "")),
                      "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled)},
         "input_gen_s": round(t_gen, 1),
     }

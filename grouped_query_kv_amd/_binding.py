@@ -37,6 +37,9 @@ _SIGNATURES = {
     "gqa_decode_workspace_bytes": (_c_size_t, [_c_int] * 5),
     "gqa_decode": (_c_int, [_c_void_p] * 6 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_decode_append": (_c_int, [_c_void_p] * 8 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_kv_append_paged": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_void_p]),
+    "gqa_decode_paged_workspace_bytes": (_c_size_t, [_c_int] * 6),
+    "gqa_decode_paged": (_c_int, [_c_void_p] * 7 + [_c_size_t] + [_c_int] * 8 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_prefill_causal": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_meanpool_convert": (_c_int, [_c_void_p, _c_void_p, _c_int64, _c_int, _c_int, _c_int64, _c_int, _c_void_p]),
 }
@@ -253,6 +256,64 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, out, workspac
         seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K,
         S_max, int(max_seq_len), d, float(scale), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype],
         _stream(stream)))
+
+
+def _need_paged(k_pool, v_pool, block_table, seq_lens):
+    _need(k_pool, "k_pool", 4)
+    _need(v_pool, "v_pool", 4)
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("v_pool must match k_pool")
+    _need(block_table, "block_table", 2, (torch.int32,))
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    if seq_lens.numel() != block_table.shape[0]:
+        raise ValueError("seq_lens must have one entry per block_table row")
+
+
+def gqa_kv_append_paged(k_new, v_new, k_pool, v_pool, block_table, seq_lens, stream=None) -> None:
+    """Write k_new/v_new [B,K,d] at logical row seq_lens[b] of the paged pools
+    [num_blocks,K,block_size,d] through block_table [B,max_blocks] and
+    increment seq_lens, all on the GPU."""
+    _need_paged(k_pool, v_pool, block_table, seq_lens)
+    num_blocks, K, block_size, d = k_pool.shape
+    B, max_blocks = block_table.shape
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, 3)
+        if tuple(t.shape) != (B, K, d) or t.dtype != k_pool.dtype:
+            raise ValueError(f"{nm} must be [B,K,d] of the pool dtype")
+    lib = load_library()
+    _check("gqa_kv_append_paged", lib.gqa_kv_append_paged(
+        k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_table.data_ptr(), seq_lens.data_ptr(), B, K, num_blocks, block_size, max_blocks, d,
+        _DTYPE_CODE[k_pool.dtype], _stream(stream)))
+
+
+def gqa_decode_paged_workspace_bytes(B: int, H: int, K: int, max_seq_len: int, d: int,
+                                     block_size: int) -> int:
+    return int(load_library().gqa_decode_paged_workspace_bytes(B, H, K, max_seq_len, d, block_size))
+
+
+def gqa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, out, workspace, max_seq_len: int,
+                     scale: float | None = None, stream=None) -> None:
+    """One decode step over a paged cache: out [B,H,d] = GQA of q [B,H,d]
+    over logical rows [0, seq_lens[b]) gathered through block_table."""
+    _need(q, "q", 3, (torch.bfloat16,))
+    _need_paged(k_pool, v_pool, block_table, seq_lens)
+    _need(out, "out", 3)
+    _need(workspace, "workspace", 1, (torch.uint8,))
+    B, H, d = q.shape
+    num_blocks, K, block_size, dk = k_pool.shape
+    if dk != d or block_table.shape[0] != B or tuple(out.shape) != (B, H, d):
+        raise ValueError("shape mismatch between q, pools, block_table and out")
+    if k_pool.dtype != q.dtype:
+        raise ValueError("q and pools must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    lib = load_library()
+    _check("gqa_decode_paged", lib.gqa_decode_paged(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K,
+        num_blocks, block_size, block_table.shape[1], int(max_seq_len), d, float(scale),
+        _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def gqa_prefill_causal(q, k, v, out, scale: float | None = None, stream=None) -> None:

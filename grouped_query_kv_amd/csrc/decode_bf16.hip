@@ -69,13 +69,22 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 // (head block 0 only; nothing else reads that row in this launch), and the
 // lengths after the append go to `lens_out` for the combine pass, which
 // publishes them to seq_lens.
-template <int D, bool APPEND>
+//
+// PAGED: kc/vc are block pools [num_blocks, K, block_size, D] and position j
+// of sequence b lives in physical block block_table[b][j / block_size], row
+// j % block_size.  block_size is a multiple of 16, so every 16-row load group
+// lies in one block and its block id is wave-uniform: each wavefront loads
+// the block ids of its partition once (one per lane) and takes them with
+// readlane.  Ids are clamped into [0, num_blocks) and lengths to the table's
+// capacity, so a malformed table cannot make a load leave the pool.
+template <int D, bool APPEND, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
     const __bf16* __restrict__ q, __bf16* __restrict__ kc, __bf16* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
     int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out) {
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, PagedArgs pg) {
+  static_assert(!(APPEND && PAGED), "fused append is for contiguous caches");
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;        // contraction steps of Q.K
   constexpr int NTILES = D / 16;        // 16-wide output tiles of P.V
@@ -91,7 +100,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   const int hb = blockIdx.y - k * head_blocks;
   const int b = blockIdx.z;
   const int G = H / K;
-  const int L_in = seq_lens[b];
+  const int L_in = PAGED ? min(seq_lens[b], pg.max_blocks * pg.block_size) : seq_lens[b];
   int L = L_in, newpos = -1;
   if (APPEND) {
     if (L_in < S_max) {
@@ -119,9 +128,24 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       qf[s] = as_bf16x8(hq_ok ? ld16(qrow + 32 * s + 8 * g) : zero_u32x4());
   }
 
-  const size_t head_base = ((size_t)b * K + k) * (size_t)S_max * D;
+  const size_t head_base = PAGED ? 0 : ((size_t)b * K + k) * (size_t)S_max * D;
   __bf16* kbase = kc + head_base;
   __bf16* vbase = vc + head_base;
+  // paged: lane i holds the physical id of logical block lb0 + i
+  const int lb0 = PAGED ? t0 / pg.block_size : 0;
+  int blk_id = 0;
+  if (PAGED) {
+    const int nb = (t1 - 1) / pg.block_size - lb0 + 1;  // <= 64 by the split plan
+    if (threadIdx.x < nb)
+      blk_id = min(max(pg.block_table[(size_t)b * pg.max_blocks + lb0 + threadIdx.x], 0), pg.num_blocks - 1);
+  }
+  // first element of cache row `tok`, where `tok0` is a wave-uniform position
+  // of the same 16-row group
+  auto row_of = [&](__bf16* base, int tok0, int tok) -> __bf16* {
+    if (!PAGED) return base + (size_t)tok * D;
+    const int blk = __builtin_amdgcn_readlane(blk_id, tok0 / pg.block_size - lb0);
+    return base + (((size_t)blk * K + k) * pg.block_size + (tok - (tok0 / pg.block_size) * pg.block_size)) * D;
+  };
   const __bf16* knew_row = APPEND ? k_new + ((size_t)b * K + k) * D : nullptr;
   const __bf16* vnew_row = APPEND ? v_new + ((size_t)b * K + k) * D : nullptr;
 
@@ -143,7 +167,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int tok = c0 + 16 * mt + n;
-      const __bf16* krow = (APPEND && tok == newpos ? knew_row : kbase + (size_t)tok * D) + 8 * g;
+      const __bf16* krow = (APPEND && tok == newpos ? knew_row : row_of(kbase, c0 + 16 * mt, tok)) + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = tok < t1 ? ld16_stream(krow + 32 * s) : zero_u32x4();
     }
@@ -152,7 +176,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int tok = c0 + i * ROWS_PER_LOAD + vrow;
-      const __bf16* vrow_p = APPEND && tok == newpos ? vnew_row : vbase + (size_t)tok * D;
+      const __bf16* vrow_p = APPEND && tok == newpos ? vnew_row : row_of(vbase, c0 + i * ROWS_PER_LOAD, tok);
       vr[i] = tok < t1 ? ld16_stream(vrow_p + vcol) : zero_u32x4();
     }
   };
@@ -257,7 +281,7 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const int32_t* seq_lens, const DecodeWorkspace& ws,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
                                     float scale_log2, const void* k_new, const void* v_new,
-                                    hipStream_t stream) {
+                                    const PagedArgs* paged, hipStream_t stream) {
   const dim3 grid(plan.parts, K * plan.head_blocks, B);
   const dim3 block(64);
   auto qp = static_cast<const __bf16*>(q);
@@ -265,16 +289,21 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
   auto vp = static_cast<__bf16*>(v_cache);
   auto kn = static_cast<const __bf16*>(k_new);
   auto vn = static_cast<const __bf16*>(v_new);
-  const bool app = k_new != nullptr;
-#define GQA_SPLIT(DD, AP)                                                                         \
-  hipLaunchKernelGGL((decode_split_bf16_kernel<DD, AP>), grid, block, 0, stream, qp, kp, vp,      \
+  const PagedArgs pg = paged ? *paged : PagedArgs{nullptr, 16, 0, 1};
+#define GQA_SPLIT(DD, AP, PG)                                                                     \
+  hipLaunchKernelGGL((decode_split_bf16_kernel<DD, AP, PG>), grid, block, 0, stream, qp, kp, vp,  \
                      seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts, \
-                     plan.head_blocks, scale_log2, kn, vn, ws.lens)
+                     plan.head_blocks, scale_log2, kn, vn, ws.lens, pg)
+#define GQA_SPLIT_D(DD)                                                                           \
+  if (paged) GQA_SPLIT(DD, false, true);                                                          \
+  else if (k_new) GQA_SPLIT(DD, true, false);                                                     \
+  else GQA_SPLIT(DD, false, false);
   if (d == 128) {
-    if (app) GQA_SPLIT(128, true); else GQA_SPLIT(128, false);
+    GQA_SPLIT_D(128)
   } else {
-    if (app) GQA_SPLIT(64, true); else GQA_SPLIT(64, false);
+    GQA_SPLIT_D(64)
   }
+#undef GQA_SPLIT_D
 #undef GQA_SPLIT
   return hipGetLastError();
 }

@@ -66,7 +66,7 @@ struct TimedRegion {
 
 namespace gqa {
 
-DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d) {
+DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, int max_part_tokens) {
   (void)d;
   DecodePlan p{};
   const int G = H / K;
@@ -85,6 +85,7 @@ DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d) {
     t = (t + 31) / 32 * 32;
     pt = (int)(t < 64 ? 64 : t);
   }
+  if (max_part_tokens > 0 && pt > max_part_tokens) pt = max_part_tokens / 32 * 32;
   p.part_tokens = pt;
   p.parts = (L + pt - 1) / pt;
   return p;
@@ -197,7 +198,8 @@ static int decode_impl(const char* fn, const void* q, const void* k_new, const v
     TimedRegion timed(s);
     r = check_hip(dtype == GQA_BF16
                       ? gqa::launch_decode_split_bf16(q, k_cache, v_cache, seq_lens, ws, plan, B, H,
-                                                      K, S_max, d, scale_log2, k_new, v_new, s)
+                                                      K, S_max, d, scale_log2, k_new, v_new,
+                                                      nullptr, s)
                       : gqa::launch_decode_split_f32(q, k_cache, v_cache, seq_lens, ws, plan, B, H,
                                                      K, S_max, d, scale_log2, k_new, v_new, s),
                   "partition-pass launch");
@@ -226,6 +228,90 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   return decode_impl("gqa_decode_append", q, k_new, v_new, k_cache, v_cache, seq_lens, out,
                      workspace, workspace_bytes, B, H, K, S_max, max_seq_len, d, scale, dtype,
                      out_dtype, stream);
+}
+
+// Paged KV cache: the largest partition whose block ids fit one per lane.
+static int paged_max_part_tokens(int block_size) { return 63 * block_size; }
+
+static int validate_paged(const char* fn, int num_blocks, int block_size, int max_blocks) {
+  if (num_blocks < 1 || max_blocks < 1) return fail(GQA_ERR_INVALID, "%s: num_blocks, max_blocks must be >= 1", fn);
+  if (block_size < 16 || block_size % 16 != 0)
+    return fail(GQA_ERR_UNSUPPORTED, "%s: block_size=%d (a multiple of 16)", fn, block_size);
+  if ((long long)max_blocks * block_size > (1LL << 30))
+    return fail(GQA_ERR_INVALID, "%s: table capacity too large", fn);
+  return GQA_OK;
+}
+
+int gqa_kv_append_paged(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* block_table, int32_t* seq_lens, int B, int K, int num_blocks,
+                        int block_size, int max_blocks, int d, int dtype, void* stream) {
+  const char* fn = "gqa_kv_append_paged";
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !seq_lens)
+    return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (B < 1 || K < 1) return fail(GQA_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (int r = validate_paged(fn, num_blocks, block_size, max_blocks)) return r;
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", fn, d);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(GQA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  const gqa::PagedArgs pg{block_table, block_size, max_blocks, num_blocks};
+  const int r = check_hip(gqa::launch_kv_append_paged(k_new, v_new, k_pool, v_pool, pg, seq_lens, B, K,
+                                                      d * eb, static_cast<hipStream_t>(stream)),
+                          "gqa_kv_append_paged launch");
+  return r ? r : ok();
+}
+
+size_t gqa_decode_paged_workspace_bytes(int B, int H, int K, int max_seq_len, int d, int block_size) {
+  if (B < 1 || H < 1 || K < 1 || K > H || H % K || max_seq_len < 0 || (d != 64 && d != 128) ||
+      block_size < 16 || block_size % 16)
+    return 0;
+  const gqa::DecodePlan p = gqa::plan_decode(B, H, K, max_seq_len, d, paged_max_part_tokens(block_size));
+  return gqa::decode_workspace_bytes(p, B, H, d);
+}
+
+int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                     const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
+                     int B, int H, int K, int num_blocks, int block_size, int max_blocks,
+                     int max_seq_len, int d, float scale, int dtype, int out_dtype, void* stream) {
+  const char* fn = "gqa_decode_paged";
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)
+    return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (int r = validate_heads(fn, B, H, K, d)) return r;
+  if (int r = validate_paged(fn, num_blocks, block_size, max_blocks)) return r;
+  if (max_seq_len < 0 || max_seq_len > max_blocks * block_size)
+    return fail(GQA_ERR_INVALID, "%s: need 0 <= max_seq_len <= max_blocks * block_size", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(GQA_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+  if (dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: paged caches are bf16", fn);
+  if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
+    return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  const gqa::DecodePlan plan =
+      gqa::plan_decode(B, H, K, max_seq_len, d, paged_max_part_tokens(block_size));
+  const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
+                need, workspace ? workspace_bytes : (size_t)0);
+  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, H, d);
+  const gqa::PagedArgs pg{block_table, block_size, max_blocks, num_blocks};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r;
+  {
+    TimedRegion timed(s);
+    r = check_hip(gqa::launch_decode_split_bf16(q, const_cast<void*>(k_pool), const_cast<void*>(v_pool),
+                                                seq_lens, ws, plan, B, H, K, max_blocks * block_size, d,
+                                                scale * gqa::kLog2eHost, nullptr, nullptr, &pg, s),
+                  "partition-pass launch");
+  }
+  if (r) return r;
+  r = check_hip(gqa::launch_decode_combine(ws, const_cast<int32_t*>(seq_lens), out, plan, B, H, d,
+                                           out_dtype == GQA_BF16, false, s),
+                "combine-pass launch");
+  return r ? r : ok();
 }
 
 int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B, int H, int K,

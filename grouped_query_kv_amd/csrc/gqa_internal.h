@@ -19,7 +19,7 @@ struct DecodePlan {
   int head_blocks;
 };
 
-DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d);
+DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, int max_part_tokens = 0);
 
 // Workspace layout of a decode call:
 //   part_acc [B*H][parts][d]   fp32 un-normalised partial outputs
@@ -40,13 +40,30 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                             int32_t* seq_lens, int B, int K, int S_max, int row_bytes,
                             hipStream_t stream);
 
+// Paged KV cache: pools [num_blocks, K, block_size, d]; block_table
+// [B, max_blocks] int32 maps logical block j / block_size of a sequence to a
+// physical block.
+struct PagedArgs {
+  const int32_t* block_table;
+  int block_size;  // positions per block, a multiple of 16
+  int max_blocks;  // block-table entries per sequence
+  int num_blocks;  // physical blocks in each pool
+};
+
 // Partition pass, bf16 inputs, matrix-core (MFMA) contraction.  With
-// k_new/v_new non-null the step's append is fused in (caches are written).
+// k_new/v_new non-null the step's append is fused in (caches are written);
+// with `paged` non-null the caches are block pools (no fused append).
 hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const int32_t* seq_lens, const DecodeWorkspace& ws,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
                                     float scale_log2, const void* k_new, const void* v_new,
-                                    hipStream_t stream);
+                                    const PagedArgs* paged, hipStream_t stream);
+
+// Append into a paged cache: row seq_lens[b] goes to block
+// block_table[b][L / block_size], row L % block_size.
+hipError_t launch_kv_append_paged(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                  const PagedArgs& pg, int32_t* seq_lens, int B, int K,
+                                  int row_bytes, hipStream_t stream);
 
 // Partition pass, fp32 inputs, vector-ALU contraction (same append option).
 hipError_t launch_decode_split_f32(const void* q, void* k_cache, void* v_cache,

@@ -37,7 +37,45 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
   if (threadIdx.x == 0) seq_lens[b] = L + 1;
 }
 
+// Paged variant: position L of sequence b lives in physical block
+// block_table[b][L / block_size], row L % block_size of each KV head.  An
+// invalid block id (outside [0, num_blocks)) or a full table leaves the
+// sequence untouched.
+__global__ __launch_bounds__(kAppendThreads) void kv_append_paged_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    uint4* __restrict__ k_pool, uint4* __restrict__ v_pool, const int32_t* __restrict__ block_table,
+    int32_t* __restrict__ seq_lens, int K, int block_size, int max_blocks, int num_blocks,
+    int row_words) {
+  const int b = blockIdx.x;
+  const int L = seq_lens[b];
+  const int blk = (L >= 0 && L < max_blocks * block_size)
+                      ? block_table[(size_t)b * max_blocks + L / block_size] : -1;
+  __syncthreads();
+  if (blk < 0 || blk >= num_blocks) return;
+  const int row = L - (L / block_size) * block_size;
+  const int words = K * row_words;
+  for (int w = threadIdx.x; w < words; w += kAppendThreads) {
+    const int k = w / row_words;
+    const int o = w - k * row_words;
+    const size_t src = (size_t)(b * K + k) * row_words + o;
+    const size_t dst = (((size_t)blk * K + k) * block_size + row) * row_words + o;
+    k_pool[dst] = k_new[src];
+    v_pool[dst] = v_new[src];
+  }
+  if (threadIdx.x == 0) seq_lens[b] = L + 1;
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_paged(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                  const PagedArgs& pg, int32_t* seq_lens, int B, int K,
+                                  int row_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(kv_append_paged_kernel, dim3(B), dim3(kAppendThreads), 0, stream,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool), pg.block_table,
+                     seq_lens, K, pg.block_size, pg.max_blocks, pg.num_blocks, row_bytes / 16);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             int32_t* seq_lens, int B, int K, int S_max, int row_bytes,

@@ -5,6 +5,9 @@ lays them out.  Every draw comes from one CPU ``torch.Generator`` seeded by
 the caller, in a fixed order, so the GPU path and the CPU oracle consume the
 very same bits.
 
+Paged caches (``paged_layout``) re-lay those caches into blocks whose
+physical order is a seeded random permutation.
+
 Recipe (per call):
   1. ragged lengths, if requested: ``torch.randint(lo, hi + 1, (B,))``;
   2. q: float32 ``randn`` [B, H, d] (times ``q_scale``), then cast;
@@ -58,6 +61,10 @@ WORKLOADS = {
     "decode_long_131k": Workload(
         "decode_long_131k", "decode", B=4, H=32, K=8, d=128, dtype="bf16", L=131072,
         q_scale=2.0, note="131072-token context, q scaled by 2"),
+    "decode_paged_llama3_8b": Workload(
+        "decode_paged_llama3_8b", "decode", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
+        append=True, note="decode_llama3_8b over a paged cache: 16-token blocks in shuffled order",
+        extra={"block_size": 16}),
     "prefill_causal_4k": Workload(
         "prefill_causal_4k", "prefill", B=2, H=64, K=8, d=128, dtype="bf16", L=4096,
         note="causal prefill, S=4096, 64 query heads over 8 KV heads"),
@@ -128,6 +135,39 @@ def meanpool_inputs(outer: int, H: int, inner: int, dtype: str, seed: int = 0) -
     """Draw a [outer, H, inner] weight-like tensor (CPU)."""
     g = torch.Generator(device="cpu").manual_seed(int(seed))
     return torch.randn((outer, H, inner), generator=g).to(_DT[dtype])
+
+
+def paged_layout(inp: dict, block_size: int, seed: int = 0, spare_blocks: int = 0,
+                 shuffle: bool = True) -> dict:
+    """Re-lay a decode batch's contiguous caches as paged pools.
+
+    Sequence b owns max_blocks = ceil(S_max / block_size) logical blocks; the
+    physical id of its block i is perm[b * max_blocks + i], with perm a
+    ``torch.randperm`` of num_blocks = B * max_blocks + spare_blocks drawn
+    from a generator seeded with ``seed`` (identity when ``shuffle`` is
+    False).  Pools are [num_blocks, K, block_size, d]: block perm[..] holds
+    the block's positions of every KV head.  Positions past S_max and the
+    spare blocks are NaN.  Adds k_pool, v_pool, block_table (int32 [B,
+    max_blocks]), block_size to a copy of ``inp``."""
+    kc, vc = inp["k_cache"], inp["v_cache"]
+    B, K, smax, d = kc.shape
+    bs = int(block_size)
+    mb = -(-smax // bs)
+    nb = B * mb + int(spare_blocks)
+    if shuffle:
+        perm = torch.randperm(nb, generator=torch.Generator(device="cpu").manual_seed(int(seed)))
+    else:
+        perm = torch.arange(nb)
+    out = dict(inp)
+    for name, cache in (("k_pool", kc), ("v_pool", vc)):
+        padded = torch.full((B, K, mb * bs, d), float("nan"), dtype=cache.dtype)
+        padded[:, :, :smax] = cache
+        pool = torch.full((nb, K, bs, d), float("nan"), dtype=cache.dtype)
+        pool[perm[:B * mb]] = padded.view(B, K, mb, bs, d).permute(0, 2, 1, 3, 4).reshape(B * mb, K, bs, d)
+        out[name] = pool
+    out["block_table"] = perm[:B * mb].reshape(B, mb).to(torch.int32).contiguous()
+    out["block_size"] = bs
+    return out
 
 
 def workload_inputs(w: Workload, seed: int = 0, s_max: int | None = None) -> dict:

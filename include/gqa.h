@@ -124,6 +124,61 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
                       int d, float scale, int dtype, int out_dtype, void* stream);
 
 /*
+ * Paged KV cache.  The K and V pools are [num_blocks, K, block_size, d]:
+ * physical block n holds block_size consecutive positions of every KV head,
+ * one row of d elements per (head, position).  block_table is [B, max_blocks]
+ * int32 (row-major): logical position j of sequence b lives in physical block
+ * block_table[b, j / block_size], row j % block_size.  Blocks may be shared
+ * between sequences and appear in any order.  Each block is K * block_size
+ * rows (not H * block_size), broadcast inside the kernel to the G query heads
+ * of its group.  (compassingai.com "分組查詢注意力", section 下游 (downstream
+ * schedulers): paged blocks hold K * s rows and are broadcast to the H/K
+ * query heads; pinghaoyang.com.cn "GQA 完全拆解", section 工程实现
+ * (engineering): paged blocks are organised by KV head and the kernel
+ * broadcasts inside the group; same page, decode memory ledger: paging
+ * removes allocation waste and is orthogonal to GQA.)
+ *
+ * Paged caches are bf16 only; block_size is a multiple of 16; num_blocks,
+ * max_blocks >= 1; max_blocks * block_size <= 2^30.  Device-side contract:
+ * 0 <= seq_lens[b] <= max_blocks * block_size and every block id a kernel
+ * reads lies in [0, num_blocks) (ids outside it are clamped on read, so a
+ * bad table yields wrong values, never an out-of-bounds access).
+ */
+
+/*
+ * Append one token per sequence into a paged cache: for every b with
+ * L = seq_lens[b] < max_blocks * block_size and n = block_table[b, L /
+ * block_size] in [0, num_blocks):
+ *   k_pool[n, k, L % block_size, :] = k_new[b, k, :]   (and v likewise)
+ * then seq_lens[b] = L + 1.  Otherwise the sequence is left untouched.
+ * The copy is bit-exact.  dtype GQA_F32 or GQA_BF16; d in {64, 128}.
+ */
+int gqa_kv_append_paged(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* block_table, int32_t* seq_lens, int B, int K,
+                        int num_blocks, int block_size, int max_blocks, int d, int dtype,
+                        void* stream);
+
+/*
+ * Bytes of device workspace gqa_decode_paged needs (0 on invalid sizes).
+ */
+size_t gqa_decode_paged_workspace_bytes(int B, int H, int K, int max_seq_len, int d,
+                                        int block_size);
+
+/*
+ * One decode step over a paged cache: the result of gqa_decode on the
+ * contiguous cache whose row j of (b, k) is k_pool[block_table[b, j /
+ * block_size], k, j % block_size, :] (and v likewise).  L_b = seq_lens[b];
+ * out[b, h, :] = 0 when L_b == 0.  max_seq_len bounds every seq_lens[b]
+ * and is at most max_blocks * block_size.  dtype GQA_BF16; out_dtype
+ * GQA_BF16 or GQA_F32; workspace of gqa_decode_paged_workspace_bytes(...).
+ */
+int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                     const int32_t* block_table, const int32_t* seq_lens, void* out,
+                     void* workspace, size_t workspace_bytes, int B, int H, int K,
+                     int num_blocks, int block_size, int max_blocks, int max_seq_len, int d,
+                     float scale, int dtype, int out_dtype, void* stream);
+
+/*
  * Causal GQA attention over a whole prefix (prefill):
  *   out[b, h, i, :] = sum_{j <= i} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
  * for i in [0, S).  k and v are [B, K, S_max, d] with S <= S_max; rows >= S

@@ -210,3 +210,74 @@ def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int,
     of KV heads in that page's notation).
     """
     return 2 * int(layers) * int(kv_heads) * int(head_dim) * int(elem_bytes) * int(tokens)
+
+
+# --------------------------------------------------------------------------
+# Paged KV cache
+# --------------------------------------------------------------------------
+# [CAI] downstream-schedulers section: a paged scheduler keeps blocks of
+# K * s rows (KV heads, not query heads) and broadcasts each block to the H/K
+# query heads of its group.  [PHY] engineering section: the paged blocks are
+# organised by KV head and the kernel broadcasts inside the group; [PHY]
+# memory ledger: paging removes allocation waste and is orthogonal to GQA.
+#
+# Reading (the pages give no index formula): a pool is [num_blocks, K,
+# block_size, d]; a block table is [B, max_blocks]; logical position j of
+# sequence b is row j % block_size of physical block block_table[b, j //
+# block_size].
+
+
+def paged_gather_ref(pool, block_table, seq_lens) -> np.ndarray:
+    """Contiguous float64 cache [B, K, max_blocks * block_size, d] holding
+    rows [0, L_b) of every (b, kv head) gathered from the paged ``pool``
+    through ``block_table``; rows >= L_b are NaN (they must never be read)."""
+    pool = np.asarray(pool)
+    num_blocks, K, bs, d = pool.shape
+    B, max_blocks = block_table.shape
+    out = np.full((B, K, max_blocks * bs, d), np.nan)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if not 0 <= L <= max_blocks * bs:
+            raise ValueError("seq_lens out of range")
+        for j in range(L):
+            n = int(block_table[b, j // bs])
+            if not 0 <= n < num_blocks:
+                raise ValueError("block id out of range")
+            out[b, :, j, :] = pool[n, :, j % bs, :]
+    return out
+
+
+def decode_paged_ref(q, k_pool, v_pool, block_table, seq_lens, scale) -> np.ndarray:
+    """One GQA decode step over a paged cache: ``decode_ref`` applied to the
+    caches that ``paged_gather_ref`` assembles (the paging changes where rows
+    live, not what is computed)."""
+    kc = paged_gather_ref(k_pool, block_table, seq_lens)
+    vc = paged_gather_ref(v_pool, block_table, seq_lens)
+    return decode_ref(q, kc, vc, seq_lens, scale)
+
+
+def kv_append_paged_ref(k_new, v_new, k_pool, v_pool, block_table, seq_lens):
+    """Append one token's K and V rows per (b, kv head) into a paged cache.
+
+    Returns new (k_pool, v_pool, seq_lens) copies: with L = L_b and
+    n = block_table[b, L // block_size], row L % block_size of block n gets
+    the new rows bit-for-bit and L_b becomes L + 1.  A sequence whose table
+    is full (L == max_blocks * block_size) or whose block id lies outside
+    [0, num_blocks) is left unchanged.  Any element dtype.
+    """
+    kp = np.array(k_pool, copy=True)
+    vp = np.array(v_pool, copy=True)
+    sl = np.array(seq_lens, copy=True)
+    num_blocks, _, bs, _ = kp.shape
+    max_blocks = block_table.shape[1]
+    for b in range(len(sl)):
+        L = int(sl[b])
+        if L >= max_blocks * bs:
+            continue
+        n = int(block_table[b, L // bs])
+        if not 0 <= n < num_blocks:
+            continue
+        kp[n, :, L % bs, :] = k_new[b]
+        vp[n, :, L % bs, :] = v_new[b]
+        sl[b] = L + 1
+    return kp, vp, sl

@@ -347,6 +347,99 @@ def check_meanpool_identity_g1(O):
     assert np.array_equal(O.meanpool_convert_ref(src, 5), src)
 
 
+# --------------------------------------------------------------------------
+# paged KV cache
+# --------------------------------------------------------------------------
+def _paged_from_contiguous(cache, bs):
+    """Cut a contiguous cache [B, K, S, d] into blocks of ``bs`` positions:
+    block b * (S // bs) + i holds positions [i * bs, (i + 1) * bs) of
+    sequence b, so the identity table arange(B * S // bs) maps back."""
+    B, K, S, d = cache.shape
+    mb = S // bs
+    pool = cache.reshape(B, K, mb, bs, d).transpose(0, 2, 1, 3, 4).reshape(B * mb, K, bs, d)
+    return pool, np.arange(B * mb, dtype=np.int32).reshape(B, mb)
+
+
+def check_paged_worked_example(O):
+    g = json.loads((GOLDEN / "paged_gather_example.json").read_text())
+    bs = g["block_size"]
+    pool = np.array(g["pool_markers"], dtype=np.float64).reshape(g["num_blocks"], 1, bs, 1)
+    table = np.array(g["block_table"], dtype=np.int32)
+    got = O.paged_gather_ref(pool, table, np.array(g["seq_lens"]))
+    for b, want in enumerate(g["gathered"]):
+        assert list(got[b, 0, :len(want), 0]) == want, f"sequence {b}: {got[b, 0, :, 0]}"
+        assert np.all(np.isnan(got[b, 0, len(want):, 0]))
+    a = g["append"]
+    pool_i = np.array(g["pool_markers"], dtype=np.int32).reshape(g["num_blocks"], 1, bs, 1)
+    new = np.full((2, 1, 1), 99, dtype=np.int32)
+    kp, vp, sl = O.kv_append_paged_ref(new, new, pool_i, pool_i, table, np.array(a["seq_lens"]))
+    assert list(sl) == a["new_seq_lens"]
+    assert kp[:, 0, :, 0].tolist() == a["pool_after"] and vp[:, 0, :, 0].tolist() == a["pool_after"]
+
+
+def check_paged_identity_table(O):
+    """A pool cut from a contiguous cache, read through the identity table,
+    is that cache: the gather returns it and decode matches the brute force."""
+    B, H, K, d, bs = 2, 4, 2, 3, 2
+    lens = [5, 8]
+    q, kc, vc, sl = _rand_decode(2000, B, H, K, d, lens, s_max=8, nan_tail=False)
+    kp, table = _paged_from_contiguous(kc, bs)
+    vp, _ = _paged_from_contiguous(vc, bs)
+    g = O.paged_gather_ref(kp, table, sl)
+    for b, L in enumerate(lens):
+        assert np.array_equal(g[b, :, :L], kc[b, :, :L])
+    ref = BF.decode_bruteforce(q.tolist(), kc.tolist(), vc.tolist(), lens, 0.7)
+    _close(O.decode_paged_ref(q, kp, vp, table, sl, 0.7), ref, 1e-13, "paged decode vs brute force")
+
+
+def check_paged_block_permutation(O):
+    """Relabelling physical blocks (and the table with them) changes nothing;
+    two sequences sharing one table give identical rows."""
+    r = _rng(2100)
+    B, H, K, d, bs, nb, mb = 3, 6, 3, 4, 4, 9, 3
+    kp = r.standard_normal((nb, K, bs, d))
+    vp = r.standard_normal((nb, K, bs, d))
+    q = r.standard_normal((B, H, d))
+    q[2] = q[0]
+    table = np.array([[4, 0, 7], [2, 2, 5], [4, 0, 7]], dtype=np.int32)
+    sl = np.array([10, 9, 10])
+    out = O.decode_paged_ref(q, kp, vp, table, sl, 0.5)
+    assert np.array_equal(out[0], out[2])
+    perm = r.permutation(nb)                         # new id of old block n is perm[n]
+    kp2 = np.empty_like(kp)
+    vp2 = np.empty_like(vp)
+    kp2[perm] = kp
+    vp2[perm] = vp
+    out2 = O.decode_paged_ref(q, kp2, vp2, perm[table].astype(np.int32), sl, 0.5)
+    _close(out2, out, 1e-15, "block relabelling")
+    # sequence 1 reads block 2 twice: rows [0, 4) and [4, 8) are the same
+    g = O.paged_gather_ref(kp, table, sl)
+    assert np.array_equal(g[1, :, 0:4], g[1, :, 4:8]) and np.array_equal(g[1, :, 8], kp[5, :, 0])
+
+
+def check_paged_append_identity(O):
+    """Appending through the identity table is the contiguous append, full
+    tables and invalid block ids are left alone."""
+    r = _rng(2200)
+    B, K, S, d, bs = 3, 2, 8, 4, 4
+    kc = r.integers(-30000, 30000, (B, K, S, d), dtype=np.int16)
+    vc = r.integers(-30000, 30000, (B, K, S, d), dtype=np.int16)
+    kn = r.integers(-30000, 30000, (B, K, d), dtype=np.int16)
+    vn = r.integers(-30000, 30000, (B, K, d), dtype=np.int16)
+    sl = np.array([3, 4, S])
+    k2, v2, s2 = O.kv_append_ref(kn, vn, kc, vc, sl)
+    kp, table = _paged_from_contiguous(kc, bs)
+    vp, _ = _paged_from_contiguous(vc, bs)
+    kp2, vp2, sp2 = O.kv_append_paged_ref(kn, vn, kp, vp, table, sl)
+    assert list(sp2) == list(s2) == [4, 5, S]
+    assert np.array_equal(kp2, _paged_from_contiguous(k2, bs)[0])
+    assert np.array_equal(vp2, _paged_from_contiguous(v2, bs)[0])
+    bad = table.copy()
+    bad[1, 1] = -1
+    kp3, _, sp3 = O.kv_append_paged_ref(kn, vn, kp, vp, bad, sl)
+    assert sp3[1] == 4 and np.array_equal(kp3[table[1, 1]], kp[table[1, 1]])
+
+
 ALL_CHECKS = [
     check_kv_bytes_golden, check_kv_head_map,
     check_bruteforce_decode, check_bruteforce_prefill, check_bruteforce_meanpool,
@@ -356,4 +449,6 @@ ALL_CHECKS = [
     check_zero_query_mean, check_constant_values, check_empty_length,
     check_incremental_equals_causal, check_prefill_closed_forms, check_append_semantics,
     check_meanpool_linearity, check_meanpool_identity_g1,
+    check_paged_worked_example, check_paged_identity_table, check_paged_block_permutation,
+    check_paged_append_identity,
 ]

@@ -127,6 +127,57 @@ def test_meanpool_rejects(lib, args, code):
     assert lib.gqa_meanpool_convert(*args, None) == code
 
 
+def _decode_paged(lib, **kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30, B=2, H=32, K=8,
+             num_blocks=64, block_size=16, max_blocks=8, max_seq_len=128, d=128, scale=0.088,
+             dtype=B.GQA_BF16, out_dtype=B.GQA_BF16)
+    a.update(kw)
+    return lib.gqa_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["out"], a["ws"], a["wsb"],
+                                a["B"], a["H"], a["K"], a["num_blocks"], a["block_size"], a["max_blocks"],
+                                a["max_seq_len"], a["d"], a["scale"], a["dtype"], a["out_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bt=None), B.GQA_ERR_INVALID),
+    (dict(block_size=8), B.GQA_ERR_UNSUPPORTED),
+    (dict(block_size=24), B.GQA_ERR_UNSUPPORTED),
+    (dict(num_blocks=0), B.GQA_ERR_INVALID),
+    (dict(max_blocks=0), B.GQA_ERR_INVALID),
+    (dict(max_seq_len=129), B.GQA_ERR_INVALID),
+    (dict(dtype=B.GQA_F32, out_dtype=B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    (dict(H=30), B.GQA_ERR_INVALID),
+    (dict(scale=float("inf")), B.GQA_ERR_INVALID),
+    (dict(bt=FAKE + 2), B.GQA_ERR_INVALID),
+    (dict(wsb=64), B.GQA_ERR_WORKSPACE),
+])
+def test_decode_paged_rejects(lib, kw, code):
+    assert _decode_paged(lib, **kw) == code
+    assert lib.gqa_last_error().decode().startswith("gqa_decode_paged")
+
+
+def test_paged_workspace_bytes(lib):
+    # partitions are capped at 63 blocks, so a long context with few heads
+    # needs more partial rows than the contiguous plan
+    assert lib.gqa_decode_paged_workspace_bytes(1, 8, 8, 1 << 20, 128, 16) > 0
+    assert lib.gqa_decode_paged_workspace_bytes(64, 8, 8, 1 << 17, 128, 16) > \
+        lib.gqa_decode_workspace_bytes(64, 8, 8, 1 << 17, 128)
+    assert lib.gqa_decode_paged_workspace_bytes(1, 8, 8, 100, 128, 8) == 0
+    assert lib.gqa_decode_paged_workspace_bytes(1, 8, 3, 100, 128, 16) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 64, 16, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 2, 8, 64, 16, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 64, 12, 8, 128, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 0, 16, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 64, 16, 8, 96, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, 2, 8, 64, 16, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+])
+def test_append_paged_rejects(lib, args, code):
+    assert lib.gqa_kv_append_paged(*args, None) == code
+    assert lib.gqa_last_error().decode().startswith("gqa_kv_append_paged")
+
+
 def test_timing_events_need_both(lib):
     assert lib.gqa_set_timing_events(FAKE, None) == B.GQA_ERR_INVALID
     assert lib.gqa_set_timing_events(None, None) == B.GQA_OK

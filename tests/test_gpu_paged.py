@@ -1,0 +1,200 @@
+"""GPU parity of the paged-cache path (gqa_decode_paged, gqa_kv_append_paged)
+against the fp64 CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_kv_amd as gqa
+from grouped_query_kv_amd.inputs import WORKLOADS, decode_inputs, paged_layout, workload_inputs
+from gpu_util import DEV, TOL, bf16_bound, f64, guarded, guards_intact, note, report, scale_of
+from oracle import decode_paged_ref, kv_append_paged_ref
+
+pytestmark = pytest.mark.gpu
+
+_INT = {torch.bfloat16: torch.int16, torch.float32: torch.int32}
+
+
+def _np(t):
+    return t.float().numpy()
+
+
+def _vmax(pool):
+    return float(pool.float().nan_to_num(0.0).abs().max())
+
+
+def _run(p, msl, out_dtype=torch.bfloat16):
+    q = p["q"].to(DEV)
+    kp, vp = p["k_pool"].to(DEV), p["v_pool"].to(DEV)
+    bt, sl = p["block_table"].to(DEV), p["seq_lens"].to(DEV)
+    B, H, d = q.shape
+    K = kp.shape[1]
+    ws = torch.empty(max(gqa.gqa_decode_paged_workspace_bytes(B, H, K, msl, d, p["block_size"]), 16),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, H, d), dtype=out_dtype, device=DEV)
+    gqa.gqa_decode_paged(q, kp, vp, bt, sl, out, ws, msl, scale=scale_of(d))
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(p):
+    return decode_paged_ref(f64(p["q"]), _np(p["k_pool"]), _np(p["v_pool"]), p["block_table"].numpy(),
+                            p["seq_lens"].numpy(), scale_of(p["q"].shape[-1]))
+
+
+CASES = [
+    # B, H, K, d, lens, block_size
+    (3, 32, 8, 128, [1, 33, 1000], 16),
+    (4, 64, 8, 128, [0, 16, 17, 3000], 16),   # empty, block edge, several partitions
+    (2, 16, 4, 64, [31, 2100], 32),
+    (2, 56, 8, 128, [300, 5], 64),            # G = 7
+    (2, 8, 8, 128, [2, 97], 16),              # K = H (MHA)
+    (2, 32, 1, 128, [129, 4100], 48),         # K = 1 (MQA), G = 32, block_size 48
+    (1, 71, 1, 64, [257], 16),                # G = 71: five head blocks
+    # partitions capped at 62 blocks of 16 rows (992 positions)
+    (40, 8, 8, 64, [8000 + 37 * i for i in range(40)], 16),
+]
+
+
+@pytest.mark.parametrize("B,H,K,d,lens,bs", CASES)
+def test_paged_decode_shapes(B, H, K, d, lens, bs):
+    note(f"paged decode B={B} H={H} K={K} d={d} max_len={max(lens)} bs={bs}")
+    inp = decode_inputs(B, H, K, d, "bf16", seed=21, lens=lens)
+    p = paged_layout(inp, bs, seed=22, spare_blocks=5)
+    out = _run(p, max(lens))
+    ref = _ref(p)
+    r = report("paged", f64(out), ref)
+    assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+    assert r["max_abs"] <= bf16_bound(ref, _vmax(p["v_pool"]))
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert torch.count_nonzero(out[b]).item() == 0
+
+
+def test_paged_shared_prefix_blocks_and_guards():
+    """Two sequences share their first blocks (a common prompt); the output is
+    written exactly in place, fp32 or bf16."""
+    B, H, K, d, bs = 3, 32, 8, 128, 16
+    inp = decode_inputs(B, H, K, d, "bf16", seed=31, lens=[700, 700, 650])
+    p = paged_layout(inp, bs, seed=32, spare_blocks=2)
+    bt = p["block_table"].clone()
+    bt[1, :20] = bt[0, :20]      # sequence 1 reads sequence 0's first 320 rows
+    bt[2, 5] = bt[2, 4]          # a block listed twice in one table
+    p["block_table"] = bt
+    p["q"][1] = p["q"][0]
+    for out_dtype in (torch.float32, torch.bfloat16):
+        q = p["q"].to(DEV)
+        kp, vp = p["k_pool"].to(DEV), p["v_pool"].to(DEV)
+        bt_d, sl = bt.to(DEV), p["seq_lens"].to(DEV)
+        out, buf, guard = guarded((B, H, d), out_dtype)
+        ws = torch.empty(gqa.gqa_decode_paged_workspace_bytes(B, H, K, 700, d, bs), dtype=torch.uint8, device=DEV)
+        gqa.gqa_decode_paged(q, kp, vp, bt_d, sl, out, ws, 700, scale=scale_of(d))
+        torch.cuda.synchronize()
+        assert guards_intact(buf, guard, out_dtype)
+        ref = _ref(p)
+        r = report(f"shared {out_dtype}", f64(out), ref)
+        assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+        assert r["max_abs"] <= bf16_bound(ref, _vmax(p["v_pool"]))
+
+
+def test_paged_matches_contiguous_decode():
+    """The same cache, paged or contiguous, gives the same attention (both
+    within the bf16 bound of the oracle and of each other)."""
+    B, H, K, d = 2, 32, 8, 128
+    inp = decode_inputs(B, H, K, d, "bf16", seed=41, lens=[5000, 1234])
+    p = paged_layout(inp, 16, seed=42)
+    out_p = _run(p, 5000)
+    q, kc, vc, sl = (inp[n].to(DEV) for n in ("q", "k_cache", "v_cache", "seq_lens"))
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, 5000, d), dtype=torch.uint8, device=DEV)
+    out_c = torch.empty_like(out_p)
+    gqa.gqa_decode(q, kc, vc, sl, out_c, ws, 5000, scale=scale_of(d))
+    torch.cuda.synchronize()
+    ref = _ref(p)
+    b = bf16_bound(ref, _vmax(p["v_pool"]))
+    assert report("paged", f64(out_p), ref)["max_abs"] <= b
+    assert report("contiguous", f64(out_c), ref)["max_abs"] <= b
+
+
+@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f32", 32)])
+def test_paged_append_bit_exact(dtype, bs):
+    """Append through the table: bit-identical pools and lengths to the
+    oracle; a full table and an invalid block id leave their sequence alone."""
+    B, K, d = 4, 8, 128
+    lens = [0, 15, 40, 47]
+    inp = decode_inputs(B, 8, K, d, dtype, seed=51, lens=lens, s_max=48)
+    p = paged_layout(inp, bs, seed=52, spare_blocks=1)
+    bt = p["block_table"].clone()
+    bt[2, 40 // bs] = -5                      # invalid id: sequence 2 untouched
+    cap = p["block_table"].shape[1] * bs
+    lens_in = torch.tensor([0, 15, 40, cap], dtype=torch.int32)  # sequence 3: table full
+    it = _INT[p["k_pool"].dtype]
+    k_ref, v_ref, s_ref = kv_append_paged_ref(
+        inp["k_new"].view(it).numpy(), inp["v_new"].view(it).numpy(), p["k_pool"].view(it).numpy(),
+        p["v_pool"].view(it).numpy(), bt.numpy(), lens_in.numpy())
+    kp, vp = p["k_pool"].to(DEV), p["v_pool"].to(DEV)
+    sl = lens_in.to(DEV)
+    note(f"paged append {dtype} bs={bs}")
+    gqa.gqa_kv_append_paged(inp["k_new"].to(DEV), inp["v_new"].to(DEV), kp, vp, bt.to(DEV), sl)
+    torch.cuda.synchronize()
+    assert sl.cpu().tolist() == list(s_ref) == [1, 16, 40, cap]
+    assert np.array_equal(kp.cpu().view(it).numpy(), k_ref)
+    assert np.array_equal(vp.cpu().view(it).numpy(), v_ref)
+
+
+def test_paged_append_then_decode():
+    """One paged decode step: append the new token, then attend over it."""
+    B, H, K, d, bs = 3, 32, 8, 128, 16
+    inp = decode_inputs(B, H, K, d, "bf16", seed=61, lens=[15, 16, 1999])
+    p = paged_layout(inp, bs, seed=62, spare_blocks=3)
+    kp, vp, bt, sl = (p[n].to(DEV) for n in ("k_pool", "v_pool", "block_table", "seq_lens"))
+    gqa.gqa_kv_append_paged(inp["k_new"].to(DEV), inp["v_new"].to(DEV), kp, vp, bt, sl)
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(gqa.gqa_decode_paged_workspace_bytes(B, H, K, 2000, d, bs), dtype=torch.uint8, device=DEV)
+    gqa.gqa_decode_paged(inp["q"].to(DEV), kp, vp, bt, sl, out, ws, 2000, scale=scale_of(d))
+    torch.cuda.synchronize()
+    it = torch.int16
+    k2, v2, s2 = kv_append_paged_ref(inp["k_new"].view(it).numpy(), inp["v_new"].view(it).numpy(),
+                                     p["k_pool"].view(it).numpy(), p["v_pool"].view(it).numpy(),
+                                     p["block_table"].numpy(), p["seq_lens"].numpy())
+    assert sl.cpu().tolist() == list(s2)
+    k2 = torch.from_numpy(k2).view(torch.bfloat16)
+    v2 = torch.from_numpy(v2).view(torch.bfloat16)
+    ref = decode_paged_ref(f64(inp["q"]), _np(k2), _np(v2), p["block_table"].numpy(), s2, scale_of(d))
+    r = report("append+decode", f64(out), ref)
+    assert r["finite"] and r["max_abs"] <= bf16_bound(ref, _vmax(v2))
+
+
+def test_paged_full_workload():
+    """The Llama-3-8B layer over 16-row blocks in shuffled order, in the
+    launch configuration the benchmark times (append, then decode)."""
+    w = WORKLOADS["decode_paged_llama3_8b"]
+    note("paged full workload: inputs")
+    inp = workload_inputs(w, seed=0)
+    p = paged_layout(inp, w.extra["block_size"], seed=1)
+    kp, vp, bt, sl = (p[n].to(DEV) for n in ("k_pool", "v_pool", "block_table", "seq_lens"))
+    B, H, d = inp["q"].shape
+    gqa.gqa_kv_append_paged(inp["k_new"].to(DEV), inp["v_new"].to(DEV), kp, vp, bt, sl)
+    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(gqa.gqa_decode_paged_workspace_bytes(B, H, w.K, w.L + 1, d, p["block_size"]),
+                     dtype=torch.uint8, device=DEV)
+    note("paged full workload: GPU")
+    gqa.gqa_decode_paged(inp["q"].to(DEV), kp, vp, bt, sl, out, ws, w.L + 1, scale=scale_of(d))
+    torch.cuda.synchronize()
+    assert sl.cpu().tolist() == [w.L + 1] * B
+    note("paged full workload: oracle")
+    ref = np.zeros((B, H, d))
+    bs = p["block_size"]
+    for b in range(B):  # per sequence: the appended cache is the contiguous one plus the new row
+        kc = inp["k_cache"][b:b + 1].clone()
+        vc = inp["v_cache"][b:b + 1].clone()
+        kc[0, :, w.L] = inp["k_new"][b]
+        vc[0, :, w.L] = inp["v_new"][b]
+        # the pool row the append wrote, read back through the table
+        blk = int(p["block_table"][b, w.L // bs])
+        assert torch.equal(kp[blk, :, w.L % bs].cpu(), inp["k_new"][b])
+        assert torch.equal(vp[blk, :, w.L % bs].cpu(), inp["v_new"][b])
+        sub = paged_layout({"k_cache": kc, "v_cache": vc}, bs, shuffle=False)
+        ref[b] = decode_paged_ref(f64(inp["q"][b:b + 1]), _np(sub["k_pool"]), _np(sub["v_pool"]),
+                                  sub["block_table"].numpy(), np.array([w.L + 1]), scale_of(d))[0]
+    r = report("paged llama3_8b", f64(out), ref)
+    assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+    assert r["max_abs"] <= bf16_bound(ref, _vmax(p["v_pool"]))

@@ -53,6 +53,19 @@ MUTATIONS = {
     "append_no_increment": [("sl[b] = L + 1", "sl[b] = L")],
     "append_v_from_k": [("vc[b, :, L, :] = v_new[b]", "vc[b, :, L, :] = k_new[b]")],
     "append_full_cache": [("if L >= S_max:\n            continue", "if L > S_max:\n            continue")],
+    "paged_row_from_block_index": [("out[b, :, j, :] = pool[n, :, j % bs, :]",
+                                    "out[b, :, j, :] = pool[n, :, j // bs, :]")],
+    "paged_table_by_row": [("n = int(block_table[b, j // bs])", "n = int(block_table[b, j % bs])")],
+    "paged_table_transposed": [("n = int(block_table[b, j // bs])",
+                                "n = int(block_table.ravel()[(j // bs) * B + b])")],
+    "paged_v_gathered_from_k": [("vc = paged_gather_ref(v_pool, block_table, seq_lens)",
+                                 "vc = paged_gather_ref(k_pool, block_table, seq_lens)")],
+    "paged_append_row": [("kp[n, :, L % bs, :] = k_new[b]", "kp[n, :, L // bs, :] = k_new[b]")],
+    "paged_append_block": [("n = int(block_table[b, L // bs])", "n = int(block_table[b, L % max_blocks])")],
+    "paged_append_no_increment": [("        vp[n, :, L % bs, :] = v_new[b]\n        sl[b] = L + 1",
+                                   "        vp[n, :, L % bs, :] = v_new[b]")],
+    "paged_append_ignores_bad_id": [("        if not 0 <= n < num_blocks:\n            continue\n        kp",
+                                     "        n = n % num_blocks\n        kp")],
     "empty_length_nan": [("        if L == 0:\n            continue\n        for k in range(K):",
                           "        for k in range(K):")],
 }
