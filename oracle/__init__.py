@@ -8,8 +8,8 @@ It is a plain, slow, obviously-correct float64 NumPy restatement of what the
 hot path computes, written from the pages' description of the method:
 
 * ``gqa_oracle``  -- the definitions (decode, causal prefill, cache append,
-  paged-cache gather / decode / append, mean-pool conversion, KV-cache byte
-  count), vectorised with NumPy.
+  paged-cache gather / decode / append, int8 cache quantisation / decode /
+  append, mean-pool conversion, KV-cache byte count), vectorised with NumPy.
 * ``bruteforce``  -- the same definitions as pure-Python scalar loops, for
   tiny inputs only; it derives the query-head -> KV-head grouping from the
   page's 1-based group formula independently of ``gqa_oracle``.
@@ -28,4 +28,8 @@ from .gqa_oracle import (  # noqa: F401
     paged_gather_ref,
     decode_paged_ref,
     kv_append_paged_ref,
+    quantize_int8_ref,
+    dequantize_int8_ref,
+    decode_int8_ref,
+    kv_append_int8_ref,
 )

@@ -281,3 +281,76 @@ def kv_append_paged_ref(k_new, v_new, k_pool, v_pool, block_table, seq_lens):
         vp[n, :, L % bs, :] = v_new[b]
         sl[b] = L + 1
     return kp, vp, sl
+
+
+# --------------------------------------------------------------------------
+# int8 KV cache
+# --------------------------------------------------------------------------
+# [PHY] section on related work after the KV ledger: quantising the cached K
+# and V from 16-bit floats to INT8 / INT4 is orthogonal to GQA (GQA cuts the
+# number of heads, quantisation the bytes per element; the savings
+# multiply).  [CSDN] section 3 (practical deployment tips): 8-bit KV-cache
+# quantisation cuts the cache memory by a further 50%.
+#
+# Reading (the pages give no quantisation rule): symmetric absmax
+# quantisation per cached row, i.e. per (sequence, KV head, position) over
+# the d elements, all in IEEE float32:
+#     amax  = max_i |x_i|
+#     inv   = 127 / amax                     (float32 division)
+#     c_i   = clamp(rint(x_i * inv), -127, 127)  (float32 product, ties to even)
+#     scale = amax / 127                     (float32 division)
+# and the dequantised value is c_i * scale.  A row of zeros gets codes 0 and
+# scale 0.  Rows must be finite.
+
+
+def quantize_int8_ref(x):
+    """Per-row int8 codes and float32 scales of ``x`` [..., d] (the rule
+    above).  Returns (codes int8 [..., d], scales float32 [...])."""
+    x = np.asarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("rows must be finite")
+    amax = np.max(np.abs(x), axis=-1)
+    codes = np.zeros(x.shape, dtype=np.int8)
+    scales = np.zeros(amax.shape, dtype=np.float32)
+    nz = amax > 0
+    inv = np.float32(127) / amax[nz]
+    c = np.rint(x[nz] * inv[..., None])
+    codes[nz] = np.clip(c, -127, 127).astype(np.int8)
+    scales[nz] = amax[nz] / np.float32(127)
+    return codes, scales
+
+
+def dequantize_int8_ref(codes, scales) -> np.ndarray:
+    """float64 values c_i * scale of int8 rows (exact in float64)."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def decode_int8_ref(q, k_codes, v_codes, k_scales, v_scales, seq_lens, scale) -> np.ndarray:
+    """One GQA decode step over an int8 cache: ``decode_ref`` on the
+    dequantised caches.  Codes [B, K, S_max, d], scales [B, K, S_max]."""
+    return decode_ref(q, dequantize_int8_ref(k_codes, k_scales),
+                      dequantize_int8_ref(v_codes, v_scales), seq_lens, scale)
+
+
+def kv_append_int8_ref(k_new, v_new, k_codes, v_codes, k_scales, v_scales, seq_lens):
+    """Quantise each new K and V row and append it at position L_b of an
+    int8 cache; returns new (k_codes, v_codes, k_scales, v_scales, seq_lens).
+    A full cache (L_b == S_max) is left unchanged."""
+    kc = np.array(k_codes, copy=True)
+    vc = np.array(v_codes, copy=True)
+    ks = np.array(k_scales, copy=True)
+    vs = np.array(v_scales, copy=True)
+    sl = np.array(seq_lens, copy=True)
+    kq, kqs = quantize_int8_ref(k_new)
+    vq, vqs = quantize_int8_ref(v_new)
+    S_max = kc.shape[2]
+    for b in range(kc.shape[0]):
+        L = int(sl[b])
+        if L >= S_max:
+            continue
+        kc[b, :, L, :] = kq[b]
+        vc[b, :, L, :] = vq[b]
+        ks[b, :, L] = kqs[b]
+        vs[b, :, L] = vqs[b]
+        sl[b] = L + 1
+    return kc, vc, ks, vs, sl

@@ -440,6 +440,105 @@ def check_paged_append_identity(O):
     assert sp3[1] == 4 and np.array_equal(kp3[table[1, 1]], kp[table[1, 1]])
 
 
+# --------------------------------------------------------------------------
+# int8 KV cache
+# --------------------------------------------------------------------------
+def check_int8_exact_grid(O):
+    """Rows on the quantisation grid come back exactly: x = c * 0.5 with
+    max |c| = 127 gives inv = 2, codes c and scale 0.5."""
+    c = np.array([[127, -64, 0, 1, -127, 3, 100, -1]], dtype=np.int8)
+    x = c.astype(np.float32) * np.float32(0.5)
+    codes, scales = O.quantize_int8_ref(x)
+    assert np.array_equal(codes, c) and scales.dtype == np.float32 and scales[0] == np.float32(0.5)
+    assert np.array_equal(O.dequantize_int8_ref(codes, scales), x.astype(np.float64))
+
+
+def check_int8_ties_to_even(O):
+    """amax = 127 makes inv = 1, so x itself is rounded: ties go to even."""
+    x = np.array([[127.0, 2.5, -2.5, 3.5, 0.5, -0.5, 1.5, 126.5]], dtype=np.float32)
+    codes, scales = O.quantize_int8_ref(x)
+    assert codes[0].tolist() == [127, 2, -2, 4, 0, 0, 2, 126]
+    assert scales[0] == np.float32(1.0)
+
+
+def check_int8_bounds_and_invariants(O):
+    r = _rng(2300)
+    x = (r.standard_normal((5, 7, 64)) * r.uniform(0.01, 100, (5, 7, 1))).astype(np.float32)
+    x[1, 2] = 0.0
+    codes, scales = O.quantize_int8_ref(x)
+    assert codes.dtype == np.int8 and scales.shape == (5, 7)
+    deq = O.dequantize_int8_ref(codes, scales)
+    err = np.abs(deq - x.astype(np.float64))
+    # half a step, plus float32 rounding of inv, the product and the scale
+    assert np.all(err <= scales[..., None].astype(np.float64) * (0.5 + 1e-5) + 1e-30)
+    amax = np.abs(x).max(axis=-1)
+    nz = amax > 0
+    assert np.all(np.abs(codes.astype(np.int32)).max(axis=-1)[nz] == 127)
+    assert np.all(codes[1, 2] == 0) and scales[1, 2] == 0
+    assert np.allclose(scales[nz], amax[nz] / 127.0, rtol=1e-6)
+    # powers of two change the scale, not the codes
+    c2, s2 = O.quantize_int8_ref(x * np.float32(8.0))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales * np.float32(8.0))
+    assert np.array_equal(O.quantize_int8_ref(-x)[0], -codes)
+
+
+def check_int8_halves_cache(O):
+    """aicoding.csdn.net, section 3 (deployment tips): 8-bit KV quantisation
+    halves the cache; with one fp32 scale per row of d = 128 the cache is
+    (128 + 4) / 256 of the bf16 one."""
+    ratio = O.kv_cache_bytes(32, 8, 128, 1, 8192) / O.kv_cache_bytes(32, 8, 128, 2, 8192)
+    assert ratio == 0.5
+    codes, scales = O.quantize_int8_ref(np.ones((8, 64, 128), dtype=np.float32))
+    assert (codes.nbytes + scales.nbytes) / (8 * 64 * 128 * 2) == (128 + 4) / 256
+
+
+def check_int8_decode_composition(O):
+    """With unit scales the int8 decode is the plain decode of the integer
+    caches (brute force); with per-row scales it is the decode of the
+    dequantised rows, position by position."""
+    r = _rng(2400)
+    B, H, K, d, lens = 2, 4, 2, 6, [5, 3]
+    q = r.standard_normal((B, H, d)) * 0.05
+    kc = r.integers(-127, 128, (B, K, 6, d)).astype(np.int8)
+    vc = r.integers(-127, 128, (B, K, 6, d)).astype(np.int8)
+    ones = np.ones((B, K, 6), dtype=np.float32)
+    ref = BF.decode_bruteforce(q.tolist(), kc.astype(float).tolist(), vc.astype(float).tolist(), lens, 0.5)
+    _close(O.decode_int8_ref(q, kc, vc, ones, ones, np.array(lens), 0.5), ref, 1e-11, "int8 unit scales")
+    ks = r.uniform(0.001, 0.1, (B, K, 6)).astype(np.float32)
+    vs = r.uniform(0.001, 0.1, (B, K, 6)).astype(np.float32)
+    kf = [[[[float(kc[b, k, j, i]) * float(ks[b, k, j]) for i in range(d)] for j in range(6)]
+           for k in range(K)] for b in range(B)]
+    vf = [[[[float(vc[b, k, j, i]) * float(vs[b, k, j]) for i in range(d)] for j in range(6)]
+           for k in range(K)] for b in range(B)]
+    ref = BF.decode_bruteforce(q.tolist(), kf, vf, lens, 0.5)
+    _close(O.decode_int8_ref(q, kc, vc, ks, vs, np.array(lens), 0.5), ref, 1e-13, "int8 scaled rows")
+
+
+def check_int8_append(O):
+    r = _rng(2500)
+    B, K, S, d = 3, 2, 4, 8
+    kc = r.integers(-127, 128, (B, K, S, d)).astype(np.int8)
+    vc = r.integers(-127, 128, (B, K, S, d)).astype(np.int8)
+    ks = r.uniform(0.1, 1, (B, K, S)).astype(np.float32)
+    vs = r.uniform(0.1, 1, (B, K, S)).astype(np.float32)
+    kn = r.standard_normal((B, K, d)).astype(np.float32)
+    vn = r.standard_normal((B, K, d)).astype(np.float32)
+    sl = np.array([0, 2, S])
+    k2, v2, ks2, vs2, s2 = O.kv_append_int8_ref(kn, vn, kc, vc, ks, vs, sl)
+    assert list(s2) == [1, 3, S]
+    kq, kqs = O.quantize_int8_ref(kn)
+    vq, vqs = O.quantize_int8_ref(vn)
+    for b, L in enumerate(sl):
+        for pos in range(S):
+            new = pos == L
+            assert np.array_equal(k2[b, :, pos], kq[b] if new else kc[b, :, pos])
+            assert np.array_equal(v2[b, :, pos], vq[b] if new else vc[b, :, pos])
+            assert np.array_equal(ks2[b, :, pos], kqs[b] if new else ks[b, :, pos])
+            assert np.array_equal(vs2[b, :, pos], vqs[b] if new else vs[b, :, pos])
+    # appended rows dequantise to within half a step of the new rows
+    assert np.all(np.abs(O.dequantize_int8_ref(kq, kqs) - kn) <= kqs[..., None] * 0.50001)
+
+
 ALL_CHECKS = [
     check_kv_bytes_golden, check_kv_head_map,
     check_bruteforce_decode, check_bruteforce_prefill, check_bruteforce_meanpool,
@@ -451,4 +550,6 @@ ALL_CHECKS = [
     check_meanpool_linearity, check_meanpool_identity_g1,
     check_paged_worked_example, check_paged_identity_table, check_paged_block_permutation,
     check_paged_append_identity,
+    check_int8_exact_grid, check_int8_ties_to_even, check_int8_bounds_and_invariants,
+    check_int8_halves_cache, check_int8_decode_composition, check_int8_append,
 ]

@@ -66,6 +66,18 @@ MUTATIONS = {
                                    "        vp[n, :, L % bs, :] = v_new[b]")],
     "paged_append_ignores_bad_id": [("        if not 0 <= n < num_blocks:\n            continue\n        kp",
                                      "        n = n % num_blocks\n        kp")],
+    "int8_scale_over_128": [("scales[nz] = amax[nz] / np.float32(127)", "scales[nz] = amax[nz] / np.float32(128)")],
+    "int8_inv_128": [("inv = np.float32(127) / amax[nz]", "inv = np.float32(128) / amax[nz]")],
+    "int8_truncate": [("c = np.rint(x[nz] * inv[..., None])", "c = np.trunc(x[nz] * inv[..., None])")],
+    "int8_round_half_up": [("c = np.rint(x[nz] * inv[..., None])", "c = np.floor(x[nz] * inv[..., None] + 0.5)")],
+    "int8_per_tensor_amax": [("amax = np.max(np.abs(x), axis=-1)",
+                              "amax = np.full(x.shape[:-1], np.max(np.abs(x)), dtype=np.float32)")],
+    "int8_v_uses_k_scales": [("dequantize_int8_ref(v_codes, v_scales), seq_lens, scale)",
+                              "dequantize_int8_ref(v_codes, k_scales), seq_lens, scale)")],
+    "int8_dequant_ignores_scale": [("return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]",
+                                    "return np.asarray(codes, dtype=np.float64) / 127.0")],
+    "int8_append_unquantised": [("        kc[b, :, L, :] = kq[b]\n", "        kc[b, :, L, :] = k_new[b]\n")],
+    "int8_append_scale_swapped": [("        ks[b, :, L] = kqs[b]\n", "        ks[b, :, L] = vqs[b]\n")],
     "empty_length_nan": [("        if L == 0:\n            continue\n        for k in range(K):",
                           "        for k in range(K):")],
 }
