@@ -10,7 +10,10 @@ new token's K/V rows of every sequence and attend over the cache including
 them (gqa_decode_append: the append fused into the partition pass, then the
 combine pass -- the same work as gqa_kv_append followed by gqa_decode).  A
 paged workload (decode_paged_llama3_8b) runs gqa_kv_append_paged and then
-gqa_decode_paged over 16-row blocks in shuffled physical order.  The default workload is
+gqa_decode_paged over 16-row blocks in shuffled physical order; an int8
+workload (decode_int8_llama3_8b) runs gqa_kv_append_int8 and then
+gqa_decode_int8 over the cache quantised once before timing (bytes counted
+as stored: d codes + one fp32 scale per row).  The default workload is
 the Llama-3-8B-shaped layer: B=16 sequences at 8192 cached tokens, 32 query
 heads over 8 KV heads, d=128, bf16 (synthetic N(0,1) data).
 
@@ -78,8 +81,10 @@ def recorded_traffic(kernel: str):
     return int(rec["read_bytes"] + rec["write_bytes"])
 
 
-def kv_bytes(lens, K, d, elem):
-    return int(sum(2 * K * int(L) * d * elem for L in lens))
+def kv_bytes(lens, K, d, elem, row_extra=0):
+    """K and V bytes of the cached rows: 2 * K * L_b rows of d elements
+    (plus `row_extra` bytes per row, the fp32 scale of an int8 row)."""
+    return int(sum(2 * K * int(L) * (d * elem + row_extra) for L in lens))
 
 
 def cpu_baseline_decode(inp, w, budget_s):
@@ -88,9 +93,12 @@ def cpu_baseline_decode(inp, w, budget_s):
     from threadpoolctl import threadpool_limits
 
     from grouped_query_kv_amd.inputs import paged_layout
-    from oracle import decode_paged_ref, decode_ref, kv_append_paged_ref, kv_append_ref
+    from oracle import (decode_int8_ref, decode_paged_ref, decode_ref, kv_append_int8_ref,
+                        kv_append_paged_ref, kv_append_ref, quantize_int8_ref)
 
     paged = "block_size" in w.extra
+    int8 = w.extra.get("kv_dtype") == "int8"
+    elem, row_extra = (1, 4) if int8 else (2, 0)
     d = w.d
     scale = float(np.float32(1.0 / math.sqrt(d)))
     done_bytes, done_seqs, t_used = 0, 0, 0.0
@@ -103,7 +111,17 @@ def cpu_baseline_decode(inp, w, budget_s):
             vc = inp["v_cache"][b:b + 1].float().numpy()
             kn = inp["k_new"][b:b + 1].float().numpy()
             vn = inp["v_new"][b:b + 1].float().numpy()
-            if paged:
+            if int8:
+                L = int(sl[0])
+                kq, ksq = quantize_int8_ref(inp["k_cache"][b:b + 1, :, :L].float().numpy())
+                vq, vsq = quantize_int8_ref(inp["v_cache"][b:b + 1, :, :L].float().numpy())
+                pad = lambda a: np.concatenate([a, np.zeros(a.shape[:2] + (1,) + a.shape[3:], a.dtype)], axis=2)
+                kq, vq, ksq, vsq = pad(kq), pad(vq), pad(ksq), pad(vsq)
+                t0 = time.perf_counter()
+                kq, vq, ksq, vsq, sl = kv_append_int8_ref(kn, vn, kq, vq, ksq, vsq, sl)
+                decode_int8_ref(q, kq, vq, ksq, vsq, sl, scale)
+                t_used += time.perf_counter() - t0
+            elif paged:
                 pg = paged_layout({"k_cache": inp["k_cache"][b:b + 1], "v_cache": inp["v_cache"][b:b + 1]},
                                   w.extra["block_size"], seed=b)
                 kp, vp = pg["k_pool"].float().numpy(), pg["v_pool"].float().numpy()
@@ -119,12 +137,12 @@ def cpu_baseline_decode(inp, w, budget_s):
                     kc, vc, sl = kv_append_ref(kn, vn, kc, vc, sl)
                 decode_ref(q, kc, vc, sl, scale)
                 t_used += time.perf_counter() - t0
-            done_bytes += kv_bytes(sl, w.K, d, 2)
+            done_bytes += kv_bytes(sl, w.K, d, elem, row_extra)
             done_seqs += 1
             b = (b + 1) % w.B
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tokens_per_s": done_seqs / t_used,
-            "sample": f"{done_seqs} whole sequences of the workload ({'paged ' if paged else ''}append + decode over "
+            "sample": f"{done_seqs} whole sequences of the workload ({'paged ' if paged else 'int8 ' if int8 else ''}append + decode over "
                       f"{int(inp['seq_lens'][0]) + (1 if w.append else 0)} positions, all 32 heads), "
                       f"{t_used:.1f} s of fp64 NumPy on 1 thread"}
 
@@ -137,7 +155,7 @@ def bench_decode(args, w):
     R = max(1, args.copies)
     visits = math.ceil((args.warmup + args.steps) / R)
     base_len = int(w.L) if w.ragged is None else w.ragged[1]
-    s_max = base_len + visits + 2
+    s_max = (base_len + visits + 2 + 3) // 4 * 4
     t_gen = time.perf_counter()
     inp = workload_inputs(w, seed=args.seed, s_max=s_max)
     t_gen = time.perf_counter() - t_gen
@@ -145,8 +163,20 @@ def bench_decode(args, w):
     q = inp["q"].to(dev)
     kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
     paged = "block_size" in w.extra
+    int8 = w.extra.get("kv_dtype") == "int8"
+    elem, row_extra = (1, 4) if int8 else (2, 0)
     copies = []
-    if paged:
+    if int8:
+        # the workload's bf16 caches quantised once on the GPU (set-up, untimed)
+        kb, vb = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+        kc0 = torch.empty(kb.shape, dtype=torch.int8, device=dev)
+        vc0 = torch.empty(vb.shape, dtype=torch.int8, device=dev)
+        ks0 = torch.empty(kb.shape[:3], dtype=torch.float32, device=dev)
+        vs0 = torch.empty(vb.shape[:3], dtype=torch.float32, device=dev)
+        gqa.gqa_kv_quantize_int8(kb, kc0, ks0)
+        gqa.gqa_kv_quantize_int8(vb, vc0, vs0)
+        del kb, vb
+    elif paged:
         pg = paged_layout(inp, w.extra["block_size"], seed=args.seed + 1)
         kc0, vc0 = pg["k_pool"].to(dev), pg["v_pool"].to(dev)
         bt = pg["block_table"].to(dev)
@@ -155,6 +185,9 @@ def bench_decode(args, w):
     for r in range(R):
         copies.append({"k": kc0 if r == 0 else kc0.clone(), "v": vc0 if r == 0 else vc0.clone(),
                        "sl": inp["seq_lens"].to(dev).clone()})
+        if int8:
+            copies[-1]["ks"] = ks0 if r == 0 else ks0.clone()
+            copies[-1]["vs"] = vs0 if r == 0 else vs0.clone()
     host_lens = [inp["seq_lens"].clone() for _ in range(R)]
     max_len = int(inp["seq_lens"].max()) + visits + 1
     if paged:
@@ -171,7 +204,13 @@ def bench_decode(args, w):
         c = copies[i % R]
         if ev is not None:
             gqa.gqa_set_timing_events(ev[0], ev[1])
-        if paged:
+        if int8:
+            # quantising append, then decode over the int8 cache (three launches)
+            gqa.gqa_kv_append_int8(kn, vn, c["k"], c["v"], c["ks"], c["vs"], c["sl"], stream=stream)
+            host_lens[i % R] += 1
+            gqa.gqa_decode_int8(q, c["k"], c["v"], c["ks"], c["vs"], c["sl"], out, ws, max_len,
+                                scale=scale, stream=stream)
+        elif paged:
             # append through the block table, then decode (three kernel launches)
             if w.append:
                 gqa.gqa_kv_append_paged(kn, vn, c["k"], c["v"], bt, c["sl"], stream=stream)
@@ -197,7 +236,7 @@ def bench_decode(args, w):
     for i in range(args.warmup, args.warmup + args.steps):
         if w.append:
             sim[i % R] += 1
-        step_bytes.append(kv_bytes(sim[i % R].tolist(), K, d, 2))
+        step_bytes.append(kv_bytes(sim[i % R].tolist(), K, d, elem, row_extra))
     # the partition pass is bracketed by timing events in every EVERY-th timed
     # step (recording events costs a couple of microseconds of gap per step)
     EVERY = 4
@@ -225,16 +264,19 @@ def bench_decode(args, w):
                    "context": (int(w.L) if w.ragged is None else list(w.ragged)),
                    "append_per_step": bool(w.append), "cache_copies": R,
                    **({"block_size": w.extra["block_size"], "block_order": "shuffled"} if paged else {}),
+                   **({"kv_dtype": "int8", "kv_row_bytes": d + 4} if int8 else {}),
                    "parallelism": "single GPU"},
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(total_bytes / args.steps),
-        "roofline": {"kernel": ("paged decode partition pass (decode_split_bf16_kernel, paged)" if paged else
+        "roofline": {"kernel": ("int8 decode partition pass (decode_split_int8_kernel)" if int8 else
+                                "paged decode partition pass (decode_split_bf16_kernel, paged)" if paged else
                                 "decode partition pass with fused append (decode_split_bf16_kernel)"),
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic("decode_split_bf16_kernel" + ("_paged" if paged else "")),
+                     "traffic": recorded_traffic("decode_split_int8_kernel" if int8 else
+                                                 "decode_split_bf16_kernel" + ("_paged" if paged else "")),
                      "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled)},
         "input_gen_s": round(t_gen, 1),
     }

@@ -13,11 +13,14 @@ from ._binding import (  # noqa: F401
     gqa_abi_version,
     gqa_decode,
     gqa_decode_append,
+    gqa_decode_int8,
     gqa_decode_paged,
     gqa_decode_paged_workspace_bytes,
     gqa_decode_workspace_bytes,
     gqa_kv_append,
     gqa_kv_append_paged,
+    gqa_kv_append_int8,
+    gqa_kv_quantize_int8,
     gqa_kv_cache_bytes,
     gqa_last_error,
     gqa_meanpool_convert,

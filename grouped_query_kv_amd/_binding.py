@@ -40,6 +40,9 @@ _SIGNATURES = {
     "gqa_kv_append_paged": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_void_p]),
     "gqa_decode_paged_workspace_bytes": (_c_size_t, [_c_int] * 6),
     "gqa_decode_paged": (_c_int, [_c_void_p] * 7 + [_c_size_t] + [_c_int] * 8 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_kv_quantize_int8": (_c_int, [_c_void_p] * 3 + [_c_int64, _c_int, _c_int, _c_void_p]),
+    "gqa_kv_append_int8": (_c_int, [_c_void_p] * 7 + [_c_int] * 5 + [_c_void_p]),
+    "gqa_decode_int8": (_c_int, [_c_void_p] * 8 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_prefill_causal": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_meanpool_convert": (_c_int, [_c_void_p, _c_void_p, _c_int64, _c_int, _c_int, _c_int64, _c_int, _c_void_p]),
 }
@@ -314,6 +317,73 @@ def gqa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, out, workspace, m
         seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K,
         num_blocks, block_size, block_table.shape[1], int(max_seq_len), d, float(scale),
         _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def gqa_kv_quantize_int8(src, codes, scales, stream=None) -> None:
+    """Quantise the rows of src [..., d] (fp32 or bf16) into int8 codes of
+    the same shape and fp32 scales [...] (one per row)."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if src.dtype not in _DTYPE_CODE:
+        raise ValueError(f"src: dtype {src.dtype} not supported")
+    d = src.shape[-1]
+    rows = src.numel() // d
+    _need(codes, "codes", src.dim(), (torch.int8,))
+    _need(scales, "scales", src.dim() - 1, (torch.float32,))
+    if codes.shape != src.shape or tuple(scales.shape) != tuple(src.shape[:-1]):
+        raise ValueError("codes must match src, scales must be src.shape[:-1]")
+    _check("gqa_kv_quantize_int8", load_library().gqa_kv_quantize_int8(
+        src.data_ptr(), codes.data_ptr(), scales.data_ptr(), rows, d, _DTYPE_CODE[src.dtype],
+        _stream(stream)))
+
+
+def _need_int8_cache(k_codes, v_codes, k_scales, v_scales):
+    _need(k_codes, "k_codes", 4, (torch.int8,))
+    _need(v_codes, "v_codes", 4, (torch.int8,))
+    _need(k_scales, "k_scales", 3, (torch.float32,))
+    _need(v_scales, "v_scales", 3, (torch.float32,))
+    if v_codes.shape != k_codes.shape or k_scales.shape != k_codes.shape[:3] or \
+            v_scales.shape != k_codes.shape[:3]:
+        raise ValueError("int8 cache: codes [B,K,S_max,d] and scales [B,K,S_max] must agree")
+
+
+def gqa_kv_append_int8(k_new, v_new, k_codes, v_codes, k_scales, v_scales, seq_lens, stream=None) -> None:
+    """Quantise k_new/v_new [B,K,d] and append them at row seq_lens[b] of an
+    int8 cache; increment seq_lens."""
+    _need_int8_cache(k_codes, v_codes, k_scales, v_scales)
+    B, K, S_max, d = k_codes.shape
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, 3)
+        if tuple(t.shape) != (B, K, d) or t.dtype != k_new.dtype:
+            raise ValueError(f"{nm} must be [B,K,d]")
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    _check("gqa_kv_append_int8", load_library().gqa_kv_append_int8(
+        k_new.data_ptr(), v_new.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+        k_scales.data_ptr(), v_scales.data_ptr(), seq_lens.data_ptr(), B, K, S_max, d,
+        _DTYPE_CODE[k_new.dtype], _stream(stream)))
+
+
+def gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, out, workspace,
+                    max_seq_len: int, scale: float | None = None, stream=None) -> None:
+    """One decode step over an int8 cache: out [B,H,d] = GQA of the bf16 q
+    [B,H,d] over the dequantised rows [0, seq_lens[b])."""
+    _need(q, "q", 3, (torch.bfloat16,))
+    _need_int8_cache(k_codes, v_codes, k_scales, v_scales)
+    _need(out, "out", 3)
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    _need(workspace, "workspace", 1, (torch.uint8,))
+    B, H, d = q.shape
+    Bk, K, S_max, dk = k_codes.shape
+    if Bk != B or dk != d or tuple(out.shape) != (B, H, d) or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, cache, seq_lens and out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("gqa_decode_int8", load_library().gqa_decode_int8(
+        q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K, S_max,
+        int(max_seq_len), d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def gqa_prefill_causal(q, k, v, out, scale: float | None = None, stream=None) -> None:

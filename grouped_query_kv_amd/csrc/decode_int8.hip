@@ -1,0 +1,267 @@
+// Decode partition pass over an int8 KV cache, on the gfx950 matrix cores.
+//
+// The cache holds int8 codes c and one fp32 scale per row (sequence, KV
+// head, position); a row reads back as c * scale (the quantisation rule is
+// in quant_int8.hip).  pinghaoyang.com.cn "GQA 完全拆解": quantising the KV
+// cache is orthogonal to GQA and multiplies its savings; aicoding.csdn.net
+// "LLaMa3与DeepSeek采用的GQA技术", section 3: 8-bit caches halve the bytes.
+// Decode is bound by those bytes, so this pass reads 2 * (d + 4) bytes per
+// position and KV head instead of 4 * d.
+//
+// It computes the same partial online-softmax state as the bf16 pass
+// (decode_bf16.hip, where the algorithm and the operand layouts of
+// v_mfma_f32_16x16x32_bf16 are described), with the scales moved out of the
+// products:
+//     s_j  = scale * (q . c^K_j) * sk_j                   (score of position j)
+//     acc += sum_j 2^(s_j - m) * sv_j * c^V_j,   l += sum_j 2^(s_j - m)
+// Codes of magnitude <= 127 are exact in bf16, so the matrix cores multiply
+// the bf16 query by the codes converted in registers; the value scale is
+// folded into the bf16 softmax weight of each position.
+//
+// Layouts: K rows go straight from HBM into operand registers.  Lane (n, g)
+// at k-step s carries head dimensions (d/4) g + 8 s .. +7 (a relabelling of
+// the contraction index applied to Q and K alike), so each lane reads one
+// contiguous d/4-byte piece of its K row.  V codes are converted to bf16 on
+// the way into LDS and read back transposed exactly as in the bf16 pass.
+#include "common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kChunk = 32;
+constexpr int kVPad = 16;
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Four int8 codes (one dword, little-endian) -> four bf16 values (exact).
+__device__ __forceinline__ uint2 i8x4_to_bf16x4(uint32_t w) {
+  const float f0 = (float)((int32_t)(w << 24) >> 24);
+  const float f1 = (float)((int32_t)(w << 16) >> 24);
+  const float f2 = (float)((int32_t)(w << 8) >> 24);
+  const float f3 = (float)((int32_t)w >> 24);
+  return uint2{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
+}
+
+// Eight codes (two dwords) -> one bf16x8 operand.
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const uint2 a = i8x4_to_bf16x4(lo);
+  const uint2 b = i8x4_to_bf16x4(hi);
+  return as_bf16x8(u32x4{a.x, a.y, b.x, b.y});
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_int8_kernel(
+    const __bf16* __restrict__ q, const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
+    const float* __restrict__ ks, const float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ part_acc, float* __restrict__ part_ml, int H, int K, int S_max,
+    int part_tokens, int parts, int head_blocks, float scale_log2) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int KSTEPS = D / 32;
+  constexpr int NTILES = D / 16;
+  constexpr int KSEG = D / 4;                 // bytes of a K row per lane
+  constexpr int KWORDS = KSEG / 16;           // 16-byte loads per K row piece
+  constexpr int LANES_PER_ROW = D / 16;       // 16-byte words per V row
+  constexpr int ROWS_PER_LOAD = 64 / LANES_PER_ROW;
+  constexpr int VLOADS = kChunk / ROWS_PER_LOAD;
+  constexpr int LDS_ROW = D + kVPad;
+
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * LDS_ROW];
+
+  const int p = blockIdx.x;
+  const int k = blockIdx.y / head_blocks;
+  const int hb = blockIdx.y - k * head_blocks;
+  const int b = blockIdx.z;
+  const int G = H / K;
+  const int L = seq_lens[b];
+  const int t0 = p * part_tokens;
+  if (t0 >= L) return;
+  const int t1 = min(t0 + part_tokens, L);
+
+  const int lane = threadIdx.x;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  const int hq = hb * 16 + n;
+  const bool hq_ok = hq < G;
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D + KSEG * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(hq_ok ? ld16(qrow + 8 * s) : zero_u32x4());
+  }
+
+  const size_t head_row0 = ((size_t)b * K + k) * (size_t)S_max;  // first row of (b, k)
+  const int8_t* kbase = kc + head_row0 * D;
+  const int8_t* vbase = vc + head_row0 * D;
+  const float* ksb = ks + head_row0;
+  const float* vsb = vs + head_row0;
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 acc[NTILES];
+#pragma unroll
+  for (int t = 0; t < NTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int vrow = lane / LANES_PER_ROW;
+  const int vcol = (lane % LANES_PER_ROW) * 16;
+  const uint16_t* tr_src = &vt[(4 * g + (n >> 2)) * LDS_ROW + 4 * (n & 3)];
+
+  u32x4 ka[2][KWORDS];
+  u32x4 vr[VLOADS];
+  f32x4 ksv[2], vsv[2];
+  auto load_k = [&](int c0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int tok = c0 + 16 * mt + n;
+      const int8_t* krow = kbase + (size_t)tok * D + KSEG * g;
+#pragma unroll
+      for (int w = 0; w < KWORDS; ++w) ka[mt][w] = tok < t1 ? ld16_stream(krow + 16 * w) : zero_u32x4();
+      // scales of the positions this lane's scores belong to: 16mt + 4g + i
+      const int s0 = c0 + 16 * mt + 4 * g;
+      ksv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(ksb + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      vsv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(vsb + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto load_v = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int tok = c0 + i * ROWS_PER_LOAD + vrow;
+      vr[i] = tok < t1 ? ld16_stream(vbase + (size_t)tok * D + vcol) : zero_u32x4();
+    }
+  };
+  load_k(t0);
+  load_v(t0);
+
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    const bool more = c0 + kChunk < t1;
+    // ---- S^T = K . Q^T (codes) for the two 16-position tiles ----
+    f32x4 st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const u32x4 w = ka[mt][s / 2];
+        const bf16x8 kf = (s & 1) ? i8x8_to_bf16x8(w[2], w[3]) : i8x8_to_bf16x8(w[0], w[1]);
+        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], st[mt], 0, 0, 0);
+      }
+    }
+    float sk[8], sv[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sk[4 * mt + i] = ksv[mt][i];
+        sv[4 * mt + i] = vsv[mt][i];
+      }
+    if (more) load_k(c0 + kChunk);
+
+    // ---- online softmax for head n over positions {16mt + 4g + i} ----
+    float x[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = c0 + 16 * mt + 4 * g + i;
+        const bool ok = tok < t1;
+        const float xv = ok ? st[mt][i] * (sk[4 * mt + i] * scale_log2) : -INFINITY;
+        x[4 * mt + i] = xv;
+        sv[4 * mt + i] = ok ? sv[4 * mt + i] : 0.f;  // rows past the end never reach the sum
+        cmax = fmaxf(cmax, xv);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.f;
+    uint32_t pw[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float e0 = fast_exp2(x[j] - m_new);
+      const float e1 = fast_exp2(x[j + 1] - m_new);
+      psum += e0 + e1;
+      pw[j / 2] = pack_bf16x2(e0 * sv[j], e1 * sv[j + 1]);
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
+    }
+
+    // ---- V codes -> bf16 rows in LDS, then transposed reads ----
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      uint16_t* dst = &vt[(i * ROWS_PER_LOAD + vrow) * LDS_ROW + vcol];
+      const uint2 a = i8x4_to_bf16x4(vr[i][0]);
+      const uint2 b2 = i8x4_to_bf16x4(vr[i][1]);
+      const uint2 c = i8x4_to_bf16x4(vr[i][2]);
+      const uint2 d2 = i8x4_to_bf16x4(vr[i][3]);
+      *reinterpret_cast<u32x4*>(dst) = u32x4{a.x, a.y, b2.x, b2.y};
+      *reinterpret_cast<u32x4*>(dst + 8) = u32x4{c.x, c.y, d2.x, d2.y};
+    }
+    __syncthreads();
+    if (more) load_v(c0 + kChunk);
+    const bf16x8 pa = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+    for (int t = 0; t < NTILES; ++t) {
+      const uint2 lo = lds_read_tr16(tr_src + 16 * t);
+      const uint2 hi = lds_read_tr16(tr_src + 16 * LDS_ROW + 16 * t);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                                       acc[t], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * g + i;
+    if (hb * 16 + hl < G) {
+      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
+    }
+  }
+  if (g == 0 && hq_ok) {
+    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    ml[0] = m_run;
+    ml[1] = l_run;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_split_int8(const void* q, const void* k_codes, const void* v_codes,
+                                    const float* k_scales, const float* v_scales,
+                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
+                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
+                                    float scale_log2, hipStream_t stream) {
+  const dim3 grid(plan.parts, K * plan.head_blocks, B);
+  auto qp = static_cast<const __bf16*>(q);
+  auto kp = static_cast<const int8_t*>(k_codes);
+  auto vp = static_cast<const int8_t*>(v_codes);
+#define GQA_I8(DD)                                                                              \
+  hipLaunchKernelGGL((decode_split_int8_kernel<DD>), grid, dim3(64), 0, stream, qp, kp, vp,      \
+                     k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max,         \
+                     plan.part_tokens, plan.parts, plan.head_blocks, scale_log2)
+  if (d == 128) GQA_I8(128); else GQA_I8(64);
+#undef GQA_I8
+  return hipGetLastError();
+}
+
+}  // namespace gqa

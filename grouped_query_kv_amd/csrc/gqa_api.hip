@@ -314,6 +314,81 @@ int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, cons
   return r ? r : ok();
 }
 
+int gqa_kv_quantize_int8(const void* src, void* codes, float* scales, int64_t rows, int d, int dtype,
+                         void* stream) {
+  const char* fn = "gqa_kv_quantize_int8";
+  if (!src || !codes || !scales) return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (rows < 1) return fail(GQA_ERR_INVALID, "%s: rows must be >= 1", fn);
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", fn, d);
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(codes) & 7u) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  const int r = check_hip(gqa::launch_quantize_rows_int8(src, codes, scales, rows, d, dtype == GQA_BF16,
+                                                         static_cast<hipStream_t>(stream)),
+                          "quantize launch");
+  return r ? r : ok();
+}
+
+int gqa_kv_append_int8(const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                       float* k_scales, float* v_scales, int32_t* seq_lens, int B, int K, int S_max,
+                       int d, int dtype, void* stream) {
+  const char* fn = "gqa_kv_append_int8";
+  if (!k_new || !v_new || !k_codes || !v_codes || !k_scales || !v_scales || !seq_lens)
+    return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (B < 1 || K < 1 || S_max < 1) return fail(GQA_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", fn, d);
+  if (dtype != GQA_F32 && dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_codes) || !aligned16(v_codes) ||
+      (reinterpret_cast<uintptr_t>(k_scales) & 3u) || (reinterpret_cast<uintptr_t>(v_scales) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  const int r = check_hip(gqa::launch_kv_append_int8(k_new, v_new, k_codes, v_codes, k_scales, v_scales,
+                                                     seq_lens, B, K, S_max, d, dtype == GQA_BF16,
+                                                     static_cast<hipStream_t>(stream)),
+                          "append launch");
+  return r ? r : ok();
+}
+
+int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
+                    const float* v_scales, const int32_t* seq_lens, void* out, void* workspace,
+                    size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len, int d,
+                    float scale, int q_dtype, int out_dtype, void* stream) {
+  const char* fn = "gqa_decode_int8";
+  if (!q || !k_codes || !v_codes || !k_scales || !v_scales || !seq_lens || !out)
+    return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (int r = validate_heads(fn, B, H, K, d)) return r;
+  if (S_max < 4 || S_max % 4 != 0 || max_seq_len < 0 || max_seq_len > S_max)
+    return fail(GQA_ERR_INVALID, "%s: need S_max a positive multiple of 4 and 0 <= max_seq_len <= S_max", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(GQA_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+  if (q_dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: queries must be bf16", fn);
+  if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
+    return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) ||
+      !aligned16(v_scales) || !aligned16(out) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d);
+  const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
+                need, workspace ? workspace_bytes : (size_t)0);
+  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, H, d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r;
+  {
+    TimedRegion timed(s);
+    r = check_hip(gqa::launch_decode_split_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, ws,
+                                                plan, B, H, K, S_max, d, scale * gqa::kLog2eHost, s),
+                  "partition-pass launch");
+  }
+  if (r) return r;
+  r = check_hip(gqa::launch_decode_combine(ws, const_cast<int32_t*>(seq_lens), out, plan, B, H, d,
+                                           out_dtype == GQA_BF16, false, s),
+                "combine-pass launch");
+  return r ? r : ok();
+}
+
 int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B, int H, int K,
                        int S, int S_max, int d, float scale, int dtype, int out_dtype, void* stream) {
   if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: null pointer");

@@ -72,6 +72,19 @@ hipError_t launch_decode_split_f32(const void* q, void* k_cache, void* v_cache,
                                    float scale_log2, const void* k_new, const void* v_new,
                                    hipStream_t stream);
 
+// int8 KV cache (codes [.., d] int8 plus one fp32 scale per row).
+hipError_t launch_quantize_rows_int8(const void* src, void* codes, float* scales, int64_t rows,
+                                     int d, bool bf16, hipStream_t stream);
+hipError_t launch_kv_append_int8(const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                                 float* k_scales, float* v_scales, int32_t* seq_lens, int B, int K,
+                                 int S_max, int d, bool bf16, hipStream_t stream);
+// Partition pass over an int8 cache (bf16 queries; S_max a multiple of 4).
+hipError_t launch_decode_split_int8(const void* q, const void* k_codes, const void* v_codes,
+                                    const float* k_scales, const float* v_scales,
+                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
+                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
+                                    float scale_log2, hipStream_t stream);
+
 // Combine pass: partials -> out (fp32 or bf16).  lens_from_ws: lengths come
 // from the workspace (fused append) and are published to seq_lens.
 hipError_t launch_decode_combine(const DecodeWorkspace& ws, int32_t* seq_lens, void* out,

@@ -65,6 +65,10 @@ WORKLOADS = {
         "decode_paged_llama3_8b", "decode", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
         append=True, note="decode_llama3_8b over a paged cache: 16-token blocks in shuffled order",
         extra={"block_size": 16}),
+    "decode_int8_llama3_8b": Workload(
+        "decode_int8_llama3_8b", "decode", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
+        append=True, note="decode_llama3_8b with the cache quantised to int8 (one fp32 scale per row)",
+        extra={"kv_dtype": "int8"}),
     "prefill_causal_4k": Workload(
         "prefill_causal_4k", "prefill", B=2, H=64, K=8, d=128, dtype="bf16", L=4096,
         note="causal prefill, S=4096, 64 query heads over 8 KV heads"),

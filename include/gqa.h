@@ -179,6 +179,52 @@ int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                      float scale, int dtype, int out_dtype, void* stream);
 
 /*
+ * int8 KV cache.  Codes k_codes, v_codes are int8 [B, K, S_max, d]; scales
+ * k_scales, v_scales are float [B, K, S_max], one per cached row; row
+ * (b, k, j) reads back as codes[b, k, j, i] * scales[b, k, j].  The pages
+ * give no quantisation rule; this library quantises each row of d elements
+ * symmetrically by its absolute maximum, in IEEE fp32 with correctly rounded
+ * division: amax = max |x_i|, c_i = clamp(rint(x_i * (127 / amax)), -127,
+ * 127), scale = amax / 127 (a zero row: codes 0, scale 0).  Rows must be
+ * finite.  (pinghaoyang.com.cn "GQA 完全拆解", the related-work list after the
+ * KV ledger: INT8 / INT4 KV quantisation is orthogonal to GQA and the savings
+ * multiply; aicoding.csdn.net "LLaMa3与DeepSeek采用的GQA技术", section 3
+ * (deployment tips): 8-bit KV quantisation halves the cache.)  An int8
+ * cache holds 2 (d + 4) bytes per position and KV head against 4 d in bf16.
+ */
+
+/*
+ * Quantise `rows` rows of d elements (src: GQA_F32 or GQA_BF16, [rows, d])
+ * into codes [rows, d] and scales [rows] by the rule above, bit-exactly.
+ * src 16-byte aligned, codes 8-byte aligned, scales 4-byte aligned.
+ */
+int gqa_kv_quantize_int8(const void* src, void* codes, float* scales, int64_t rows, int d,
+                         int dtype, void* stream);
+
+/*
+ * Append one token per sequence into an int8 cache: for every b with
+ * L = seq_lens[b] < S_max, quantise k_new[b, k, :] and v_new[b, k, :]
+ * (dtype GQA_F32 or GQA_BF16) and store codes and scales at position L of
+ * every KV head k, then seq_lens[b] = L + 1.  A full cache is left untouched.
+ */
+int gqa_kv_append_int8(const void* k_new, const void* v_new, void* k_codes, void* v_codes,
+                       float* k_scales, float* v_scales, int32_t* seq_lens, int B, int K,
+                       int S_max, int d, int dtype, void* stream);
+
+/*
+ * One decode step over an int8 cache: gqa_decode's result on the cache
+ * whose rows are the dequantised codes * scales.  q is bf16 [B, H, d]
+ * (q_dtype must be GQA_BF16); out_dtype GQA_BF16 or GQA_F32.  S_max must be
+ * a multiple of 4 (scale rows are read 16 bytes at a time) and every
+ * pointer 16-byte aligned.  Workspace: gqa_decode_workspace_bytes(B, H, K,
+ * max_seq_len, d) bytes.
+ */
+int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
+                    const float* v_scales, const int32_t* seq_lens, void* out, void* workspace,
+                    size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len, int d,
+                    float scale, int q_dtype, int out_dtype, void* stream);
+
+/*
  * Causal GQA attention over a whole prefix (prefill):
  *   out[b, h, i, :] = sum_{j <= i} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
  * for i in [0, S).  k and v are [B, K, S_max, d] with S <= S_max; rows >= S

@@ -178,6 +178,53 @@ def test_append_paged_rejects(lib, args, code):
     assert lib.gqa_last_error().decode().startswith("gqa_kv_append_paged")
 
 
+def _decode_int8(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, sl=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30, B=2, H=32,
+             K=8, S_max=128, max_seq_len=100, d=128, scale=0.088, q_dtype=B.GQA_BF16, out_dtype=B.GQA_BF16)
+    a.update(kw)
+    return lib.gqa_decode_int8(a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["sl"], a["out"], a["ws"], a["wsb"],
+                               a["B"], a["H"], a["K"], a["S_max"], a["max_seq_len"], a["d"], a["scale"],
+                               a["q_dtype"], a["out_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=None), B.GQA_ERR_INVALID),
+    (dict(S_max=130, max_seq_len=100), B.GQA_ERR_INVALID),   # scale rows need S_max % 4 == 0
+    (dict(max_seq_len=129), B.GQA_ERR_INVALID),
+    (dict(q_dtype=B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    (dict(out_dtype=5), B.GQA_ERR_UNSUPPORTED),
+    (dict(d=96), B.GQA_ERR_UNSUPPORTED),
+    (dict(vs=FAKE + 4), B.GQA_ERR_INVALID),
+    (dict(scale=-1.0), B.GQA_ERR_INVALID),
+    (dict(wsb=32), B.GQA_ERR_WORKSPACE),
+])
+def test_decode_int8_rejects(lib, kw, code):
+    assert _decode_int8(lib, **kw) == code
+    assert lib.gqa_last_error().decode().startswith("gqa_decode_int8")
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, 10, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, 0, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, 10, 32, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, 10, 128, 3), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE + 8, FAKE, FAKE, 10, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE + 4, FAKE, 10, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+])
+def test_quantize_int8_rejects(lib, args, code):
+    assert lib.gqa_kv_quantize_int8(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, 8, 16, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 0, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 16, 128, 7), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE + 2, FAKE, FAKE, FAKE, FAKE, 2, 8, 16, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+])
+def test_append_int8_rejects(lib, args, code):
+    assert lib.gqa_kv_append_int8(*args, None) == code
+
+
 def test_timing_events_need_both(lib):
     assert lib.gqa_set_timing_events(FAKE, None) == B.GQA_ERR_INVALID
     assert lib.gqa_set_timing_events(None, None) == B.GQA_OK
