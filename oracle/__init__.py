@@ -9,7 +9,8 @@ hot path computes, written from the pages' description of the method:
 
 * ``gqa_oracle``  -- the definitions (decode, causal prefill, cache append,
   paged-cache gather / decode / append, int8 cache quantisation / decode /
-  append, mean-pool conversion, KV-cache byte count), vectorised with NumPy.
+  append, chunked prefill over a cache, cross-attention, multi-row append,
+  mean-pool conversion, KV-cache byte count), vectorised with NumPy.
 * ``bruteforce``  -- the same definitions as pure-Python scalar loops, for
   tiny inputs only; it derives the query-head -> KV-head grouping from the
   page's 1-based group formula independently of ``gqa_oracle``.
@@ -32,4 +33,7 @@ from .gqa_oracle import (  # noqa: F401
     dequantize_int8_ref,
     decode_int8_ref,
     kv_append_int8_ref,
+    prefill_chunk_ref,
+    cross_attention_ref,
+    kv_append_rows_ref,
 )

@@ -354,3 +354,100 @@ def kv_append_int8_ref(k_new, v_new, k_codes, v_codes, k_scales, v_scales, seq_l
         vs[b, :, L] = vqs[b]
         sl[b] = L + 1
     return kc, vc, ks, vs, sl
+
+
+# --------------------------------------------------------------------------
+# Prefill over an existing cache (chunked prefill) and cross-attention
+# --------------------------------------------------------------------------
+# [PHY] memory ledger: the query at position t attends to cached rows 1..t;
+# prefill computes a whole run of positions at once.  Reading: a chunk of
+# S_q new tokens whose K/V rows have been appended, so that the cache of
+# sequence b holds L_b rows ending with the chunk, puts query i at absolute
+# position L_b - S_q + i; it attends causally to rows j <= L_b - S_q + i.
+# [PHY] GQA section: GQA is used for decoder self-attention and for
+# cross-attention (not for encoder self-attention); cross-attention has no
+# causal mask: every query attends to all L_b rows of its (encoder) K/V.
+# A query with no visible row gets a zero output row.
+
+
+def _attend_rows(q_rows, Kc, Vc, keep, scale):
+    """softmax(scale * q_rows @ Kc^T) @ Vc over the kept keys; rows with no
+    kept key are zero.  q_rows [R, d], Kc/Vc [L, d], keep [R, L] bool."""
+    out = np.zeros((q_rows.shape[0], Vc.shape[1]))
+    if Kc.shape[0] == 0:
+        return out
+    s = float(scale) * (q_rows @ Kc.T)
+    s = np.where(keep, s, -np.inf)
+    has = keep.any(axis=1)
+    if has.any():
+        out[has] = _softmax_rows(s[has]) @ Vc
+    return out
+
+
+def prefill_chunk_ref(q, k_cache, v_cache, seq_lens, scale) -> np.ndarray:
+    """Causal GQA attention of a chunk of S_q queries over a cache that
+    already holds the chunk: q [B, H, S_q, d], caches [B, K, S_max, d],
+    seq_lens [B] = L_b (rows in the cache, chunk included).  Query i of
+    sequence b sits at position L_b - S_q + i and sees rows
+    j <= L_b - S_q + i (j < L_b).  Returns [B, H, S_q, d] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, Sq, d = q.shape
+    K = k_cache.shape[1]
+    if H % K != 0:
+        raise ValueError("H must be divisible by K")
+    G = H // K
+    out = np.zeros((B, H, Sq, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if not 0 <= L <= k_cache.shape[2]:
+            raise ValueError("seq_lens out of range")
+        pos = L - Sq + np.arange(Sq)                                  # absolute positions
+        keep = np.arange(L)[None, :] <= pos[:, None]                  # [S_q, L]
+        for g in range(K):
+            Kc = np.asarray(k_cache[b, g, :L, :], dtype=np.float64)
+            Vc = np.asarray(v_cache[b, g, :L, :], dtype=np.float64)
+            for h in range(g * G, (g + 1) * G):
+                out[b, h] = _attend_rows(q[b, h], Kc, Vc, keep, scale)
+    return out
+
+
+def cross_attention_ref(q, k, v, kv_lens, scale) -> np.ndarray:
+    """Non-causal GQA attention: q [B, H, S_q, d] over rows [0, L_b) of
+    k, v [B, K, S_max, d], L_b = kv_lens[b].  Returns [B, H, S_q, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, Sq, d = q.shape
+    K = k.shape[1]
+    if H % K != 0:
+        raise ValueError("H must be divisible by K")
+    G = H // K
+    out = np.zeros((B, H, Sq, d))
+    for b in range(B):
+        L = int(kv_lens[b])
+        if not 0 <= L <= k.shape[2]:
+            raise ValueError("kv_lens out of range")
+        keep = np.ones((Sq, L), dtype=bool)
+        for g in range(K):
+            Kc = np.asarray(k[b, g, :L, :], dtype=np.float64)
+            Vc = np.asarray(v[b, g, :L, :], dtype=np.float64)
+            for h in range(g * G, (g + 1) * G):
+                out[b, h] = _attend_rows(q[b, h], Kc, Vc, keep, scale)
+    return out
+
+
+def kv_append_rows_ref(k_new, v_new, k_cache, v_cache, seq_lens):
+    """Append T rows per (b, KV head): k_new, v_new [B, K, T, d] go to
+    positions [L_b, L_b + T) and L_b becomes L_b + T; a sequence without room
+    for all T rows (L_b + T > S_max) is left unchanged.  Any dtype."""
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    sl = np.array(seq_lens, copy=True)
+    T = k_new.shape[2]
+    S_max = kc.shape[2]
+    for b in range(kc.shape[0]):
+        L = int(sl[b])
+        if L + T > S_max:
+            continue
+        kc[b, :, L:L + T, :] = k_new[b]
+        vc[b, :, L:L + T, :] = v_new[b]
+        sl[b] = L + T
+    return kc, vc, sl

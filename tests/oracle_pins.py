@@ -539,6 +539,80 @@ def check_int8_append(O):
     assert np.all(np.abs(O.dequantize_int8_ref(kq, kqs) - kn) <= kqs[..., None] * 0.50001)
 
 
+# --------------------------------------------------------------------------
+# chunked prefill over a cache, cross-attention, multi-row append
+# --------------------------------------------------------------------------
+def check_chunk_equals_causal_rows(O):
+    """A chunk of S_q queries at the end of a cache of L_b rows gives rows
+    [L_b - S_q, L_b) of causal prefill over the whole sequence (the pages:
+    prefill row i is what decode step i computes)."""
+    r = _rng(2600)
+    B, H, K, d, Sq, S = 3, 6, 2, 8, 5, 14
+    lens = [14, 9, 5]
+    qf = r.standard_normal((B, H, S, d))
+    k = r.standard_normal((B, K, S, d))
+    v = r.standard_normal((B, K, S, d))
+    qc = np.stack([qf[b, :, L - Sq:L] for b, L in enumerate(lens)])
+    got = O.prefill_chunk_ref(qc, k, v, np.array(lens), 0.4)
+    for b, L in enumerate(lens):
+        want = O.prefill_causal_ref(qf[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], 0.4,
+                                    rows=range(L - Sq, L))
+        _close(got[b], want[0], 1e-13, f"chunk rows of sequence {b}")
+
+
+def check_chunk_single_token_is_decode(O):
+    q, kc, vc, sl = _rand_decode(2700, 3, 8, 2, 6, [7, 1, 12], nan_tail=False)
+    got = O.prefill_chunk_ref(q[:, :, None, :], kc, vc, sl, 0.3)
+    _close(got[:, :, 0], O.decode_ref(q, kc, vc, sl, 0.3), 1e-14, "chunk of one = decode")
+    ref = BF.decode_bruteforce(q.tolist(), kc.tolist(), vc.tolist(), sl.tolist(), 0.3)
+    _close(got[:, :, 0], ref, 1e-13, "chunk of one vs brute force")
+
+
+def check_cross_attention_sdpa(O):
+    """Non-causal GQA: torch's fp64 scaled_dot_product_attention with
+    enable_gqa (no mask) on each sequence's valid rows."""
+    r = _rng(2800)
+    B, H, K, d, Sq, S = 3, 8, 2, 16, 7, 20
+    lens = [20, 3, 11]
+    q = r.standard_normal((B, H, Sq, d))
+    k = r.standard_normal((B, K, S, d))
+    v = r.standard_normal((B, K, S, d))
+    got = O.cross_attention_ref(q, k, v, np.array(lens), 0.25)
+    for b, L in enumerate(lens):
+        want = _sdpa(q[b:b + 1], k[b:b + 1, :, :L].copy(), v[b:b + 1, :, :L].copy(), 0.25)
+        _close(got[b], want[0], 1e-12, f"cross-attention sequence {b}")
+
+
+def check_cross_rows_are_decodes(O):
+    """Each query row of cross-attention is a decode step over all L_b rows;
+    L_b = 0 gives zeros, and the rows do not depend on each other."""
+    q, kc, vc, sl = _rand_decode(2900, 2, 4, 4, 8, [6, 0], nan_tail=False)
+    qq = np.stack([q, -q, 2 * q], axis=2)                                     # [B, H, 3, d]
+    got = O.cross_attention_ref(qq, kc, vc, sl, 0.5)
+    for i in range(3):
+        _close(got[:, :, i], O.decode_ref(qq[:, :, i], kc, vc, sl, 0.5), 1e-14, f"cross row {i}")
+    assert np.all(got[1] == 0)
+
+
+def check_append_rows(O):
+    r = _rng(3000)
+    B, K, S, d, T = 3, 2, 9, 4, 3
+    kc = r.integers(-9999, 9999, (B, K, S, d), dtype=np.int16)
+    vc = r.integers(-9999, 9999, (B, K, S, d), dtype=np.int16)
+    kn = r.integers(-9999, 9999, (B, K, T, d), dtype=np.int16)
+    vn = r.integers(-9999, 9999, (B, K, T, d), dtype=np.int16)
+    sl = np.array([0, 6, 7])                          # the last has no room for 3 rows
+    k2, v2, s2 = O.kv_append_rows_ref(kn, vn, kc, vc, sl)
+    assert list(s2) == [3, 9, 7]
+    # the same as T single-row appends (for the sequences with room)
+    k3, v3, s3 = kc, vc, sl
+    for t in range(T):
+        k3, v3, s3 = O.kv_append_ref(kn[:, :, t], vn[:, :, t], k3, v3, s3)
+    for b in (0, 1):
+        assert np.array_equal(k2[b], k3[b]) and np.array_equal(v2[b], v3[b])
+    assert np.array_equal(k2[2], kc[2]) and np.array_equal(v2[2], vc[2])
+
+
 ALL_CHECKS = [
     check_kv_bytes_golden, check_kv_head_map,
     check_bruteforce_decode, check_bruteforce_prefill, check_bruteforce_meanpool,
@@ -552,4 +626,6 @@ ALL_CHECKS = [
     check_paged_append_identity,
     check_int8_exact_grid, check_int8_ties_to_even, check_int8_bounds_and_invariants,
     check_int8_halves_cache, check_int8_decode_composition, check_int8_append,
+    check_chunk_equals_causal_rows, check_chunk_single_token_is_decode, check_cross_attention_sdpa,
+    check_cross_rows_are_decodes, check_append_rows,
 ]

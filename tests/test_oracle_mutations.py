@@ -78,6 +78,21 @@ MUTATIONS = {
                                     "return np.asarray(codes, dtype=np.float64) / 127.0")],
     "int8_append_unquantised": [("        kc[b, :, L, :] = kq[b]\n", "        kc[b, :, L, :] = k_new[b]\n")],
     "int8_append_scale_swapped": [("        ks[b, :, L] = kqs[b]\n", "        ks[b, :, L] = vqs[b]\n")],
+    "chunk_offset_plus_one": [("pos = L - Sq + np.arange(Sq)", "pos = L - Sq + 1 + np.arange(Sq)")],
+    "chunk_offset_from_zero": [("pos = L - Sq + np.arange(Sq)", "pos = np.arange(Sq)")],
+    "chunk_strict_mask": [("keep = np.arange(L)[None, :] <= pos[:, None]", "keep = np.arange(L)[None, :] < pos[:, None]")],
+    "cross_causal": [("keep = np.ones((Sq, L), dtype=bool)", "keep = np.arange(L)[None, :] <= np.arange(Sq)[:, None]")],
+    "cross_drops_last_row": [("Kc = np.asarray(k[b, g, :L, :], dtype=np.float64)",
+                              "Kc = np.asarray(k[b, g, :max(L - 1, 0), :], dtype=np.float64)"),
+                             ("Vc = np.asarray(v[b, g, :L, :], dtype=np.float64)",
+                              "Vc = np.asarray(v[b, g, :max(L - 1, 0), :], dtype=np.float64)"),
+                             ("keep = np.ones((Sq, L), dtype=bool)", "keep = np.ones((Sq, max(L - 1, 0)), dtype=bool)")],
+    "cross_group_interleaved": [("        keep = np.ones((Sq, L), dtype=bool)\n        for g in range(K):\n            Kc = np.asarray(k[b, g, :L, :], dtype=np.float64)\n            Vc = np.asarray(v[b, g, :L, :], dtype=np.float64)\n            for h in range(g * G, (g + 1) * G):",
+                                 "        keep = np.ones((Sq, L), dtype=bool)\n        for g in range(K):\n            Kc = np.asarray(k[b, g, :L, :], dtype=np.float64)\n            Vc = np.asarray(v[b, g, :L, :], dtype=np.float64)\n            for h in range(g, H, K):")],
+    "attend_rows_unmasked": [("    s = np.where(keep, s, -np.inf)\n    has", "    has")],
+    "append_rows_partial": [("        if L + T > S_max:\n            continue\n        kc[b, :, L:L + T, :] = k_new[b]",
+                             "        if L >= S_max:\n            continue\n        T2 = min(T, S_max - L)\n        kc[b, :, L:L + T2, :] = k_new[b, :, :T2]")],
+    "append_rows_no_increment": [("        sl[b] = L + T\n", "        sl[b] = L + 1\n")],
     "empty_length_nan": [("        if L == 0:\n            continue\n        for k in range(K):",
                           "        for k in range(K):")],
 }
