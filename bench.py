@@ -3,7 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 With --workload prefill_causal_4k it times the causal prefill instead (one
-step = one prefill of the whole batch; value in TFLOP/s of unmasked work).
+step = one prefill of the whole batch; value in TFLOP/s of unmasked work);
+prefill_chunk_8k times a chunked-prefill step (append a 2048-row chunk, then
+its queries attend over the 8192-row cache) and cross_attention_4k a
+non-causal cross-attention step.
 
 A step is one pass of the whole decode hot path over one batch: append the
 new token's K/V rows of every sequence and attend over the cache including
@@ -283,12 +286,22 @@ def bench_decode(args, w):
     return res, inp
 
 
+def visible_pairs(w):
+    """(query, key) pairs that carry weight, per (sequence, head)."""
+    if w.kind == "prefill":
+        return w.L * (w.L + 1) // 2
+    if w.kind == "chunk":
+        T = w.extra["chunk"]
+        return T * (w.L - T) + T * (T + 1) // 2
+    return w.extra["S_q"] * w.L                       # cross-attention: no mask
+
+
 def cpu_baseline_prefill(inp, w, budget_s):
     """Time the fp64 oracle (unchanged) on whole (sequence, head) slices of
-    the prefill workload, one BLAS thread, until about `budget_s` seconds."""
+    the workload, one BLAS thread, until about `budget_s` seconds."""
     from threadpoolctl import threadpool_limits
 
-    from oracle import prefill_causal_ref
+    from oracle import cross_attention_ref, prefill_causal_ref, prefill_chunk_ref
 
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     G = w.H // w.K
@@ -297,19 +310,40 @@ def cpu_baseline_prefill(inp, w, budget_s):
         while t_used < budget_s and heads < w.B * w.H:
             b, h = divmod(heads, w.H)
             q = inp["q"][b:b + 1, h:h + 1].double().numpy()
-            k = inp["k"][b:b + 1, h // G:h // G + 1].float().numpy()
-            v = inp["v"][b:b + 1, h // G:h // G + 1].float().numpy()
+            kv = slice(h // G, h // G + 1)
+            if w.kind == "chunk":   # the cache after the chunk's append
+                T = w.extra["chunk"]
+                L0 = w.L - T
+                k = torch.cat([inp["k"][b:b + 1, kv, :L0], inp["k_new"][b:b + 1, kv]], dim=2).float().numpy()
+                v = torch.cat([inp["v"][b:b + 1, kv, :L0], inp["v_new"][b:b + 1, kv]], dim=2).float().numpy()
+            else:
+                k = inp["k"][b:b + 1, kv].float().numpy()
+                v = inp["v"][b:b + 1, kv].float().numpy()
             t0 = time.perf_counter()
-            prefill_causal_ref(q, k, v, scale)
+            if w.kind == "prefill":
+                prefill_causal_ref(q, k, v, scale)
+            elif w.kind == "chunk":
+                prefill_chunk_ref(q, k, v, np.array([w.L]), scale)
+            else:
+                cross_attention_ref(q, k, v, np.array([w.L]), scale)
             t_used += time.perf_counter() - t0
-            done += 2.0 * w.d * w.L * (w.L + 1)
+            done += 4.0 * w.d * visible_pairs(w)
             heads += 1
     return {"value": done / t_used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{heads} whole (sequence, head) slices of the workload ({w.L} causal rows each), "
+            "sample": f"{heads} whole (sequence, head) slices of the workload, "
                       f"{t_used:.1f} s of fp64 NumPy on 1 thread"}
 
 
+PREFILL_METRIC = {
+    "prefill": "GQA causal prefill TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
+    "chunk": "GQA chunked prefill over a KV cache TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
+    "cross": "GQA cross-attention TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
+}
+
+
 def bench_prefill(args, w):
+    """Prefill-family step: causal prefill; chunked prefill (append the
+    chunk's rows, then its queries attend over the cache); cross-attention."""
     import grouped_query_kv_amd as gqa
     from grouped_query_kv_amd.inputs import workload_inputs
 
@@ -321,34 +355,55 @@ def bench_prefill(args, w):
     out = torch.empty_like(q)
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     stream = torch.cuda.current_stream()
+    if w.kind != "prefill":
+        lens0 = inp["kv_lens"].to(dev)
+        lens = lens0.clone()
+    if w.kind == "chunk":
+        kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
+
+    def step(ev=None):
+        if w.kind == "chunk":
+            lens.copy_(lens0)          # every step appends the same chunk to the same cache
+            gqa.gqa_kv_append_rows(kn, vn, k, v, lens, stream=stream)
+        if ev is not None:
+            gqa.gqa_set_timing_events(*ev)
+        if w.kind == "prefill":
+            gqa.gqa_prefill_causal(q, k, v, out, scale=scale, stream=stream)
+        elif w.kind == "chunk":
+            gqa.gqa_prefill_chunk(q, k, v, lens, out, scale=scale, stream=stream)
+        else:
+            gqa.gqa_cross_attention(q, k, v, lens, out, scale=scale, stream=stream)
+        if ev is not None:
+            gqa.gqa_set_timing_events(None, None)
+
     for _ in range(args.warmup):
-        gqa.gqa_prefill_causal(q, k, v, out, scale=scale, stream=stream)
+        step()
     events = [(gqa.HipEvent(), gqa.HipEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for ev in events:
-        gqa.gqa_set_timing_events(*ev)
-        gqa.gqa_prefill_causal(q, k, v, out, scale=scale, stream=stream)
-        gqa.gqa_set_timing_events(None, None)
+        step(ev)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern_ms = float(np.mean([a.elapsed_ms(b) for a, b in events]))
-    flops = 2.0 * w.B * w.H * w.d * w.L * (w.L + 1)   # unmasked (j <= i) score entries only
+    flops = 4.0 * w.B * w.H * w.d * visible_pairs(w)   # two products, visible pairs only
     ms_per_step = elapsed * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kern_ms * 1e-3) / 1e12
+    S_q = {"prefill": w.L, "chunk": w.extra.get("chunk"), "cross": w.extra.get("S_q")}[w.kind]
+    cfg = {"workload": w.name, "B": w.B, "H": w.H, "K": w.K, "d": w.d, "S_q": S_q, "kv_len": w.L,
+           "parallelism": "single GPU"}
     res = {
-        "metric": "GQA causal prefill TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
+        "metric": PREFILL_METRIC[w.kind],
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "K": w.K, "d": w.d, "S": w.L,
-                   "parallelism": "single GPU"},
-        "tokens_per_s": round(w.B * w.L / (ms_per_step * 1e-3), 1),
-        "roofline": {"kernel": "causal prefill (prefill_causal_kernel)", "bound": "mfma",
+        "config": cfg,
+        "tokens_per_s": round(w.B * S_q / (ms_per_step * 1e-3), 1),
+        "roofline": {"kernel": f"{w.kind} attention (prefill_kernel)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic("prefill_causal_kernel"),
+                     "traffic": recorded_traffic("prefill_causal_kernel") if w.kind == "prefill" else None,
                      "avg_kernel_us": round(kern_ms * 1e3, 3)},
         "input_gen_s": round(t_gen, 1),
     }
@@ -364,7 +419,7 @@ def main():
     from grouped_query_kv_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    if w.kind == "prefill":
+    if w.kind in ("prefill", "chunk", "cross"):
         res, inp = bench_prefill(args, w)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline_prefill(inp, w, args.cpu_seconds)

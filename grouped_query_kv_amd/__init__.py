@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     GQAError,
     HipEvent,
     gqa_abi_version,
+    gqa_cross_attention,
     gqa_decode,
     gqa_decode_append,
     gqa_decode_int8,
@@ -20,11 +21,13 @@ from ._binding import (  # noqa: F401
     gqa_kv_append,
     gqa_kv_append_paged,
     gqa_kv_append_int8,
+    gqa_kv_append_rows,
     gqa_kv_quantize_int8,
     gqa_kv_cache_bytes,
     gqa_last_error,
     gqa_meanpool_convert,
     gqa_prefill_causal,
+    gqa_prefill_chunk,
     gqa_set_timing_events,
     header_symbols,
     load_library,

@@ -43,6 +43,9 @@ _SIGNATURES = {
     "gqa_kv_quantize_int8": (_c_int, [_c_void_p] * 3 + [_c_int64, _c_int, _c_int, _c_void_p]),
     "gqa_kv_append_int8": (_c_int, [_c_void_p] * 7 + [_c_int] * 5 + [_c_void_p]),
     "gqa_decode_int8": (_c_int, [_c_void_p] * 8 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_prefill_chunk": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_cross_attention": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_kv_append_rows": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_void_p]),
     "gqa_prefill_causal": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_meanpool_convert": (_c_int, [_c_void_p, _c_void_p, _c_int64, _c_int, _c_int, _c_int64, _c_int, _c_void_p]),
 }
@@ -402,6 +405,68 @@ def gqa_prefill_causal(q, k, v, out, scale: float | None = None, stream=None) ->
     _check("gqa_prefill_causal", lib.gqa_prefill_causal(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, K, S, S_max, d,
         float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def _prefill_shapes(q, k, v, out):
+    _need(q, "q", 4, (torch.bfloat16,))
+    _need(k, "k", 4, (torch.bfloat16,))
+    _need(v, "v", 4, (torch.bfloat16,))
+    _need(out, "out", 4)
+    B, H, S, d = q.shape
+    Bk, K, S_max, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape or tuple(out.shape) != (B, H, S, d):
+        raise ValueError("shape mismatch between q, k, v and out")
+    return B, H, S, d, K, S_max
+
+
+def gqa_prefill_chunk(q, k_cache, v_cache, seq_lens, out, scale: float | None = None, stream=None) -> None:
+    """Causal attention of the last S positions (q/out [B,H,S,d]) over caches
+    [B,K,S_max,d] holding seq_lens[b] rows, the chunk included."""
+    B, H, S, d, K, S_max = _prefill_shapes(q, k_cache, v_cache, out)
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("gqa_prefill_chunk", load_library().gqa_prefill_chunk(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+        B, H, K, S, S_max, d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def gqa_cross_attention(q, k, v, kv_lens, out, scale: float | None = None, stream=None) -> None:
+    """Non-causal attention of q/out [B,H,S_q,d] over rows [0, kv_lens[b]) of
+    k, v [B,K,S_max,d]."""
+    B, H, S, d, K, S_max = _prefill_shapes(q, k, v, out)
+    _need(kv_lens, "kv_lens", 1, (torch.int32,))
+    if kv_lens.numel() != B:
+        raise ValueError("kv_lens must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("gqa_cross_attention", load_library().gqa_cross_attention(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_lens.data_ptr(), out.data_ptr(),
+        B, H, K, S, S_max, d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def gqa_kv_append_rows(k_new, v_new, k_cache, v_cache, seq_lens, stream=None) -> None:
+    """Append k_new/v_new [B,K,T,d] at rows [seq_lens[b], seq_lens[b] + T) of
+    the caches [B,K,S_max,d] and add T to seq_lens."""
+    _need(k_cache, "k_cache", 4)
+    B, K, S_max, d = k_cache.shape
+    _need(v_cache, "v_cache", 4)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    _need(k_new, "k_new", 4)
+    _need(v_new, "v_new", 4)
+    T = k_new.shape[2]
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        if tuple(t.shape) != (B, K, T, d) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{nm} must be [B,K,T,d] of the cache dtype")
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    _check("gqa_kv_append_rows", load_library().gqa_kv_append_rows(
+        k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+        B, K, T, S_max, d, _DTYPE_CODE[k_cache.dtype], _stream(stream)))
 
 
 def gqa_meanpool_convert(src, dst, stream=None) -> None:

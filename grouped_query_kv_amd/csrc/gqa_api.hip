@@ -389,27 +389,71 @@ int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, con
   return r ? r : ok();
 }
 
-int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B, int H, int K,
-                       int S, int S_max, int d, float scale, int dtype, int out_dtype, void* stream) {
-  if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: null pointer");
-  if (int r = validate_heads("gqa_prefill_causal", B, H, K, d)) return r;
-  if (S < 1 || S_max < S) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: need 1 <= S <= S_max");
+// Shared validation and launch of the prefill family.
+static int prefill_impl(const char* fn, const void* q, const void* k, const void* v, void* out,
+                        const int32_t* kv_lens, int B, int H, int K, int S, int S_kv, int S_max,
+                        int d, float scale, int dtype, int out_dtype, bool causal, void* stream) {
+  if (!q || !k || !v || !out) return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (int r = validate_heads(fn, B, H, K, d)) return r;
+  if (S < 1 || S_max < 1 || S_kv > S_max)
+    return fail(GQA_ERR_INVALID, "%s: need S >= 1 and key lengths <= S_max", fn);
   if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(GQA_ERR_INVALID, "gqa_prefill_causal: scale must be finite and > 0");
-  if (dtype != GQA_BF16)
-    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_causal: only bf16 inputs (matrix-core path)");
+    return fail(GQA_ERR_INVALID, "%s: scale must be finite and > 0", fn);
+  if (dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: only bf16 inputs (matrix-core path)", fn);
   if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
-    return fail(GQA_ERR_UNSUPPORTED, "gqa_prefill_causal: out_dtype %d", out_dtype);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(GQA_ERR_INVALID, "gqa_prefill_causal: misaligned pointer");
+    return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(kv_lens) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int r;
   {
     TimedRegion timed(s);
-    r = check_hip(gqa::launch_prefill_causal_bf16(q, k, v, out, B, H, K, S, S_max, d,
-                                                  scale * gqa::kLog2eHost, out_dtype == GQA_BF16, s),
-                  "gqa_prefill_causal launch");
+    r = check_hip(gqa::launch_prefill_bf16(q, k, v, out, kv_lens, B, H, K, S, S_kv, S_max, d,
+                                           scale * gqa::kLog2eHost, out_dtype == GQA_BF16, causal, s),
+                  "prefill launch");
   }
+  return r ? r : ok();
+}
+
+int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out, int B, int H, int K,
+                       int S, int S_max, int d, float scale, int dtype, int out_dtype, void* stream) {
+  if (S < 1 || S_max < S) return fail(GQA_ERR_INVALID, "gqa_prefill_causal: need 1 <= S <= S_max");
+  return prefill_impl("gqa_prefill_causal", q, k, v, out, nullptr, B, H, K, S, S, S_max, d, scale,
+                      dtype, out_dtype, true, stream);
+}
+
+int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                      void* out, int B, int H, int K, int S, int S_max, int d, float scale, int dtype,
+                      int out_dtype, void* stream) {
+  if (!seq_lens) return fail(GQA_ERR_INVALID, "gqa_prefill_chunk: null pointer");
+  if (S < 1 || S_max < S) return fail(GQA_ERR_INVALID, "gqa_prefill_chunk: need 1 <= S <= S_max");
+  return prefill_impl("gqa_prefill_chunk", q, k_cache, v_cache, out, seq_lens, B, H, K, S, 0, S_max, d,
+                      scale, dtype, out_dtype, true, stream);
+}
+
+int gqa_cross_attention(const void* q, const void* k, const void* v, const int32_t* kv_lens, void* out,
+                        int B, int H, int K, int S_q, int S_max, int d, float scale, int dtype,
+                        int out_dtype, void* stream) {
+  if (!kv_lens) return fail(GQA_ERR_INVALID, "gqa_cross_attention: null pointer");
+  return prefill_impl("gqa_cross_attention", q, k, v, out, kv_lens, B, H, K, S_q, 0, S_max, d, scale,
+                      dtype, out_dtype, false, stream);
+}
+
+int gqa_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       int32_t* seq_lens, int B, int K, int T, int S_max, int d, int dtype, void* stream) {
+  const char* fn = "gqa_kv_append_rows";
+  if (!k_new || !v_new || !k_cache || !v_cache || !seq_lens) return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (B < 1 || K < 1 || T < 1 || S_max < 1) return fail(GQA_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", fn, d);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(GQA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  const int r = check_hip(gqa::launch_kv_append_rows(k_new, v_new, k_cache, v_cache, seq_lens, B, K, T,
+                                                     S_max, d * eb, static_cast<hipStream_t>(stream)),
+                          "append launch");
   return r ? r : ok();
 }
 

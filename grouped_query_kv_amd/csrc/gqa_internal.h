@@ -91,9 +91,18 @@ hipError_t launch_decode_combine(const DecodeWorkspace& ws, int32_t* seq_lens, v
                                  const DecodePlan& plan, int B, int H, int d, bool out_bf16,
                                  bool lens_from_ws, hipStream_t stream);
 
-hipError_t launch_prefill_causal_bf16(const void* q, const void* k, const void* v, void* out,
-                                      int B, int H, int K, int S, int S_max, int d,
-                                      float scale_log2, bool out_bf16, hipStream_t stream);
+// Prefill family (bf16 in): S queries per sequence over L_b keys
+// (kv_lens[b], or S_kv when kv_lens is null); causal: key j visible to query
+// i iff j <= L_b - S + i.
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out,
+                               const int32_t* kv_lens, int B, int H, int K, int S, int S_kv,
+                               int S_max, int d, float scale_log2, bool out_bf16, bool causal,
+                               hipStream_t stream);
+
+// Append T rows per (sequence, KV head) at seq_lens[b] (two launches).
+hipError_t launch_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 int32_t* seq_lens, int B, int K, int T, int S_max, int row_bytes,
+                                 hipStream_t stream);
 
 hipError_t launch_meanpool(const void* src, void* dst, int64_t outer, int H, int K, int64_t inner,
                            bool bf16, hipStream_t stream);

@@ -65,7 +65,53 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_paged_kernel(
   if (threadIdx.x == 0) seq_lens[b] = L + 1;
 }
 
+// Multi-row variant: T rows per (sequence, KV head) go to positions
+// [L, L + T); a sequence without room for all T rows is left untouched.
+__global__ __launch_bounds__(kAppendThreads) void kv_append_rows_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int32_t* __restrict__ seq_lens,
+    int K, int T, int S_max, int row_words) {
+  const int b = blockIdx.x;
+  const int L = seq_lens[b];
+  __syncthreads();
+  if (L < 0 || L > S_max - T) return;
+  const int words = T * row_words;  // per KV head: T consecutive rows in both layouts
+  for (int k = blockIdx.y; k < K; k += gridDim.y) {
+    const size_t src0 = ((size_t)b * K + k) * words;
+    const size_t dst0 = (((size_t)b * K + k) * S_max + L) * row_words;
+    for (int w = threadIdx.x; w < words; w += kAppendThreads) {
+      k_cache[dst0 + w] = k_new[src0 + w];
+      v_cache[dst0 + w] = v_new[src0 + w];
+    }
+  }
+}
+
+// Publishes the new lengths once every copy of kv_append_rows_kernel has read
+// the old ones (a separate launch orders the two).
+__global__ void bump_lens_kernel(int32_t* __restrict__ seq_lens, int B, int T, int S_max) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) {
+    const int L = seq_lens[b];
+    if (L >= 0 && L <= S_max - T) seq_lens[b] = L + T;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 int32_t* seq_lens, int B, int K, int T, int S_max, int row_bytes,
+                                 hipStream_t stream) {
+  const int ky = K < 8 ? K : 8;
+  hipLaunchKernelGGL(kv_append_rows_kernel, dim3(B, ky), dim3(kAppendThreads), 0, stream,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), seq_lens, K, T,
+                     S_max, row_bytes / 16);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bump_lens_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, seq_lens, B, T,
+                     S_max);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append_paged(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                                   const PagedArgs& pg, int32_t* seq_lens, int B, int K,

@@ -1,6 +1,15 @@
-// Causal GQA prefill on the gfx950 matrix cores (bf16 in, fp32 accumulate).
+// GQA prefill on the gfx950 matrix cores (bf16 in, fp32 accumulate): causal
+// prefill, prefill of a chunk over a cache, and non-causal cross-attention.
 //
-// out[b,h,i,:] = sum_{j<=i} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
+// out[b,h,i,:] = sum_{j visible} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
+//
+// With L_b keys in the cache (kv_lens[b], or S_kv for every sequence) and
+// S query positions, key j is visible to query i iff j < L_b and, when
+// causal, j <= L_b - S + i: the queries are the last S positions of the
+// sequence (L_b = S is plain causal prefill; L_b > S is a chunk appended to
+// a cache holding L_b - S earlier rows).  Non-causal: every j < L_b (GQA in
+// cross-attention, pinghaoyang.com.cn "GQA 完全拆解", GQA section).  A query
+// with no visible key gets a zero row.
 //
 // pinghaoyang.com.cn "GQA 完全拆解": section 解码推理的内存账本 (prefill runs the
 // whole prefix in parallel; row i is what decode step i computes) and section
@@ -9,9 +18,12 @@
 // group).  compassingai.com "分組查詢注意力", 技術原理: heads regrouped [K, G].
 //
 // Work decomposition: one 256-thread workgroup per (sequence b, KV head k,
-// block of 16 query positions, chunk of up to 8 heads of the group).  Each of
-// the 4 wavefronts owns two (head, 16 positions) row tiles, so one workgroup
-// covers 8 heads x 16 positions = 128 rows that all read the same K/V tiles.
+// span of query positions, chunk of heads of the group).  Each of the 4
+// wavefronts owns two (head, 16 positions) row tiles, so one workgroup
+// covers 128 rows that all read the same K/V tiles: 8 heads x 16 positions
+// when the group has 8 or more heads, else hpw heads (G rounded up to a
+// power of two) x 8/hpw blocks of 16 positions, so that small groups (G =
+// 4 in Llama-3-8B, G = 1 in MHA) still fill every row tile.
 // The key loop walks 64-key tiles of [0, q0 + 16), copied from global memory
 // straight into LDS (global_load_lds_dwordx4: lane i of a wavefront lands
 // its 16 bytes at LDS base + 16 i, with no register staging).  Rows are kept
@@ -24,7 +36,7 @@
 // The tiles are double-buffered: the copies of tile j+1 are in flight while
 // tile j is multiplied, and one barrier per tile orders the buffers.
 // Per tile and row tile: S^T[64 x 16] = K_tile . Q^T (v_mfma_f32_16x16x32_bf16),
-// causal mask on the diagonal tile only, base-2 online softmax in fp32 with
+// mask only on the diagonal (or last) tile, base-2 online softmax in fp32 with
 // lazy rescaling, O[16 x D] += P[16 x 64] . V_tile, where the score layout of
 // the first product is used directly as the P operand of the second, and the
 // softmax denominators come from the same product against a block of ones.
@@ -51,10 +63,11 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
+template <int D, bool OUT_BF16, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kg, const __bf16* __restrict__ vg,
-    void* __restrict__ out, int H, int K, int S, int S_max, int head_chunks, float scale_log2) {
+    void* __restrict__ out, const int32_t* __restrict__ kv_lens, int H, int K, int S, int S_kv,
+    int S_max, int head_chunks, int hpw_log2, float scale_log2) {
   constexpr int KSTEPS = D / 32;
   constexpr int DT = D / 16;
   constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -63,9 +76,13 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [stage][K|V]
 
-  const int nqb = (S + kBQ - 1) / kBQ;
+  // the 8 row tiles of a workgroup: hpw heads x (8 / hpw) blocks of 16
+  // positions (hpw = 8 unless the group has fewer heads)
+  const int hpw = 1 << hpw_log2;
+  const int qspan = kBQ * (8 >> hpw_log2);  // query positions per workgroup
+  const int nqb = (S + qspan - 1) / qspan;
   const int qb = nqb - 1 - (int)blockIdx.x;
-  const int q0 = qb * kBQ;
+  const int q0 = qb * qspan;
   const int k = blockIdx.y / head_chunks;
   const int hc = blockIdx.y - k * head_chunks;
   const int b = blockIdx.z;
@@ -77,18 +94,29 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
   const int n = lane & 15;
   const int g = lane >> 4;
 
-  int hglob[2];
+  const int L = kv_lens ? kv_lens[b] : S_kv;  // keys of this sequence
+  const int q_off = CAUSAL ? L - S : 0;        // absolute position of query 0
+  // Row tile j of this wave: head hglob[j], positions rq0[j] .. +15; this
+  // lane's score column is position rq0[j] + n, which sees keys [0, lim[j]).
+  // The workgroup needs keys [0, kend); keys >= mask_from are hidden from
+  // some of its rows.
+  int hglob[2], rq0[2], lim[2];
   bool hok[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int hl = hc * kHeadsWG + 2 * wave + j;
+    const int r = 2 * wave + j;
+    const int hl = hc * hpw + (r & (hpw - 1));
     hok[j] = hl < G;
     hglob[j] = k * G + (hok[j] ? hl : 0);
+    rq0[j] = q0 + kBQ * (r >> hpw_log2);
+    lim[j] = CAUSAL ? min(q_off + rq0[j] + n + 1, L) : L;
   }
-  const int pos_n = q0 + n;  // query position of this lane's score column
+  const int kend = CAUSAL ? min(q_off + q0 + qspan, L) : L;
+  const int mask_from = CAUSAL ? min(q_off + q0 + 1, L) : L;
   bf16x8 qf[2][KSTEPS];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    const int pos_n = rq0[j] + n;
     const bool ld = hok[j] && pos_n < S;
     const __bf16* qrow = q + (((size_t)b * H + hglob[j]) * S + (ld ? pos_n : 0)) * D;
 #pragma unroll
@@ -113,8 +141,7 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
   const size_t kv_base = ((size_t)b * K + k) * (size_t)S_max * D;
   const __bf16* kbase = kg + kv_base;
   const __bf16* vbase = vg + kv_base;
-  const int kend = min(q0 + kBQ, S);
-  const int ntiles = (kend + kBN - 1) / kBN;
+  const int ntiles = kend > 0 ? (kend + kBN - 1) / kBN : 0;
   const bool any_head = hok[0];
 
   // LDS layout of a staged tile: whole rows of D bf16, their 16-byte chunks
@@ -125,8 +152,7 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
   // Copy ii of a tensor fills LDS chunks [64 ii, 64 ii + 64); lane l's chunk
   // is row (64 ii + l) / CPR, physical chunk l % CPR, so the lane fetches the
   // global chunk that belongs there.  Rows past the last key are fetched from
-  // the last key instead (finite values; the causal mask gives them zero
-  // weight).
+  // the last key instead (finite values; the mask gives them zero weight).
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   int crow[COPIES], koff[COPIES], voff[COPIES];
 #pragma unroll
@@ -197,14 +223,14 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
           st[jj][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[jj][s2], st[jj][mt], 0, 0, 0);
       }
     }
-    if (kb0 + kBN > q0) {  // diagonal tile: drop keys after the row's position
+    if (kb0 + kBN > mask_from) {  // diagonal / last tile: drop keys >= the row's limit
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (kb0 + 16 * mt + 4 * g + i > pos_n) st[jj][mt][i] = -INFINITY;
+            if (kb0 + 16 * mt + 4 * g + i >= lim[jj]) st[jj][mt][i] = -INFINITY;
     }
 
     // ---- online softmax per row tile ----
@@ -233,7 +259,8 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
           for (int t = 0; t < DT; ++t) acc[jj][t][i] *= a;
         }
       }
-      const float mneg = -m_run[jj];
+      // a row that has seen no visible key yet keeps all weights at zero
+      const float mneg = m_run[jj] == -INFINITY ? 0.f : -m_run[jj];
       uint32_t pw[8];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -266,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  copy_tile(0, S0{});
+  if (ntiles > 0) copy_tile(0, S0{});
   // Tiles alternate between the two LDS stages; the loop is unrolled by two
   // so each stage's addresses are compile-time offsets.
   for (int j = 0; j < ntiles; j += 2) {
@@ -288,9 +315,9 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
     if (!hok[jj]) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pos = q0 + 4 * g + i;
+      const int pos = rq0[jj] + 4 * g + i;
       if (pos >= S) continue;
-      const float inv = 1.f / lsum[jj][i];
+      const float inv = lsum[jj][i] > 0.f ? 1.f / lsum[jj][i] : 0.f;  // no visible key: zero row
       const size_t orow = (((size_t)b * H + hglob[jj]) * S + pos) * D;
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
@@ -306,24 +333,33 @@ __global__ __launch_bounds__(256, 2) void prefill_causal_kernel(
 
 }  // namespace
 
-hipError_t launch_prefill_causal_bf16(const void* q, const void* k, const void* v, void* out,
-                                      int B, int H, int K, int S, int S_max, int d,
-                                      float scale_log2, bool out_bf16, hipStream_t stream) {
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out,
+                               const int32_t* kv_lens, int B, int H, int K, int S, int S_kv,
+                               int S_max, int d, float scale_log2, bool out_bf16, bool causal,
+                               hipStream_t stream) {
   const int G = H / K;
-  const int head_chunks = (G + kHeadsWG - 1) / kHeadsWG;
-  const dim3 grid((S + kBQ - 1) / kBQ, K * head_chunks, B);
+  // heads per workgroup: the group's heads rounded up to a power of two (at
+  // most 8); the remaining row tiles take further blocks of positions
+  int hpw_log2 = 0;
+  while ((1 << hpw_log2) < G && (1 << hpw_log2) < kHeadsWG) ++hpw_log2;
+  const int head_chunks = (G + (1 << hpw_log2) - 1) >> hpw_log2;
+  const int qspan = kBQ * (kHeadsWG >> hpw_log2);
+  const dim3 grid((S + qspan - 1) / qspan, K * head_chunks, B);
   const dim3 block(256);
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<const __bf16*>(k);
   auto vp = static_cast<const __bf16*>(v);
-#define GQA_PREFILL(DD, OB)                                                                     \
-  hipLaunchKernelGGL((prefill_causal_kernel<DD, OB>), grid, block, 0, stream, qp, kp, vp, out, \
-                     H, K, S, S_max, head_chunks, scale_log2)
+#define GQA_PREFILL(DD, OB, CA)                                                                 \
+  hipLaunchKernelGGL((prefill_kernel<DD, OB, CA>), grid, block, 0, stream, qp, kp, vp, out,      \
+                     kv_lens, H, K, S, S_kv, S_max, head_chunks, hpw_log2, scale_log2)
+#define GQA_PREFILL_C(DD, OB)                                                                   \
+  if (causal) GQA_PREFILL(DD, OB, true); else GQA_PREFILL(DD, OB, false);
   if (d == 128) {
-    if (out_bf16) GQA_PREFILL(128, true); else GQA_PREFILL(128, false);
+    if (out_bf16) { GQA_PREFILL_C(128, true) } else { GQA_PREFILL_C(128, false) }
   } else {
-    if (out_bf16) GQA_PREFILL(64, true); else GQA_PREFILL(64, false);
+    if (out_bf16) { GQA_PREFILL_C(64, true) } else { GQA_PREFILL_C(64, false) }
   }
+#undef GQA_PREFILL_C
 #undef GQA_PREFILL
   return hipGetLastError();
 }

@@ -34,7 +34,7 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str               # "decode" or "prefill"
+    kind: str               # "decode", "prefill", "chunk" or "cross"
     B: int
     H: int
     K: int
@@ -69,6 +69,13 @@ WORKLOADS = {
         "decode_int8_llama3_8b", "decode", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
         append=True, note="decode_llama3_8b with the cache quantised to int8 (one fp32 scale per row)",
         extra={"kv_dtype": "int8"}),
+    "prefill_chunk_8k": Workload(
+        "prefill_chunk_8k", "chunk", B=2, H=64, K=8, d=128, dtype="bf16", L=8192,
+        note="a 2048-token chunk continuing a 6144-row cache (queries at positions 6144..8191)",
+        extra={"chunk": 2048}),
+    "cross_attention_4k": Workload(
+        "cross_attention_4k", "cross", B=4, H=32, K=8, d=128, dtype="bf16", L=4096,
+        note="1024 decoder queries over 4096 encoder rows, no mask", extra={"S_q": 1024}),
     "prefill_causal_4k": Workload(
         "prefill_causal_4k", "prefill", B=2, H=64, K=8, d=128, dtype="bf16", L=4096,
         note="causal prefill, S=4096, 64 query heads over 8 KV heads"),
@@ -135,6 +142,34 @@ def prefill_inputs(B: int, H: int, K: int, S: int, d: int, dtype: str, seed: int
     return {"q": q, "k": k, "v": v, "S_max": smax, "seed": int(seed)}
 
 
+def attention_inputs(B: int, H: int, K: int, S_q: int, d: int, dtype: str, seed: int = 0,
+                     kv_lens=None, s_max: int | None = None, rows_new: int = 0) -> dict:
+    """Draw queries [B, H, S_q, d] and K/V caches [B, K, S_max, d] holding
+    kv_lens[b] rows each (rows past them NaN), for chunked prefill and
+    cross-attention; with rows_new > 0 also k_new, v_new [B, K, rows_new, d]
+    (a chunk to append).  Draw order: q, then k rows, v rows (sequence by
+    sequence), then k_new, v_new."""
+    dt = _DT[dtype]
+    lens = [int(x) for x in kv_lens]
+    if len(lens) != B:
+        raise ValueError("kv_lens must have B entries")
+    smax = max(lens) + rows_new if s_max is None else int(s_max)
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    q = torch.randn((B, H, S_q, d), generator=g).to(dt)
+    k = torch.full((B, K, smax, d), float("nan"), dtype=dt)
+    v = torch.full((B, K, smax, d), float("nan"), dtype=dt)
+    for b, L in enumerate(lens):
+        k[b, :, :L] = torch.randn((K, L, d), generator=g).to(dt)
+    for b, L in enumerate(lens):
+        v[b, :, :L] = torch.randn((K, L, d), generator=g).to(dt)
+    out = {"q": q, "k": k, "v": v, "kv_lens": torch.tensor(lens, dtype=torch.int32), "S_max": smax,
+           "seed": int(seed)}
+    if rows_new:
+        out["k_new"] = torch.randn((B, K, rows_new, d), generator=g).to(dt)
+        out["v_new"] = torch.randn((B, K, rows_new, d), generator=g).to(dt)
+    return out
+
+
 def meanpool_inputs(outer: int, H: int, inner: int, dtype: str, seed: int = 0) -> torch.Tensor:
     """Draw a [outer, H, inner] weight-like tensor (CPU)."""
     g = torch.Generator(device="cpu").manual_seed(int(seed))
@@ -178,6 +213,14 @@ def workload_inputs(w: Workload, seed: int = 0, s_max: int | None = None) -> dic
     """Inputs of a named workload."""
     if w.kind == "prefill":
         return prefill_inputs(w.B, w.H, w.K, w.L, w.d, w.dtype, seed=seed, s_max=s_max)
+    if w.kind == "chunk":
+        # the cache before the chunk, plus the chunk's rows to append
+        T = w.extra["chunk"]
+        return attention_inputs(w.B, w.H, w.K, T, w.d, w.dtype, seed=seed, kv_lens=[w.L - T] * w.B,
+                                s_max=s_max or w.L, rows_new=T)
+    if w.kind == "cross":
+        return attention_inputs(w.B, w.H, w.K, w.extra["S_q"], w.d, w.dtype, seed=seed,
+                                kv_lens=[w.L] * w.B, s_max=s_max)
     if w.ragged is not None:
         return decode_inputs(w.B, w.H, w.K, w.d, w.dtype, seed=seed, ragged=w.ragged,
                              q_scale=w.q_scale, s_max=s_max)

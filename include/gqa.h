@@ -238,6 +238,47 @@ int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
                        int dtype, int out_dtype, void* stream);
 
 /*
+ * Prefill of a chunk over a cache: q, out [B, H, S, d]; the caches
+ * [B, K, S_max, d] already hold the chunk's K/V rows as their last S rows,
+ * L_b = seq_lens[b] rows in all (device int32 [B]).  Query i of sequence b
+ * sits at position L_b - S + i and attends causally:
+ *   out[b, h, i, :] = sum_{j <= L_b - S + i} softmax_j(scale q . k_j) v_j.
+ * (pinghaoyang.com.cn "GQA 完全拆解", decode memory ledger: the query at
+ * position t attends to cached rows 1..t; prefill computes a run of
+ * positions at once -- a chunk is such a run continuing a cache.)
+ * gqa_prefill_causal is the case L_b = S.  Device-side contract:
+ * S <= seq_lens[b] <= S_max (a query with no visible row gets zeros).
+ * dtype GQA_BF16; out_dtype GQA_BF16 or GQA_F32; scale finite and > 0.
+ */
+int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* seq_lens, void* out, int B, int H, int K, int S, int S_max,
+                      int d, float scale, int dtype, int out_dtype, void* stream);
+
+/*
+ * Non-causal GQA attention (cross-attention): q, out [B, H, S_q, d] over rows
+ * [0, L_b) of k, v [B, K, S_max, d], L_b = kv_lens[b] (device int32 [B],
+ * 0 <= L_b <= S_max):
+ *   out[b, h, i, :] = sum_{j < L_b} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
+ * and zeros when L_b = 0.  (pinghaoyang.com.cn "GQA 完全拆解", GQA section:
+ * grouped KV heads are used in decoder self-attention and in
+ * cross-attention, not in encoder self-attention.)  Types as prefill.
+ */
+int gqa_cross_attention(const void* q, const void* k, const void* v, const int32_t* kv_lens,
+                        void* out, int B, int H, int K, int S_q, int S_max, int d, float scale,
+                        int dtype, int out_dtype, void* stream);
+
+/*
+ * Append T rows per sequence: for every b with L = seq_lens[b] and
+ * L + T <= S_max, k_cache[b, k, L + t, :] = k_new[b, k, t, :] (and v) for
+ * t < T and every k, then seq_lens[b] = L + T; a sequence without room for
+ * all T rows is left untouched.  k_new, v_new [B, K, T, d]; bit-exact copy;
+ * dtype GQA_F32 or GQA_BF16.  Two kernel launches (copy, then lengths).
+ */
+int gqa_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                       int32_t* seq_lens, int B, int K, int T, int S_max, int d, int dtype,
+                       void* stream);
+
+/*
  * Mean-pool conversion of per-head weights into group weights:
  *   dst[o, g, i] = (sum_{r < G} src[o, g*G + r, i]) / G
  * with src [outer, H, inner] and dst [outer, K, inner], both of `dtype`.

@@ -32,6 +32,9 @@ CASES = [
     (1, 16, 1, 130, 128, 130),   # G = 16: two head chunks
     (2, 4, 4, 33, 64, 40),       # K = H (MHA)
     (1, 8, 8, 1, 128, 1),        # one position
+    (1, 10, 5, 150, 128, 150),   # G = 2: four 16-position blocks per workgroup
+    (2, 10, 2, 90, 64, 96),      # G = 5: three idle row tiles
+    (1, 4, 4, 300, 128, 300),    # G = 1 (MHA): eight blocks per workgroup, S not a multiple of 128
 ]
 
 
