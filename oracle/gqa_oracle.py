@@ -451,3 +451,36 @@ def kv_append_rows_ref(k_new, v_new, k_cache, v_cache, seq_lens):
         vc[b, :, L:L + T, :] = v_new[b]
         sl[b] = L + T
     return kc, vc, sl
+
+
+# --------------------------------------------------------------------------
+# Fused K/V projection and append
+# --------------------------------------------------------------------------
+# [PHY] engineering section: GQA's W_K and W_V are [G, d_k, d_model] (G KV
+# heads in that page's notation); inference frameworks merge them into one
+# W_KV of shape [G, 2 d_k, d_model] so that a single GEMM yields both K and
+# V.  Reading: for head k, rows [0, d) of W_KV[k] are W_K[k] and rows
+# [d, 2d) are W_V[k]; a token's hidden state x (length d_model) gives
+# K_k = W_KV[k, :d] x and V_k = W_KV[k, d:] x, which are appended to the
+# cache (no bias; positional rotation, which the same section leaves to the
+# unchanged rest of the model, is not part of this step).
+
+
+def kv_project_ref(x, w_kv):
+    """K and V rows of T tokens per sequence: x [B, T, d_model], w_kv
+    [K, 2d, d_model] -> (k_rows, v_rows), each [B, K, T, d] float64."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w_kv, dtype=np.float64)
+    K, d2, dm = w.shape
+    d = d2 // 2
+    y = np.einsum("btm,kjm->bktj", x, w)                 # [B, K, T, 2d]
+    return y[..., :d], y[..., d:]
+
+
+def kv_project_append_ref(x, w_kv, k_cache, v_cache, seq_lens):
+    """Project the T new tokens of every sequence and append their K/V rows
+    at positions [L_b, L_b + T) (float64 caches returned, with the new
+    lengths); a sequence without room for T rows is left unchanged."""
+    kr, vr = kv_project_ref(x, w_kv)
+    return kv_append_rows_ref(kr, vr, np.asarray(k_cache, dtype=np.float64),
+                              np.asarray(v_cache, dtype=np.float64), seq_lens)

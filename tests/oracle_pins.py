@@ -613,6 +613,53 @@ def check_append_rows(O):
     assert np.array_equal(k2[2], kc[2]) and np.array_equal(v2[2], vc[2])
 
 
+# --------------------------------------------------------------------------
+# fused K/V projection
+# --------------------------------------------------------------------------
+def check_project_identity_weights(O):
+    """d_model = d, W_K = I and W_V = 2 I for every head: K rows are the
+    tokens themselves and V rows twice them."""
+    r = _rng(3100)
+    B, T, K, d = 2, 3, 4, 8
+    x = r.standard_normal((B, T, d))
+    w = np.concatenate([np.broadcast_to(np.eye(d), (K, d, d)), np.broadcast_to(2 * np.eye(d), (K, d, d))], axis=1)
+    kr, vr = O.kv_project_ref(x, w)
+    for k in range(K):
+        assert np.array_equal(kr[:, k], x) and np.array_equal(vr[:, k], 2 * x)
+
+
+def check_project_linear_library(O):
+    """torch.nn.functional.linear (fp64) on W_KV flattened to [K * 2d, d_model]."""
+    r = _rng(3200)
+    B, T, K, d, dm = 2, 5, 3, 4, 16
+    x = r.standard_normal((B, T, dm))
+    w = r.standard_normal((K, 2 * d, dm))
+    y = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(w.reshape(K * 2 * d, dm))).numpy()
+    y = y.reshape(B, T, K, 2 * d).transpose(0, 2, 1, 3)          # [B, K, T, 2d]
+    kr, vr = O.kv_project_ref(x, w)
+    _close(kr, y[..., :d], 1e-12, "K rows")
+    _close(vr, y[..., d:], 1e-12, "V rows")
+
+
+def check_project_append(O):
+    r = _rng(3300)
+    B, T, K, d, dm, S = 3, 2, 2, 4, 8, 6
+    x = r.standard_normal((B, T, dm))
+    w = r.standard_normal((K, 2 * d, dm))
+    kc = r.standard_normal((B, K, S, d))
+    vc = r.standard_normal((B, K, S, d))
+    sl = np.array([0, 3, 5])                      # the last has no room for two rows
+    k2, v2, s2 = O.kv_project_append_ref(x, w, kc, vc, sl)
+    assert list(s2) == [2, 5, 5]
+    for b, L in enumerate([0, 3]):
+        for t in range(T):
+            for k in range(K):
+                _close(k2[b, k, L + t], w[k, :d] @ x[b, t], 1e-12, "appended K")
+                _close(v2[b, k, L + t], w[k, d:] @ x[b, t], 1e-12, "appended V")
+    assert np.array_equal(k2[2], kc[2]) and np.array_equal(v2[2], vc[2])
+    assert np.array_equal(k2[1, :, :3], kc[1, :, :3])
+
+
 ALL_CHECKS = [
     check_kv_bytes_golden, check_kv_head_map,
     check_bruteforce_decode, check_bruteforce_prefill, check_bruteforce_meanpool,
@@ -628,4 +675,5 @@ ALL_CHECKS = [
     check_int8_halves_cache, check_int8_decode_composition, check_int8_append,
     check_chunk_equals_causal_rows, check_chunk_single_token_is_decode, check_cross_attention_sdpa,
     check_cross_rows_are_decodes, check_append_rows,
+    check_project_identity_weights, check_project_linear_library, check_project_append,
 ]

@@ -93,6 +93,10 @@ MUTATIONS = {
     "append_rows_partial": [("        if L + T > S_max:\n            continue\n        kc[b, :, L:L + T, :] = k_new[b]",
                              "        if L >= S_max:\n            continue\n        T2 = min(T, S_max - L)\n        kc[b, :, L:L + T2, :] = k_new[b, :, :T2]")],
     "append_rows_no_increment": [("        sl[b] = L + T\n", "        sl[b] = L + 1\n")],
+    "project_k_v_swapped": [("    return y[..., :d], y[..., d:]", "    return y[..., d:], y[..., :d]")],
+    "project_transposed_weight": [('y = np.einsum("btm,kjm->bktj", x, w)', 'y = np.einsum("btm,kjm->bktj", x, w[:, ::-1, :])')],
+    "project_heads_interleaved": [('y = np.einsum("btm,kjm->bktj", x, w)',
+                                   'y = np.einsum("btm,kjm->bktj", x, w.reshape(2, K, d, dm).transpose(1, 0, 2, 3).reshape(K, 2 * d, dm))')],
     "empty_length_nan": [("        if L == 0:\n            continue\n        for k in range(K):",
                           "        for k in range(K):")],
 }
