@@ -410,6 +410,89 @@ def bench_prefill(args, w):
     return res, inp
 
 
+def bench_project(args, w):
+    """Fused K/V projection + append of one decode token per sequence: HBM
+    bound on reading W_KV once per step."""
+    import grouped_query_kv_amd as gqa
+    from grouped_query_kv_amd.inputs import projection_inputs
+
+    dev = torch.device("cuda:0")
+    dm, T = w.extra["d_model"], w.extra["T"]
+    t_gen = time.perf_counter()
+    inp = projection_inputs(w.B, T, dm, w.K, w.d, seed=args.seed)
+    t_gen = time.perf_counter() - t_gen
+    x = inp["x"].to(dev)
+    # one W_KV per layer of a 32-layer model (537 MB in all, beyond the 256 MB
+    # Infinity Cache), visited in turn, so every step reads its W_KV from HBM
+    layers = 32
+    wkvs = [inp["w_kv"].to(dev) for _ in range(layers)]
+    S_max = w.L + T
+    kc = torch.zeros((w.B, w.K, S_max, w.d), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    lens0 = torch.full((w.B,), w.L, dtype=torch.int32, device=dev)
+    lens = lens0.clone()
+    ws = torch.empty(gqa.gqa_kv_project_workspace_bytes(w.B, T, dm, w.K, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        lens.copy_(lens0)              # every step writes the same position
+        if ev is not None:
+            gqa.gqa_set_timing_events(*ev)
+        gqa.gqa_kv_project_append(x, wkvs[i % layers], kc, vc, lens, ws, stream=stream)
+        if ev is not None:
+            gqa.gqa_set_timing_events(None, None)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [(gqa.HipEvent(), gqa.HipEvent()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, ev in enumerate(events):
+        step(args.warmup + i, ev)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_ms = float(np.mean([a.elapsed_ms(b) for a, b in events]))
+    byts = wkvs[0].numel() * 2 + x.numel() * 2 + 2 * w.B * T * w.K * w.d * 2   # W_KV + x read, K/V rows written
+    ms_per_step = elapsed * 1e3 / args.steps
+    res = {
+        "metric": "GQA fused K/V projection + append GB/s (W_KV streamed once per step), 1xMI355X",
+        "value": round(byts / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": T, "d_model": dm, "K": w.K, "d": w.d,
+                   "w_kv_copies": layers, "parallelism": "single GPU"},
+        "tokens_per_s": round(w.B * T / (ms_per_step * 1e-3), 1),
+        "roofline": {"kernel": "K/V projection (kv_project_kernel)",
+                     "bound": "hbm",
+                     "achieved": round(byts / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(byts / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_kernel_us": round(kern_ms * 1e3, 3)},
+        "input_gen_s": round(t_gen, 1),
+    }
+    return res, inp
+
+
+def cpu_baseline_project(inp, w, budget_s):
+    """The oracle's projection of whole steps (all tokens, all heads), one
+    BLAS thread, repeated for about `budget_s` seconds."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kv_project_ref
+
+    x = inp["x"].float().numpy()
+    wk = inp["w_kv"].float().numpy()
+    byts = wk.size * 2 + x.size * 2 + 2 * x.shape[0] * x.shape[1] * wk.shape[0] * (wk.shape[1] // 2) * 2
+    steps, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s:
+            t0 = time.perf_counter()
+            kv_project_ref(x, wk)
+            t_used += time.perf_counter() - t0
+            steps += 1
+    return {"value": steps * byts / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} whole projection steps, {t_used:.1f} s of fp64 NumPy on 1 thread"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -419,7 +502,11 @@ def main():
     from grouped_query_kv_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    if w.kind in ("prefill", "chunk", "cross"):
+    if w.kind == "project":
+        res, inp = bench_project(args, w)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_project(inp, w, args.cpu_seconds)
+    elif w.kind in ("prefill", "chunk", "cross"):
         res, inp = bench_prefill(args, w)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline_prefill(inp, w, args.cpu_seconds)

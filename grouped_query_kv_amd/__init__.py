@@ -24,6 +24,9 @@ from ._binding import (  # noqa: F401
     gqa_kv_append_rows,
     gqa_kv_quantize_int8,
     gqa_kv_cache_bytes,
+    gqa_kv_project,
+    gqa_kv_project_append,
+    gqa_kv_project_workspace_bytes,
     gqa_last_error,
     gqa_meanpool_convert,
     gqa_prefill_causal,

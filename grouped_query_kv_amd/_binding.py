@@ -46,6 +46,9 @@ _SIGNATURES = {
     "gqa_prefill_chunk": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_cross_attention": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_kv_append_rows": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_void_p]),
+    "gqa_kv_project": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_void_p]),
+    "gqa_kv_project_workspace_bytes": (_c_size_t, [_c_int] * 5),
+    "gqa_kv_project_append": (_c_int, [_c_void_p] * 6 + [_c_size_t] + [_c_int] * 7 + [_c_void_p]),
     "gqa_prefill_causal": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_meanpool_convert": (_c_int, [_c_void_p, _c_void_p, _c_int64, _c_int, _c_int, _c_int64, _c_int, _c_void_p]),
 }
@@ -467,6 +470,46 @@ def gqa_kv_append_rows(k_new, v_new, k_cache, v_cache, seq_lens, stream=None) ->
     _check("gqa_kv_append_rows", load_library().gqa_kv_append_rows(
         k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
         B, K, T, S_max, d, _DTYPE_CODE[k_cache.dtype], _stream(stream)))
+
+
+def gqa_kv_project(x, w_kv, k_out, v_out, stream=None) -> None:
+    """Project x [B,T,d_model] by W_KV [K,2d,d_model] into K and V rows
+    k_out, v_out [B,K,T,d] (bf16)."""
+    _need(x, "x", 3, (torch.bfloat16,))
+    _need(w_kv, "w_kv", 3, (torch.bfloat16,))
+    _need(k_out, "k_out", 4, (torch.bfloat16,))
+    _need(v_out, "v_out", 4, (torch.bfloat16,))
+    B, T, dm = x.shape
+    K, d2, dmw = w_kv.shape
+    d = d2 // 2
+    if dmw != dm or tuple(k_out.shape) != (B, K, T, d) or v_out.shape != k_out.shape:
+        raise ValueError("shape mismatch between x, w_kv and the outputs")
+    _check("gqa_kv_project", load_library().gqa_kv_project(
+        x.data_ptr(), w_kv.data_ptr(), k_out.data_ptr(), v_out.data_ptr(), B, T, dm, K, d, GQA_BF16,
+        _stream(stream)))
+
+
+def gqa_kv_project_workspace_bytes(B: int, T: int, d_model: int, K: int, d: int) -> int:
+    return int(load_library().gqa_kv_project_workspace_bytes(B, T, d_model, K, d))
+
+
+def gqa_kv_project_append(x, w_kv, k_cache, v_cache, seq_lens, workspace, stream=None) -> None:
+    """Project x [B,T,d_model] by W_KV [K,2d,d_model] and append the K/V rows
+    at seq_lens[b] of the caches [B,K,S_max,d]; add T to seq_lens.
+    workspace: uint8 GPU tensor of gqa_kv_project_workspace_bytes(...) bytes."""
+    _need(x, "x", 3, (torch.bfloat16,))
+    _need(w_kv, "w_kv", 3, (torch.bfloat16,))
+    _need(k_cache, "k_cache", 4, (torch.bfloat16,))
+    _need(v_cache, "v_cache", 4, (torch.bfloat16,))
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    B, T, dm = x.shape
+    Bk, K, S_max, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or Bk != B or tuple(w_kv.shape) != (K, 2 * d, dm) or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between x, w_kv, caches and seq_lens")
+    _need(workspace, "workspace", 1, (torch.uint8,))
+    _check("gqa_kv_project_append", load_library().gqa_kv_project_append(
+        x.data_ptr(), w_kv.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), B, T, dm, K, S_max, d, GQA_BF16, _stream(stream)))
 
 
 def gqa_meanpool_convert(src, dst, stream=None) -> None:

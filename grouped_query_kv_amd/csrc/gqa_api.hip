@@ -457,6 +457,68 @@ int gqa_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void
   return r ? r : ok();
 }
 
+static int validate_project(const char* fn, int B, int T, int d_model, int K, int d, int dtype) {
+  if (B < 1 || T < 1 || K < 1 || d_model < 1) return fail(GQA_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (d != 64 && d != 128) return fail(GQA_ERR_UNSUPPORTED, "%s: d=%d (64 or 128)", fn, d);
+  if (d_model % 32 != 0) return fail(GQA_ERR_UNSUPPORTED, "%s: d_model=%d (a multiple of 32)", fn, d_model);
+  if (dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: bf16 only (matrix-core path)", fn);
+  if ((long long)B * T > (1LL << 24) || (long long)B * T * K * d > (1LL << 30))
+    return fail(GQA_ERR_INVALID, "%s: too many tokens", fn);
+  return GQA_OK;
+}
+
+int gqa_kv_project(const void* x, const void* w_kv, void* k_out, void* v_out, int B, int T, int d_model,
+                   int K, int d, int dtype, void* stream) {
+  const char* fn = "gqa_kv_project";
+  if (!x || !w_kv || !k_out || !v_out) return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (int r = validate_project(fn, B, T, d_model, K, d, dtype)) return r;
+  if (!aligned16(x) || !aligned16(w_kv) || (reinterpret_cast<uintptr_t>(k_out) & 1u) ||
+      (reinterpret_cast<uintptr_t>(v_out) & 1u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r;
+  {
+    TimedRegion timed(s);
+    r = check_hip(gqa::launch_kv_project(x, w_kv, k_out, v_out, B, T, d_model, K, d, s), "projection launch");
+  }
+  return r ? r : ok();
+}
+
+size_t gqa_kv_project_workspace_bytes(int B, int T, int d_model, int K, int d) {
+  if (B < 1 || T < 1 || K < 1 || d_model < 32 || d_model % 32 || (d != 64 && d != 128) ||
+      (long long)B * T > (1LL << 24) || (long long)B * T * K * d > (1LL << 30))
+    return 0;
+  return 2 * (size_t)B * T * K * d * 2;  // the K and V rows, bf16
+}
+
+int gqa_kv_project_append(const void* x, const void* w_kv, void* k_cache, void* v_cache,
+                          int32_t* seq_lens, void* workspace, size_t workspace_bytes, int B, int T,
+                          int d_model, int K, int S_max, int d, int dtype, void* stream) {
+  const char* fn = "gqa_kv_project_append";
+  if (!x || !w_kv || !k_cache || !v_cache || !seq_lens) return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
+  if (S_max < 1) return fail(GQA_ERR_INVALID, "%s: sizes must be >= 1", fn);
+  if (int r = validate_project(fn, B, T, d_model, K, d, dtype)) return r;
+  if (!aligned16(x) || !aligned16(w_kv) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
+  const size_t rows_bytes = (size_t)B * T * K * d * 2;
+  if (!workspace || workspace_bytes < 2 * rows_bytes || !aligned16(workspace))
+    return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
+                2 * rows_bytes, workspace ? workspace_bytes : (size_t)0);
+  char* k_rows = static_cast<char*>(workspace);
+  char* v_rows = k_rows + rows_bytes;  // rows_bytes is a multiple of 128
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r;
+  {
+    TimedRegion timed(s);
+    r = check_hip(gqa::launch_kv_project(x, w_kv, k_rows, v_rows, B, T, d_model, K, d, s), "projection launch");
+  }
+  if (r) return r;
+  r = check_hip(gqa::launch_kv_append_rows(k_rows, v_rows, k_cache, v_cache, seq_lens, B, K, T, S_max, d * 2, s),
+                "append launch");
+  return r ? r : ok();
+}
+
 int gqa_meanpool_convert(const void* src, void* dst, int64_t outer, int H, int K, int64_t inner,
                          int dtype, void* stream) {
   if (!src || !dst) return fail(GQA_ERR_INVALID, "gqa_meanpool_convert: null pointer");

@@ -99,6 +99,14 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                int S_max, int d, float scale_log2, bool out_bf16, bool causal,
                                hipStream_t stream);
 
+// seq_lens[b] += T where L + T <= S_max (run after the launch that wrote the rows).
+hipError_t launch_bump_lens(int32_t* seq_lens, int B, int T, int S_max, hipStream_t stream);
+
+// K/V projection of B*T tokens x [B, T, d_model] by W_KV [K, 2d, d_model]
+// (bf16) into rows k_out, v_out [B, K, T, d].
+hipError_t launch_kv_project(const void* x, const void* w_kv, void* k_out, void* v_out, int B, int T,
+                             int d_model, int K, int d, hipStream_t stream);
+
 // Append T rows per (sequence, KV head) at seq_lens[b] (two launches).
 hipError_t launch_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                  int32_t* seq_lens, int B, int K, int T, int S_max, int row_bytes,

@@ -67,10 +67,12 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_paged_kernel(
 
 // Multi-row variant: T rows per (sequence, KV head) go to positions
 // [L, L + T); a sequence without room for all T rows is left untouched.
+// With `publish` (one workgroup per sequence) the workgroup also writes the
+// new length after its barrier; otherwise a separate launch does.
 __global__ __launch_bounds__(kAppendThreads) void kv_append_rows_kernel(
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int32_t* __restrict__ seq_lens,
-    int K, int T, int S_max, int row_words) {
+    int K, int T, int S_max, int row_words, bool publish) {
   const int b = blockIdx.x;
   const int L = seq_lens[b];
   __syncthreads();
@@ -84,10 +86,11 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_rows_kernel(
       v_cache[dst0 + w] = v_new[src0 + w];
     }
   }
+  if (publish && threadIdx.x == 0) seq_lens[b] = L + T;
 }
 
-// Publishes the new lengths once every copy of kv_append_rows_kernel has read
-// the old ones (a separate launch orders the two).
+// Publishes the new lengths once every workgroup of the writing launch has
+// read the old ones (a separate launch orders the two).
 __global__ void bump_lens_kernel(int32_t* __restrict__ seq_lens, int B, int T, int S_max) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) {
@@ -101,13 +104,21 @@ __global__ void bump_lens_kernel(int32_t* __restrict__ seq_lens, int B, int T, i
 hipError_t launch_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                  int32_t* seq_lens, int B, int K, int T, int S_max, int row_bytes,
                                  hipStream_t stream) {
-  const int ky = K < 8 ? K : 8;
+  // a few rows per sequence (a decode step): one workgroup per sequence,
+  // which also publishes the length; else up to 8 per sequence and a
+  // separate length update
+  const long long words = (long long)K * T * (row_bytes / 16);
+  const int ky = words <= 8192 ? 1 : (K < 8 ? K : 8);
   hipLaunchKernelGGL(kv_append_rows_kernel, dim3(B, ky), dim3(kAppendThreads), 0, stream,
                      static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), seq_lens, K, T,
-                     S_max, row_bytes / 16);
+                     S_max, row_bytes / 16, ky == 1);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || ky == 1) return e;
+  return launch_bump_lens(seq_lens, B, T, S_max, stream);
+}
+
+hipError_t launch_bump_lens(int32_t* seq_lens, int B, int T, int S_max, hipStream_t stream) {
   hipLaunchKernelGGL(bump_lens_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, seq_lens, B, T,
                      S_max);
   return hipGetLastError();

@@ -34,7 +34,7 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str               # "decode", "prefill", "chunk" or "cross"
+    kind: str               # "decode", "prefill", "chunk", "cross" or "project"
     B: int
     H: int
     K: int
@@ -76,6 +76,10 @@ WORKLOADS = {
     "cross_attention_4k": Workload(
         "cross_attention_4k", "cross", B=4, H=32, K=8, d=128, dtype="bf16", L=4096,
         note="1024 decoder queries over 4096 encoder rows, no mask", extra={"S_q": 1024}),
+    "kv_project_llama3_8b": Workload(
+        "kv_project_llama3_8b", "project", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
+        note="fused K/V projection of one decode token per sequence, d_model 4096, appended at 8192",
+        extra={"d_model": 4096, "T": 1}),
     "prefill_causal_4k": Workload(
         "prefill_causal_4k", "prefill", B=2, H=64, K=8, d=128, dtype="bf16", L=4096,
         note="causal prefill, S=4096, 64 query heads over 8 KV heads"),
@@ -168,6 +172,16 @@ def attention_inputs(B: int, H: int, K: int, S_q: int, d: int, dtype: str, seed:
         out["k_new"] = torch.randn((B, K, rows_new, d), generator=g).to(dt)
         out["v_new"] = torch.randn((B, K, rows_new, d), generator=g).to(dt)
     return out
+
+
+def projection_inputs(B: int, T: int, d_model: int, K: int, d: int, seed: int = 0) -> dict:
+    """Hidden states x [B, T, d_model] ~ N(0, 1) and a merged K/V projection
+    W_KV [K, 2d, d_model] ~ N(0, 1/d_model) (so projected rows are O(1)),
+    both bf16.  Draw order: x, then W_KV."""
+    g = torch.Generator(device="cpu").manual_seed(int(seed))
+    x = torch.randn((B, T, d_model), generator=g).to(torch.bfloat16)
+    w = (torch.randn((K, 2 * d, d_model), generator=g) / d_model ** 0.5).to(torch.bfloat16)
+    return {"x": x, "w_kv": w, "seed": int(seed)}
 
 
 def meanpool_inputs(outer: int, H: int, inner: int, dtype: str, seed: int = 0) -> torch.Tensor:

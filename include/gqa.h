@@ -279,6 +279,38 @@ int gqa_kv_append_rows(const void* k_new, const void* v_new, void* k_cache, void
                        void* stream);
 
 /*
+ * Fused K/V projection.  x [B, T, d_model] holds the hidden states of T new
+ * tokens per sequence; w_kv [K, 2d, d_model] is the merged key/value
+ * projection (rows [0, d) of head k are W_K[k], rows [d, 2d) are W_V[k]):
+ *   k_out[b, k, t, :] = W_KV[k, 0:d, :] x[b, t, :],   v_out[b, k, t, :] = W_KV[k, d:2d, :] x[b, t, :]
+ * with fp32 accumulation rounded to bf16; k_out, v_out are [B, K, T, d], the
+ * layout gqa_kv_append_rows takes (and, for T = 1, the k_new / v_new of
+ * gqa_decode_append, which appends them inside the attention pass).
+ * (pinghaoyang.com.cn "GQA 完全拆解", section 工程实现 (engineering): W_K, W_V
+ * are [G, d_k, d_model] with G KV heads, and frameworks merge them into one
+ * W_KV [G, 2 d_k, d_model] so that one GEMM yields K and V.)  No bias and
+ * no positional rotation.  bf16 only; d_model a multiple of 32; d in
+ * {64, 128}; x and w_kv 16-byte aligned.  One kernel launch; each W_KV
+ * byte is read once per 16 tokens.
+ */
+int gqa_kv_project(const void* x, const void* w_kv, void* k_out, void* v_out, int B, int T,
+                   int d_model, int K, int d, int dtype, void* stream);
+
+/*
+ * gqa_kv_project followed by gqa_kv_append_rows: the projected rows are
+ * written at positions [L_b, L_b + T) of k_cache, v_cache [B, K, S_max, d]
+ * and seq_lens[b] += T (a sequence without room for T rows is left
+ * untouched).  workspace: device buffer of at least
+ * gqa_kv_project_workspace_bytes(B, T, d_model, K, d) bytes (the projected
+ * rows; content on entry does not matter).  Two kernel launches (three when
+ * a sequence's T rows exceed 8192 16-byte words).
+ */
+size_t gqa_kv_project_workspace_bytes(int B, int T, int d_model, int K, int d);
+int gqa_kv_project_append(const void* x, const void* w_kv, void* k_cache, void* v_cache,
+                          int32_t* seq_lens, void* workspace, size_t workspace_bytes, int B, int T,
+                          int d_model, int K, int S_max, int d, int dtype, void* stream);
+
+/*
  * Mean-pool conversion of per-head weights into group weights:
  *   dst[o, g, i] = (sum_{r < G} src[o, g*G + r, i]) / G
  * with src [outer, H, inner] and dst [outer, K, inner], both of `dtype`.

@@ -46,14 +46,18 @@ def guards_intact(buf: torch.Tensor, guard: int, dtype) -> bool:
     return bool(torch.isnan(head).all() and torch.isnan(tail).all())
 
 
+BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8-bit significand, round to nearest even)
+
+
 def bf16_bound(ref: np.ndarray, v_absmax: float, weights_in_denominator: bool = False) -> float:
     """Arithmetic error bound of a bf16 attention output.  Each softmax weight
-    is rounded to bf16 once (relative 2^-9) before multiplying V, and the
-    output is rounded once more (2^-9 |out|).  When the denominator also sums
-    the rounded weights (prefill) the weighted mean can move by up to twice
-    the weight error.  fp32 accumulation error is orders smaller."""
-    w = 2.0 ** -8 if weights_in_denominator else 2.0 ** -9
-    return w * v_absmax + 2.0 ** -9 * float(np.abs(ref).max()) + 1e-6
+    is rounded to bf16 once (relative error <= u = 2^-8) before multiplying V,
+    which moves the weighted sum by at most u * max|v|; the output is rounded
+    once more (u |out|).  When the denominator also sums the rounded weights
+    (prefill) the quotient can move by up to twice the weight error.  fp32
+    accumulation error is orders smaller."""
+    w = 2 * BF16_U if weights_in_denominator else BF16_U
+    return w * v_absmax + BF16_U * float(np.abs(ref).max()) + 1e-6
 
 
 def report(name: str, got: np.ndarray, ref: np.ndarray) -> dict:

@@ -29,6 +29,32 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), f"libgqa.so does not export {name}"
 
 
+def test_binding_signatures_match_header():
+    """Every declaration in include/gqa.h has a binding signature with the
+    same number of parameters and pointer/integer/float kinds."""
+    import re
+    text = B.HEADER.read_text()
+    decls = re.findall(r"^(?:int|size_t|uint64_t|const char\s*\*)\s*(gqa_\w+)\s*\(([^;()]*)\)\s*;", text,
+                       flags=re.M)
+    assert len(decls) == len(B._SIGNATURES), sorted(set(B._SIGNATURES) ^ {n for n, _ in decls})
+    for name, params in decls:
+        ps = [x.strip() for x in params.replace("\n", " ").split(",")]
+        ps = [] if ps == ["void"] else ps
+        argtypes = B._SIGNATURES[name][1]
+        assert len(ps) == len(argtypes), f"{name}: header {len(ps)} params, binding {len(argtypes)}"
+        for decl, at in zip(ps, argtypes):
+            if "*" in decl:
+                kind = ctypes.c_void_p
+            elif decl.startswith("float"):
+                kind = ctypes.c_float
+            elif decl.startswith(("int64_t", "uint64_t", "size_t")):
+                kind = (ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t)
+            else:
+                kind = ctypes.c_int
+            ok = at in kind if isinstance(kind, tuple) else at == kind
+            assert ok, f"{name}: parameter '{decl}' bound as {at}"
+
+
 def test_abi_version(lib):
     assert lib.gqa_abi_version() == 1
 
@@ -223,6 +249,75 @@ def test_quantize_int8_rejects(lib, args, code):
 ])
 def test_append_int8_rejects(lib, args, code):
     assert lib.gqa_kv_append_int8(*args, None) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, FAKE, 16, 1, 4096, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 16, 1, 100, 8, 128, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 16, 0, 4096, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE + 8, FAKE, FAKE, 16, 1, 4096, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE + 1, FAKE, 16, 1, 4096, 8, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+])
+def test_project_only_rejects(lib, args, code):
+    assert lib.gqa_kv_project(*args, None) == code
+
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 1, 4096, 8, 64, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 2, 1, 4096, 8, 64, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 0, 4096, 8, 64, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 1, 4004, 8, 64, 128, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 1, 4096, 8, 64, 96, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 1, 4096, 8, 64, 128, B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 1, 4096, 8, 64, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, 2, 1, 4096, 8, 64, 128, B.GQA_BF16), B.GQA_ERR_WORKSPACE),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, None, 1 << 30, 2, 1, 4096, 8, 64, 128, B.GQA_BF16), B.GQA_ERR_WORKSPACE),
+])
+def test_project_rejects(lib, args, code):
+    assert lib.gqa_kv_project_append(*args, None) == code
+    assert lib.gqa_last_error().decode().startswith("gqa_kv_project_append")
+
+
+def test_project_workspace_bytes(lib):
+    # the projected K and V rows, bf16
+    assert lib.gqa_kv_project_workspace_bytes(16, 1, 4096, 8, 128) == 2 * 16 * 8 * 128 * 2
+    assert lib.gqa_kv_project_workspace_bytes(2, 2048, 4096, 8, 128) == 2 * 2 * 2048 * 8 * 128 * 2
+    assert lib.gqa_kv_project_workspace_bytes(16, 1, 4004, 8, 128) == 0
+    assert lib.gqa_kv_project_workspace_bytes(16, 1, 4096, 8, 96) == 0
+
+
+@pytest.mark.parametrize("fn", ["gqa_prefill_chunk", "gqa_cross_attention"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=None), B.GQA_ERR_INVALID),
+    (dict(S=0), B.GQA_ERR_INVALID),
+    (dict(H=12, K=8), B.GQA_ERR_INVALID),
+    (dict(d=80), B.GQA_ERR_UNSUPPORTED),
+    (dict(dtype=B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), B.GQA_ERR_INVALID),
+    (dict(lens=FAKE + 2), B.GQA_ERR_INVALID),
+])
+def test_chunk_cross_reject(lib, fn, kw, code):
+    a = dict(lens=FAKE, S=64, H=32, K=8, d=128, dtype=B.GQA_BF16, scale=0.088)
+    a.update(kw)
+    f = getattr(lib, fn)
+    if fn == "gqa_prefill_chunk":
+        rc = f(FAKE, FAKE, FAKE, a["lens"], FAKE, 2, a["H"], a["K"], a["S"], 128, a["d"], a["scale"],
+               a["dtype"], B.GQA_BF16, None)
+    else:
+        rc = f(FAKE, FAKE, FAKE, a["lens"], FAKE, 2, a["H"], a["K"], a["S"], 128, a["d"], a["scale"],
+               a["dtype"], B.GQA_BF16, None)
+    assert rc == code and lib.gqa_last_error().decode().startswith(fn)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, FAKE, FAKE, 2, 8, 4, 64, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 0, 64, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 4, 64, 32, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE + 1, 2, 8, 4, 64, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
+])
+def test_append_rows_rejects(lib, args, code):
+    assert lib.gqa_kv_append_rows(*args, None) == code
 
 
 def test_timing_events_need_both(lib):

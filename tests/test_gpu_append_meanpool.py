@@ -63,7 +63,7 @@ def test_meanpool_vs_oracle(dtype, outer, H, K, inner):
     got = f64(dst)
     scale = float(np.abs(f64(src)).max())
     if dtype == "bf16":
-        # one rounding of the fp32 mean to bf16 (relative 2^-9) plus the fp32 sum
+        # one rounding of the fp32 mean to bf16 (relative u = 2^-8) plus the fp32 sum
         bound = np.abs(ref) * 2.0 ** -8 + 1e-6 * scale
     else:
         bound = np.full(ref.shape, 1e-6 * scale)
