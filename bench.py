@@ -259,7 +259,7 @@ def bench_decode(args, w):
     kern_avg_ms = float(np.mean(kern_ms))
     achieved = float(np.mean([step_bytes[j] for j in sampled])) / (kern_avg_ms * 1e-3) / 1e9
     res = {
-        "metric": "GQA decode KV-read GB/s (% of HBM peak) + attention tokens/s, 1xMI355X",
+        "metric": "GQA decode KV-read GB/s (% of HBM peak) + attention tokens/s, 1\u00d7MI355X",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -335,9 +335,9 @@ def cpu_baseline_prefill(inp, w, budget_s):
 
 
 PREFILL_METRIC = {
-    "prefill": "GQA causal prefill TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
-    "chunk": "GQA chunked prefill over a KV cache TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
-    "cross": "GQA cross-attention TFLOP/s (fraction of bf16 MFMA peak), 1xMI355X",
+    "prefill": "GQA causal prefill TFLOP/s (fraction of bf16 MFMA peak), 1\u00d7MI355X",
+    "chunk": "GQA chunked prefill over a KV cache TFLOP/s (fraction of bf16 MFMA peak), 1\u00d7MI355X",
+    "cross": "GQA cross-attention TFLOP/s (fraction of bf16 MFMA peak), 1\u00d7MI355X",
 }
 
 
@@ -455,7 +455,7 @@ def bench_project(args, w):
     byts = wkvs[0].numel() * 2 + x.numel() * 2 + 2 * w.B * T * w.K * w.d * 2   # W_KV + x read, K/V rows written
     ms_per_step = elapsed * 1e3 / args.steps
     res = {
-        "metric": "GQA fused K/V projection + append GB/s (W_KV streamed once per step), 1xMI355X",
+        "metric": "GQA fused K/V projection + append GB/s (W_KV streamed once per step), 1\u00d7MI355X",
         "value": round(byts / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
