@@ -1,6 +1,7 @@
 // Decode combine pass: merges the partitions' online-softmax states.
 //
-// For query head h of sequence b with n = ceil(L_b / part_tokens) partitions
+// For query head h of sequence b with n active partitions (those starting
+// below L_b, of balanced_part_tokens(L_b, part_tokens) positions each)
 // holding (m_p, l_p, acc_p) in base-2 units:
 //     M = max_p m_p,  w_p = 2^(m_p - M),
 //     out = (sum_p w_p acc_p) / (sum_p w_p l_p),
@@ -31,7 +32,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   const int b = bh / H;
   const int lane = threadIdx.x;
   const int L = LENS_FROM_WS ? ws_lens[b] : seq_lens[b];
-  const int n = L > 0 ? min(parts, (L + part_tokens - 1) / part_tokens) : 0;
+  const int pt_b = balanced_part_tokens(L, part_tokens);
+  const int n = L > 0 ? min(parts, (L + pt_b - 1) / pt_b) : 0;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)bh * parts;
   const float* pa = part_acc + (size_t)bh * parts * D + lane * PER;
 

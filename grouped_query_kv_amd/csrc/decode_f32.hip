@@ -57,9 +57,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
     }
     if (p == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens_out[b] = L;
   }
-  const int t0 = p * part_tokens;
+  const int pt_b = balanced_part_tokens(L, part_tokens);
+  const int t0 = p * pt_b;
   if (t0 >= L) return;
-  const int t1 = min(t0 + part_tokens, L);
+  const int t1 = min(t0 + pt_b, L);
   const int nh = min(kHB, G - hb * kHB);  // real heads in this block
 
   const int tid = threadIdx.x;

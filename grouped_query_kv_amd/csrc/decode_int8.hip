@@ -86,9 +86,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
   const int b = blockIdx.z;
   const int G = H / K;
   const int L = seq_lens[b];
-  const int t0 = p * part_tokens;
+  const int pt_b = balanced_part_tokens(L, part_tokens);
+  const int t0 = p * pt_b;
   if (t0 >= L) return;
-  const int t1 = min(t0 + part_tokens, L);
+  const int t1 = min(t0 + pt_b, L);
 
   const int lane = threadIdx.x;
   const int n = lane & 15;

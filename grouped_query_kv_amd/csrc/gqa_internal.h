@@ -21,6 +21,19 @@ struct DecodePlan {
 
 DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, int max_part_tokens = 0);
 
+// Partition length of a sequence of L positions under a plan of `pt`
+// positions per partition: the ceil(L / pt) partitions are made equal
+// (rounded up to a multiple of 32, so never longer than pt), so that the
+// last partition of a short or ragged sequence is not a small leftover.
+// Every partition pass and the combine pass use it, so they agree on which
+// partitions exist: p is active iff p * balanced_part_tokens(L, pt) < L.
+__host__ __device__ inline int balanced_part_tokens(int L, int pt) {
+  if (L <= 0) return pt;
+  const int n = (L + pt - 1) / pt;
+  const int even = (L + n - 1) / n;
+  return (even + 31) / 32 * 32;
+}
+
 // Workspace layout of a decode call:
 //   part_acc [B*H][parts][d]   fp32 un-normalised partial outputs
 //   part_ml  [B*H][parts][2]   fp32 running max (log2 units) and running sum
