@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
     int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, PagedArgs pg) {
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, PagedArgs pg, int p_slowest) {
   static_assert(!(APPEND && PAGED), "fused append is for contiguous caches");
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;        // contraction steps of Q.K
@@ -95,10 +95,27 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * LDS_ROW];
 
-  const int p = blockIdx.x;
-  const int k = blockIdx.y / head_blocks;
-  const int hb = blockIdx.y - k * head_blocks;
-  const int b = blockIdx.z;
+  // Work item of this workgroup.  With many partitions per sequence the
+  // grid is (partition, unit, b): consecutive workgroups stream adjacent
+  // parts of one head.  With few (large batches) it is one-dimensional with
+  // the partition index slowest, so every sequence's first partitions are
+  // dispatched before anyone's last and the short sequences of a ragged
+  // batch do not leave the end of the launch to a few long ones.
+  int p, y, b;
+  if (p_slowest) {
+    const int nub = gridDim.x / parts;  // units * B
+    p = blockIdx.x / nub;
+    const int rem = blockIdx.x - p * nub;
+    const int units = K * head_blocks;
+    b = rem / units;
+    y = rem - b * units;
+  } else {
+    p = blockIdx.x;
+    y = blockIdx.y;
+    b = blockIdx.z;
+  }
+  const int k = y / head_blocks;
+  const int hb = y - k * head_blocks;
   const int G = H / K;
   const int L_in = PAGED ? min(seq_lens[b], pg.max_blocks * pg.block_size) : seq_lens[b];
   int L = L_in, newpos = -1;
@@ -107,7 +124,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       newpos = L_in;
       L = L_in + 1;
     }
-    if (p == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens_out[b] = L;
+    if (p == 0 && y == 0 && threadIdx.x == 0) lens_out[b] = L;
   }
   const int pt_b = balanced_part_tokens(L, part_tokens);
   const int t0 = p * pt_b;
@@ -283,7 +300,12 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
                                     float scale_log2, const void* k_new, const void* v_new,
                                     const PagedArgs* paged, hipStream_t stream) {
-  const dim3 grid(plan.parts, K * plan.head_blocks, B);
+  // few partitions per sequence: one-dimensional grid, partition slowest
+  // (measured on the ragged 70B layer: 4% faster; with 24 partitions per
+  // sequence the three-dimensional order is 1.3% faster)
+  const bool p_slowest = plan.parts > 1 && plan.parts <= 8;
+  const dim3 grid = p_slowest ? dim3(plan.parts * K * plan.head_blocks * B)
+                              : dim3(plan.parts, K * plan.head_blocks, B);
   const dim3 block(64);
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<__bf16*>(k_cache);
@@ -294,7 +316,7 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
 #define GQA_SPLIT(DD, AP, PG)                                                                     \
   hipLaunchKernelGGL((decode_split_bf16_kernel<DD, AP, PG>), grid, block, 0, stream, qp, kp, vp,  \
                      seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts, \
-                     plan.head_blocks, scale_log2, kn, vn, ws.lens, pg)
+                     plan.head_blocks, scale_log2, kn, vn, ws.lens, pg, p_slowest ? 1 : 0)
 #define GQA_SPLIT_D(DD)                                                                           \
   if (paged) GQA_SPLIT(DD, false, true);                                                          \
   else if (k_new) GQA_SPLIT(DD, true, false);                                                     \
