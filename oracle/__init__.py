@@ -10,8 +10,9 @@ hot path computes, written from the pages' description of the method:
 * ``gqa_oracle``  -- the definitions (decode, causal prefill, cache append,
   paged-cache gather / decode / append, int8 cache quantisation / decode /
   append, chunked prefill over a cache, cross-attention, multi-row append,
-  fused K/V projection + append, mean-pool conversion, KV-cache byte count),
-  vectorised with NumPy.
+  fused K/V projection + append, mean-pool conversion, KV-cache byte count,
+  and the partition/merge model of the two-pass decode), vectorised with
+  NumPy.
 * ``bruteforce``  -- the same definitions as pure-Python scalar loops, for
   tiny inputs only; it derives the query-head -> KV-head grouping from the
   page's 1-based group formula independently of ``gqa_oracle``.
@@ -39,4 +40,6 @@ from .gqa_oracle import (  # noqa: F401
     kv_append_rows_ref,
     kv_project_ref,
     kv_project_append_ref,
+    decode_partials_ref,
+    combine_partials_ref,
 )

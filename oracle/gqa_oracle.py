@@ -484,3 +484,59 @@ def kv_project_append_ref(x, w_kv, k_cache, v_cache, seq_lens):
     kr, vr = kv_project_ref(x, w_kv)
     return kv_append_rows_ref(kr, vr, np.asarray(k_cache, dtype=np.float64),
                               np.asarray(v_cache, dtype=np.float64), seq_lens)
+
+
+# --------------------------------------------------------------------------
+# Split model (test infrastructure for the two-pass decode)
+# --------------------------------------------------------------------------
+# The decode is computed in partitions of the cached positions whose partial
+# states are merged afterwards (the block-wise online softmax the foundit.cn
+# article and the engineering section of pinghaoyang.com.cn name, via
+# FlashAttention).  For a partition P the partial state of a query is
+#     m_P = max_{j in P} s_j,  l_P = sum_{j in P} e^{s_j - m_P},
+#     acc_P = sum_{j in P} e^{s_j - m_P} v_j
+# (m = -inf, l = 0, acc = 0 for an empty partition) and the merge is
+#     M = max_P m_P,  out = sum_P e^{m_P - M} acc_P / sum_P e^{m_P - M} l_P,
+# which equals the softmax-weighted sum over all positions because
+# e^{s - m_P} e^{m_P - M} = e^{s - M}.
+
+
+def decode_partials_ref(q, k_cache, v_cache, seq_lens, scale, bounds):
+    """float64 partial states of every query head for the position ranges
+    ``bounds`` = [(t0, t1), ...] (clipped to [0, L_b)).
+    Returns (m [B, H, P], l [B, H, P], acc [B, H, P, d])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, d = q.shape
+    K = k_cache.shape[1]
+    G = H // K
+    P = len(bounds)
+    m = np.full((B, H, P), -np.inf)
+    l = np.zeros((B, H, P))
+    acc = np.zeros((B, H, P, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        for h in range(H):
+            k = h // G
+            for p, (t0, t1) in enumerate(bounds):
+                t0, t1 = max(t0, 0), min(t1, L)
+                if t0 >= t1:
+                    continue
+                s = float(scale) * (np.asarray(k_cache[b, k, t0:t1], dtype=np.float64) @ q[b, h])
+                m[b, h, p] = s.max()
+                e = np.exp(s - m[b, h, p])
+                l[b, h, p] = e.sum()
+                acc[b, h, p] = e @ np.asarray(v_cache[b, k, t0:t1], dtype=np.float64)
+    return m, l, acc
+
+
+def combine_partials_ref(m, l, acc) -> np.ndarray:
+    """Merge partial states over the last partition axis; a query whose
+    partitions are all empty gets a zero row."""
+    M = m.max(axis=-1, keepdims=True)
+    w = np.where(np.isfinite(m), np.exp(m - np.where(np.isfinite(M), M, 0.0)), 0.0)
+    num = (w[..., None] * acc).sum(axis=-2)
+    den = (w * l).sum(axis=-1)
+    out = np.zeros_like(num)
+    nz = den > 0
+    out[nz] = num[nz] / den[nz][..., None]
+    return out

@@ -660,6 +660,33 @@ def check_project_append(O):
     assert np.array_equal(k2[1, :, :3], kc[1, :, :3])
 
 
+# --------------------------------------------------------------------------
+# split model of the two-pass decode
+# --------------------------------------------------------------------------
+def check_split_merge_equals_decode(O):
+    """Any partition plan -- equal, ragged, with empty partitions, one
+    position per partition -- merges to the plain decode (1e-12)."""
+    q, kc, vc, sl = _rand_decode(3400, 3, 8, 2, 16, [37, 0, 100], nan_tail=False)
+    ref = O.decode_ref(q, kc, vc, sl, 0.3)
+    plans = [[(0, 101)], [(0, 32), (32, 64), (64, 96), (96, 128)], [(0, 7), (7, 50), (50, 51), (51, 200)],
+             [(0, 5), (300, 400), (5, 101)], [(j, j + 1) for j in range(101)]]
+    for bounds in plans:
+        out = O.combine_partials_ref(*O.decode_partials_ref(q, kc, vc, sl, 0.3, bounds))
+        _close(out, ref, 1e-12, f"merge over {len(bounds)} partitions")
+        assert np.all(out[1] == 0), "an empty sequence merges to zeros"
+
+
+def check_split_partials_closed_form(O):
+    """One position per partition: m is the score, l = 1 and acc = v."""
+    q, kc, vc, sl = _rand_decode(3500, 1, 2, 1, 4, [3], nan_tail=False)
+    m, l, acc = O.decode_partials_ref(q, kc, vc, sl, 0.5, [(0, 1), (1, 2), (2, 3), (3, 4)])
+    for h in range(2):
+        for j in range(3):
+            _close(m[0, h, j], 0.5 * kc[0, 0, j] @ q[0, h], 1e-15, "score")
+            assert l[0, h, j] == 1.0 and np.array_equal(acc[0, h, j], vc[0, 0, j])
+        assert m[0, h, 3] == -np.inf and l[0, h, 3] == 0 and not acc[0, h, 3].any()
+
+
 ALL_CHECKS = [
     check_kv_bytes_golden, check_kv_head_map,
     check_bruteforce_decode, check_bruteforce_prefill, check_bruteforce_meanpool,
@@ -676,4 +703,5 @@ ALL_CHECKS = [
     check_chunk_equals_causal_rows, check_chunk_single_token_is_decode, check_cross_attention_sdpa,
     check_cross_rows_are_decodes, check_append_rows,
     check_project_identity_weights, check_project_linear_library, check_project_append,
+    check_split_merge_equals_decode, check_split_partials_closed_form,
 ]

@@ -97,6 +97,10 @@ MUTATIONS = {
     "project_transposed_weight": [('y = np.einsum("btm,kjm->bktj", x, w)', 'y = np.einsum("btm,kjm->bktj", x, w[:, ::-1, :])')],
     "project_heads_interleaved": [('y = np.einsum("btm,kjm->bktj", x, w)',
                                    'y = np.einsum("btm,kjm->bktj", x, w.reshape(2, K, d, dm).transpose(1, 0, 2, 3).reshape(K, 2 * d, dm))')],
+    "merge_without_rescale": [("    num = (w[..., None] * acc).sum(axis=-2)", "    num = acc.sum(axis=-2)")],
+    "merge_unweighted_denominator": [("    den = (w * l).sum(axis=-1)", "    den = l.sum(axis=-1)")],
+    "partials_unshifted_sum": [("                l[b, h, p] = e.sum()", "                l[b, h, p] = np.exp(s).sum()")],
+    "partials_end_inclusive": [("                t0, t1 = max(t0, 0), min(t1, L)", "                t0, t1 = max(t0, 0), min(t1 + 1, L)")],
     "empty_length_nan": [("        if L == 0:\n            continue\n        for k in range(K):",
                           "        for k in range(K):")],
 }
