@@ -90,9 +90,19 @@ def kv_bytes(lens, K, d, elem, row_extra=0):
     return int(sum(2 * K * int(L) * (d * elem + row_extra) for L in lens))
 
 
+def host_cores():
+    """The host cores this process may use (at most 16: the share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def cpu_baseline_decode(inp, w, budget_s):
     """Time the fp64 oracle (unchanged) on whole sequences of the workload,
-    one BLAS thread, until about `budget_s` seconds have been spent."""
+    on the host's cores (BLAS threads), until about `budget_s` seconds have
+    been spent."""
     from threadpoolctl import threadpool_limits
 
     from grouped_query_kv_amd.inputs import paged_layout
@@ -105,7 +115,8 @@ def cpu_baseline_decode(inp, w, budget_s):
     d = w.d
     scale = float(np.float32(1.0 / math.sqrt(d)))
     done_bytes, done_seqs, t_used = 0, 0, 0.0
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         b = 0
         while t_used < budget_s:
             sl = inp["seq_lens"][b:b + 1].numpy()
@@ -143,11 +154,11 @@ def cpu_baseline_decode(inp, w, budget_s):
             done_bytes += kv_bytes(sl, w.K, d, elem, row_extra)
             done_seqs += 1
             b = (b + 1) % w.B
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "tokens_per_s": done_seqs / t_used,
             "sample": f"{done_seqs} whole sequences of the workload ({'paged ' if paged else 'int8 ' if int8 else ''}append + decode over "
                       f"{int(inp['seq_lens'][0]) + (1 if w.append else 0)} positions, all 32 heads), "
-                      f"{t_used:.1f} s of fp64 NumPy on 1 thread"}
+                      f"{t_used:.1f} s of fp64 NumPy on {cores} BLAS threads"}
 
 
 def bench_decode(args, w):
@@ -258,6 +269,23 @@ def bench_decode(args, w):
     value = total_bytes / elapsed / 1e9
     kern_avg_ms = float(np.mean(kern_ms))
     achieved = float(np.mean([step_bytes[j] for j in sampled])) / (kern_avg_ms * 1e-3) / 1e9
+    p10, p50, p90 = (float(x) for x in np.percentile(kern_ms, [10, 50, 90]))
+    # warm figure: the same cache copy every step (it partly stays in the
+    # 256 MB Infinity Cache); never the headline
+    warm_ms = None
+    if not (paged or int8):
+        wev = (gqa.HipEvent(), gqa.HipEvent())
+        c0 = copies[0]
+        for _ in range(6):
+            gqa.gqa_decode(q, c0["k"], c0["v"], c0["sl"], out, ws, max_len, scale=scale, stream=stream)
+        wts = []
+        for _ in range(10):
+            gqa.gqa_set_timing_events(*wev)
+            gqa.gqa_decode(q, c0["k"], c0["v"], c0["sl"], out, ws, max_len, scale=scale, stream=stream)
+            gqa.gqa_set_timing_events(None, None)
+            wts.append(wev[0].elapsed_ms(wev[1]))
+        warm_ms = float(np.median(wts))
+    copy_gbs = copy_ceiling(dev)
     res = {
         "metric": "GQA decode KV-read GB/s (% of HBM peak) + attention tokens/s, 1\u00d7MI355X",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -280,10 +308,31 @@ def bench_decode(args, w):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("decode_split_int8_kernel" if int8 else
                                                  "decode_split_bf16_kernel" + ("_paged" if paged else "")),
-                     "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled)},
+                     "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled),
+                     "kernel_us_p10_p50_p90": [round(p10 * 1e3, 2), round(p50 * 1e3, 2), round(p90 * 1e3, 2)],
+                     "copy_ceiling_GBps": round(copy_gbs, 1),
+                     **({"warm_kernel_us": round(warm_ms * 1e3, 2)} if warm_ms is not None else {})},
         "input_gen_s": round(t_gen, 1),
     }
     return res, inp
+
+
+def copy_ceiling(dev, nbytes=1 << 30):
+    """Device-to-device copy rate of a 1 GiB buffer (read + write bytes / time):
+    a measured ceiling for streaming kernels, beside the 8 TB/s spec."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def visible_pairs(w):
@@ -298,7 +347,7 @@ def visible_pairs(w):
 
 def cpu_baseline_prefill(inp, w, budget_s):
     """Time the fp64 oracle (unchanged) on whole (sequence, head) slices of
-    the workload, one BLAS thread, until about `budget_s` seconds."""
+    the workload, on the host's cores, until about `budget_s` seconds."""
     from threadpoolctl import threadpool_limits
 
     from oracle import cross_attention_ref, prefill_causal_ref, prefill_chunk_ref
@@ -306,7 +355,8 @@ def cpu_baseline_prefill(inp, w, budget_s):
     scale = float(np.float32(1.0 / math.sqrt(w.d)))
     G = w.H // w.K
     done, t_used, heads = 0.0, 0.0, 0
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         while t_used < budget_s and heads < w.B * w.H:
             b, h = divmod(heads, w.H)
             q = inp["q"][b:b + 1, h:h + 1].double().numpy()
@@ -329,9 +379,9 @@ def cpu_baseline_prefill(inp, w, budget_s):
             t_used += time.perf_counter() - t0
             done += 4.0 * w.d * visible_pairs(w)
             heads += 1
-    return {"value": done / t_used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": done / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} whole (sequence, head) slices of the workload, "
-                      f"{t_used:.1f} s of fp64 NumPy on 1 thread"}
+                      f"{t_used:.1f} s of fp64 NumPy on {cores} BLAS threads"}
 
 
 PREFILL_METRIC = {
@@ -473,8 +523,8 @@ def bench_project(args, w):
 
 
 def cpu_baseline_project(inp, w, budget_s):
-    """The oracle's projection of whole steps (all tokens, all heads), one
-    BLAS thread, repeated for about `budget_s` seconds."""
+    """The oracle's projection of whole steps (all tokens, all heads), on the
+    host's cores, repeated for about `budget_s` seconds."""
     from threadpoolctl import threadpool_limits
 
     from oracle import kv_project_ref
@@ -483,14 +533,15 @@ def cpu_baseline_project(inp, w, budget_s):
     wk = inp["w_kv"].float().numpy()
     byts = wk.size * 2 + x.size * 2 + 2 * x.shape[0] * x.shape[1] * wk.shape[0] * (wk.shape[1] // 2) * 2
     steps, t_used = 0, 0.0
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         while t_used < budget_s:
             t0 = time.perf_counter()
             kv_project_ref(x, wk)
             t_used += time.perf_counter() - t0
             steps += 1
-    return {"value": steps * byts / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{steps} whole projection steps, {t_used:.1f} s of fp64 NumPy on 1 thread"}
+    return {"value": steps * byts / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} whole projection steps, {t_used:.1f} s of fp64 NumPy on {cores} BLAS threads"}
 
 
 def main():
