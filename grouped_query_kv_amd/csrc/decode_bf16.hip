@@ -300,10 +300,11 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
                                     float scale_log2, const void* k_new, const void* v_new,
                                     const PagedArgs* paged, hipStream_t stream) {
-  // few partitions per sequence: one-dimensional grid, partition slowest
-  // (measured on the ragged 70B layer: 4% faster; with 24 partitions per
-  // sequence the three-dimensional order is 1.3% faster)
-  const bool p_slowest = plan.parts > 1 && plan.parts <= 8;
+  // many (sequence, head) units -- a large batch -- : one-dimensional grid,
+  // partition slowest (measured on the ragged 70B layer, 512 units: 4%
+  // faster; on the Llama-3-8B layer, 128 units, the three-dimensional order
+  // is 1.3% faster)
+  const bool p_slowest = plan.parts > 1 && B * K * plan.head_blocks >= 256;
   const dim3 grid = p_slowest ? dim3(plan.parts * K * plan.head_blocks * B)
                               : dim3(plan.parts, K * plan.head_blocks, B);
   const dim3 block(64);
