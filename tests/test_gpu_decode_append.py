@@ -91,3 +91,36 @@ def test_fused_step_full_workload():
         assert torch.equal(kc[b, :, w.L].cpu(), inp["k_new"][b]) and torch.equal(vc[b, :, w.L].cpu(), inp["v_new"][b])
     r = report("fused llama3_8b", f64(out), ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+
+
+def test_many_fused_steps_until_a_cache_fills():
+    """40 consecutive fused decode steps on a ragged batch whose shortest
+    cache fills up on the way: after every step the lengths match the
+    oracle's appends, the output matches the oracle's decode, and at the end
+    the caches are bit-identical to the oracle's (full caches stop growing)."""
+    B, H, K, d, S_max = 3, 16, 4, 128, 64
+    lens = [40, 0, 30]
+    inp = decode_inputs(B, H, K, d, "bf16", seed=121, lens=lens, s_max=S_max)
+    g = torch.Generator().manual_seed(122)
+    it = torch.int16
+    kc, vc, sl = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV), inp["seq_lens"].to(DEV)
+    k_ref, v_ref = inp["k_cache"].view(it).numpy(), inp["v_cache"].view(it).numpy()
+    s_ref = inp["seq_lens"].numpy()
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, S_max, d), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    for step in range(40):
+        q = torch.randn((B, H, d), generator=g).to(torch.bfloat16)
+        kn = torch.randn((B, K, d), generator=g).to(torch.bfloat16)
+        vn = torch.randn((B, K, d), generator=g).to(torch.bfloat16)
+        gqa.gqa_decode_append(q.to(DEV), kn.to(DEV), vn.to(DEV), kc, vc, sl, out, ws, S_max, scale=scale_of(d))
+        k_ref, v_ref, s_ref = kv_append_ref(kn.view(it).numpy(), vn.view(it).numpy(), k_ref, v_ref, s_ref)
+        torch.cuda.synchronize()
+        assert sl.cpu().tolist() == list(s_ref), f"step {step}"
+        kf = torch.from_numpy(k_ref.copy()).view(torch.bfloat16).float().numpy()
+        vf = torch.from_numpy(v_ref.copy()).view(torch.bfloat16).float().numpy()
+        ref = decode_ref(f64(q), kf, vf, s_ref, scale_of(d))
+        vmax = max(float(np.abs(vf[b, :, :L]).max()) if L else 0.0 for b, L in enumerate(s_ref))
+        err = float(np.abs(f64(out) - ref).max())
+        assert np.isfinite(err) and err <= bf16_bound(ref, vmax), f"step {step}: {err}"
+    assert list(s_ref) == [S_max, 40, S_max]
+    assert np.array_equal(kc.cpu().view(it).numpy(), k_ref) and np.array_equal(vc.cpu().view(it).numpy(), v_ref)
