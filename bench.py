@@ -14,9 +14,10 @@ them (gqa_decode_append: the append fused into the partition pass, then the
 combine pass -- the same work as gqa_kv_append followed by gqa_decode).  A
 paged workload (decode_paged_llama3_8b) runs gqa_kv_append_paged and then
 gqa_decode_paged over 16-row blocks in shuffled physical order; an int8
-workload (decode_int8_llama3_8b) runs gqa_kv_append_int8 and then
-gqa_decode_int8 over the cache quantised once before timing (bytes counted
-as stored: d codes + one fp32 scale per row).  The default workload is
+workload (decode_int8_llama3_8b) runs gqa_decode_append_int8 (the
+quantising append fused into the int8 partition pass) over the cache
+quantised once before timing (bytes counted as stored: d codes + one fp32
+scale per row).  The default workload is
 the Llama-3-8B-shaped layer: B=16 sequences at 8192 cached tokens, 32 query
 heads over 8 KV heads, d=128, bf16 (synthetic N(0,1) data).
 
@@ -219,11 +220,10 @@ def bench_decode(args, w):
         if ev is not None:
             gqa.gqa_set_timing_events(ev[0], ev[1])
         if int8:
-            # quantising append, then decode over the int8 cache (three launches)
-            gqa.gqa_kv_append_int8(kn, vn, c["k"], c["v"], c["ks"], c["vs"], c["sl"], stream=stream)
+            # quantising append fused into the int8 partition pass (two launches)
+            gqa.gqa_decode_append_int8(q, kn, vn, c["k"], c["v"], c["ks"], c["vs"], c["sl"], out, ws,
+                                       max_len, scale=scale, stream=stream)
             host_lens[i % R] += 1
-            gqa.gqa_decode_int8(q, c["k"], c["v"], c["ks"], c["vs"], c["sl"], out, ws, max_len,
-                                scale=scale, stream=stream)
         elif paged:
             # append through the block table, then decode (three kernel launches)
             if w.append:

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "gqa_kv_quantize_int8": (_c_int, [_c_void_p] * 3 + [_c_int64, _c_int, _c_int, _c_void_p]),
     "gqa_kv_append_int8": (_c_int, [_c_void_p] * 7 + [_c_int] * 5 + [_c_void_p]),
     "gqa_decode_int8": (_c_int, [_c_void_p] * 8 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_decode_append_int8": (_c_int, [_c_void_p] * 10 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_prefill_chunk": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_cross_attention": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_kv_append_rows": (_c_int, [_c_void_p] * 5 + [_c_int] * 6 + [_c_void_p]),
@@ -390,6 +391,33 @@ def gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, out, work
         q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),
         seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K, S_max,
         int(max_seq_len), d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def gqa_decode_append_int8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales, seq_lens, out,
+                           workspace, max_seq_len: int, scale: float | None = None, stream=None) -> None:
+    """gqa_kv_append_int8 followed by gqa_decode_int8, fused into two kernel
+    launches (bf16 q, k_new, v_new).  max_seq_len bounds the lengths after
+    the append."""
+    _need(q, "q", 3, (torch.bfloat16,))
+    _need_int8_cache(k_codes, v_codes, k_scales, v_scales)
+    _need(out, "out", 3)
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    _need(workspace, "workspace", 1, (torch.uint8,))
+    B, H, d = q.shape
+    Bk, K, S_max, dk = k_codes.shape
+    if Bk != B or dk != d or tuple(out.shape) != (B, H, d) or seq_lens.numel() != B:
+        raise ValueError("shape mismatch between q, cache, seq_lens and out")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, 3, (torch.bfloat16,))
+        if tuple(t.shape) != (B, K, d):
+            raise ValueError(f"{nm} must be [B,K,d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("gqa_decode_append_int8", load_library().gqa_decode_append_int8(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+        k_scales.data_ptr(), v_scales.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), B, H, K, S_max, int(max_seq_len), d, float(scale),
+        GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def gqa_prefill_causal(q, k, v, out, scale: float | None = None, stream=None) -> None:

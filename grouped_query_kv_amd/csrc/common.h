@@ -40,5 +40,16 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
 // 2^x on the hardware exponential unit; exp2(-inf) = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The int8 cache rule for a row with maximum magnitude amax > 0: code of x
+// is clamp(rint(x * (127 / amax)), -127, 127) and the row's scale is
+// amax / 127, all in IEEE fp32 with correctly rounded division (a row of
+// zeros has codes 0 and scale 0).  Shared by every kernel that quantises.
+__device__ __forceinline__ float int8_inv(float amax) { return __fdiv_rn(127.f, amax); }
+__device__ __forceinline__ int int8_code(float x, float inv) {
+  const float c = rintf(__fmul_rn(x, inv));
+  return (int)fminf(fmaxf(c, -127.f), 127.f);
+}
+__device__ __forceinline__ float int8_scale(float amax) { return __fdiv_rn(amax, 127.f); }
+
 
 }  // namespace gqa

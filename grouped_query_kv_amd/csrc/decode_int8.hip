@@ -62,12 +62,26 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // needed to keep the same bytes in flight.  (Measured on the Llama-3-8B layer
 // and a 131072-token context: 10-15% faster than the unconstrained
 // allocation at two waves, and than 64-position chunks at two waves.)
-template <int D>
+//
+// APPEND: the quantising append fused in.  The step's new rows k_new, v_new
+// (bf16) belong at position L_in = seq_lens[b] when the cache has room; it is
+// the last position of the sequence, so only workgroups of its last
+// partition see it.  Each of them quantises the rows by the cache rule (the
+// same fp32 operations as the standalone append, so the same codes and
+// scales) into its own slot of the workspace -- codes, and the 4-aligned
+// group of scales around the new position with the new scale in place --
+// and its loads take the slot instead of the cache for that position (a
+// pointer select, so the loop keeps its shape).  After the loop the first
+// head block copies the slot into the cache; no other workgroup of this
+// launch reads that cache row or scale.  The lengths after the append go to
+// `lens_out` for the combine pass.
+template <int D, bool APPEND>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_int8_kernel(
-    const __bf16* __restrict__ q, const int8_t* __restrict__ kc, const int8_t* __restrict__ vc,
-    const float* __restrict__ ks, const float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
+    const __bf16* __restrict__ q, int8_t* __restrict__ kc, int8_t* __restrict__ vc,
+    float* __restrict__ ks, float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
     float* __restrict__ part_acc, float* __restrict__ part_ml, int H, int K, int S_max,
-    int part_tokens, int parts, int head_blocks, float scale_log2) {
+    int part_tokens, int parts, int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, uint8_t* __restrict__ slots) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;
   constexpr int NTILES = D / 16;
@@ -85,7 +99,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
   const int hb = blockIdx.y - k * head_blocks;
   const int b = blockIdx.z;
   const int G = H / K;
-  const int L = seq_lens[b];
+  const int L_in = seq_lens[b];
+  int L = L_in, newpos = -1;
+  if (APPEND) {
+    if (L_in < S_max) {
+      newpos = L_in;
+      L = L_in + 1;
+    }
+    if (p == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens_out[b] = L;
+  }
   const int pt_b = balanced_part_tokens(L, part_tokens);
   const int t0 = p * pt_b;
   if (t0 >= L) return;
@@ -105,10 +127,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
   }
 
   const size_t head_row0 = ((size_t)b * K + k) * (size_t)S_max;  // first row of (b, k)
-  const int8_t* kbase = kc + head_row0 * D;
-  const int8_t* vbase = vc + head_row0 * D;
-  const float* ksb = ks + head_row0;
-  const float* vsb = vs + head_row0;
+  int8_t* kbase = kc + head_row0 * D;
+  int8_t* vbase = vc + head_row0 * D;
+  float* ksb = ks + head_row0;
+  float* vsb = vs + head_row0;
+
+  // The new rows: slot = [K codes (D) | V codes (D) | K scales (4) | V scales (4)].
+  const bool has_new = APPEND && newpos >= t0 && newpos < t1;  // wave-uniform
+  const int s0_new = has_new ? (newpos & ~3) : -4;              // its scale group
+  int8_t* slot = reinterpret_cast<int8_t*>(slots) +
+                 (APPEND ? ((size_t)blockIdx.z * gridDim.y + blockIdx.y) * (2 * D + 32) : 0);
+  float* slot_sc = reinterpret_cast<float*>(slot + 2 * D);
+  if (has_new) {
+    constexpr int E = D / 64;  // elements per lane
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const __bf16* src = (r == 0 ? k_new : v_new) + ((size_t)b * K + k) * D + E * lane;
+      float x[E];
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        x[e] = static_cast<float>(src[e]);
+        amax = fmaxf(amax, fabsf(x[e]));
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const float inv = amax > 0.f ? int8_inv(amax) : 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) slot[r * D + E * lane + e] = amax > 0.f ? (int8_t)int8_code(x[e], inv) : 0;
+      if (lane < 4) {  // scale group: cached scales before the new position, 0 after it
+        const int pos = s0_new + lane;
+        const float* rs = r == 0 ? ksb : vsb;
+        slot_sc[4 * r + lane] = pos < newpos ? rs[pos] : pos == newpos ? (amax > 0.f ? int8_scale(amax) : 0.f) : 0.f;
+      }
+    }
+    __syncthreads();  // the slot's stores are visible to every lane of the workgroup
+  }
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -127,20 +181,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int tok = c0 + 16 * mt + n;
-      const int8_t* krow = kbase + (size_t)tok * D + KSEG * g;
+      const int8_t* krow = (APPEND && tok == newpos ? slot : kbase + (size_t)tok * D) + KSEG * g;
 #pragma unroll
       for (int w = 0; w < KWORDS; ++w) ka[mt][w] = tok < t1 ? ld16_stream(krow + 16 * w) : zero_u32x4();
       // scales of the positions this lane's scores belong to: 16mt + 4g + i
       const int s0 = c0 + 16 * mt + 4 * g;
-      ksv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(ksb + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
-      vsv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(vsb + s0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const bool sc_new = APPEND && s0 == s0_new;
+      const float* kss = sc_new ? slot_sc : ksb + s0;
+      const float* vss = sc_new ? slot_sc + 4 : vsb + s0;
+      ksv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(kss) : f32x4{0.f, 0.f, 0.f, 0.f};
+      vsv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(vss) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   auto load_v = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int tok = c0 + i * ROWS_PER_LOAD + vrow;
-      vr[i] = tok < t1 ? ld16_stream(vbase + (size_t)tok * D + vcol) : zero_u32x4();
+      const int8_t* vrow_p = APPEND && tok == newpos ? slot + D : vbase + (size_t)tok * D;
+      vr[i] = tok < t1 ? ld16_stream(vrow_p + vcol) : zero_u32x4();
     }
   };
   load_k(t0);
@@ -233,6 +291,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
     __syncthreads();
   }
 
+  if (APPEND && has_new && hb == 0) {  // the appended rows join the cache
+    if (lane < 2 * (D / 16)) {
+      const int r = lane / (D / 16), w = lane % (D / 16);
+      *reinterpret_cast<u32x4*>((r == 0 ? kbase : vbase) + (size_t)newpos * D + 16 * w) =
+          ld16(slot + r * D + 16 * w);
+    }
+    if (lane < 2) (lane == 0 ? ksb : vsb)[newpos] = slot_sc[4 * lane + (newpos - s0_new)];
+  }
+
   const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -252,20 +319,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
 
 }  // namespace
 
-hipError_t launch_decode_split_int8(const void* q, const void* k_codes, const void* v_codes,
-                                    const float* k_scales, const float* v_scales,
-                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
-                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
-                                    float scale_log2, hipStream_t stream) {
+hipError_t launch_decode_split_int8(const void* q, void* k_codes, void* v_codes, float* k_scales,
+                                    float* v_scales, const int32_t* seq_lens,
+                                    const DecodeWorkspace& ws, const DecodePlan& plan, int B, int H,
+                                    int K, int S_max, int d, float scale_log2, const void* k_new,
+                                    const void* v_new, hipStream_t stream) {
   const dim3 grid(plan.parts, K * plan.head_blocks, B);
   auto qp = static_cast<const __bf16*>(q);
-  auto kp = static_cast<const int8_t*>(k_codes);
-  auto vp = static_cast<const int8_t*>(v_codes);
-#define GQA_I8(DD)                                                                              \
-  hipLaunchKernelGGL((decode_split_int8_kernel<DD>), grid, dim3(64), 0, stream, qp, kp, vp,      \
+  auto kp = static_cast<int8_t*>(k_codes);
+  auto vp = static_cast<int8_t*>(v_codes);
+  auto kn = static_cast<const __bf16*>(k_new);
+  auto vn = static_cast<const __bf16*>(v_new);
+#define GQA_I8(DD, AP)                                                                          \
+  hipLaunchKernelGGL((decode_split_int8_kernel<DD, AP>), grid, dim3(64), 0, stream, qp, kp, vp,  \
                      k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max,         \
-                     plan.part_tokens, plan.parts, plan.head_blocks, scale_log2)
-  if (d == 128) GQA_I8(128); else GQA_I8(64);
+                     plan.part_tokens, plan.parts, plan.head_blocks, scale_log2, kn, vn, ws.lens, \
+                     ws.new_rows)
+  if (d == 128) {
+    if (k_new) GQA_I8(128, true); else GQA_I8(128, false);
+  } else {
+    if (k_new) GQA_I8(64, true); else GQA_I8(64, false);
+  }
 #undef GQA_I8
   return hipGetLastError();
 }

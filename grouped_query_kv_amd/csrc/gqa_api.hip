@@ -100,7 +100,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d) {
   const size_t rows = (size_t)B * H * p.parts;
   return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float)) +
-         align256((size_t)B * sizeof(int32_t));
+         align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * H * (2 * d + 32));
 }
 
 DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d) {
@@ -112,6 +112,8 @@ DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, i
   w.part_ml = reinterpret_cast<float*>(c);
   c += align256(rows * 2 * sizeof(float));
   w.lens = reinterpret_cast<int32_t*>(c);
+  c += align256((size_t)B * sizeof(int32_t));
+  w.new_rows = reinterpret_cast<uint8_t*>(c);
   return w;
 }
 
@@ -354,11 +356,12 @@ int gqa_kv_append_int8(const void* k_new, const void* v_new, void* k_codes, void
   return r ? r : ok();
 }
 
-int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
-                    const float* v_scales, const int32_t* seq_lens, void* out, void* workspace,
-                    size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len, int d,
-                    float scale, int q_dtype, int out_dtype, void* stream) {
-  const char* fn = "gqa_decode_int8";
+// Shared body of gqa_decode_int8 and gqa_decode_append_int8 (k_new == nullptr: no append).
+static int decode_int8_impl(const char* fn, const void* q, const void* k_new, const void* v_new,
+                            void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                            int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
+                            int B, int H, int K, int S_max, int max_seq_len, int d, float scale,
+                            int q_dtype, int out_dtype, void* stream) {
   if (!q || !k_codes || !v_codes || !k_scales || !v_scales || !seq_lens || !out)
     return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
   if (int r = validate_heads(fn, B, H, K, d)) return r;
@@ -370,7 +373,8 @@ int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, con
   if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
     return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
   if (!aligned16(q) || !aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) ||
-      !aligned16(v_scales) || !aligned16(out) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+      !aligned16(v_scales) || !aligned16(out) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
+      (k_new && (!aligned16(k_new) || !aligned16(v_new))))
     return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
   const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d);
   const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
@@ -383,14 +387,38 @@ int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, con
   {
     TimedRegion timed(s);
     r = check_hip(gqa::launch_decode_split_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, ws,
-                                                plan, B, H, K, S_max, d, scale * gqa::kLog2eHost, s),
+                                                plan, B, H, K, S_max, d, scale * gqa::kLog2eHost,
+                                                k_new, v_new, s),
                   "partition-pass launch");
   }
   if (r) return r;
-  r = check_hip(gqa::launch_decode_combine(ws, const_cast<int32_t*>(seq_lens), out, plan, B, H, d,
-                                           out_dtype == GQA_BF16, false, s),
+  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16,
+                                           k_new != nullptr, s),
                 "combine-pass launch");
   return r ? r : ok();
+}
+
+int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
+                    const float* v_scales, const int32_t* seq_lens, void* out, void* workspace,
+                    size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len, int d,
+                    float scale, int q_dtype, int out_dtype, void* stream) {
+  // read-only use of the cache and lengths (no append)
+  return decode_int8_impl("gqa_decode_int8", q, nullptr, nullptr, const_cast<void*>(k_codes),
+                          const_cast<void*>(v_codes), const_cast<float*>(k_scales),
+                          const_cast<float*>(v_scales), const_cast<int32_t*>(seq_lens), out,
+                          workspace, workspace_bytes, B, H, K, S_max, max_seq_len, d, scale,
+                          q_dtype, out_dtype, stream);
+}
+
+int gqa_decode_append_int8(const void* q, const void* k_new, const void* v_new, void* k_codes,
+                           void* v_codes, float* k_scales, float* v_scales, int32_t* seq_lens,
+                           void* out, void* workspace, size_t workspace_bytes, int B, int H, int K,
+                           int S_max, int max_seq_len, int d, float scale, int dtype, int out_dtype,
+                           void* stream) {
+  if (!k_new || !v_new) return fail(GQA_ERR_INVALID, "gqa_decode_append_int8: null pointer");
+  return decode_int8_impl("gqa_decode_append_int8", q, k_new, v_new, k_codes, v_codes, k_scales,
+                          v_scales, seq_lens, out, workspace, workspace_bytes, B, H, K, S_max,
+                          max_seq_len, d, scale, dtype, out_dtype, stream);
 }
 
 // Shared validation and launch of the prefill family.

@@ -38,13 +38,18 @@ __host__ __device__ inline int balanced_part_tokens(int L, int pt) {
 //   part_acc [B*H][parts][d]   fp32 un-normalised partial outputs
 //   part_ml  [B*H][parts][2]   fp32 running max (log2 units) and running sum
 //   lens     [B]               int32 lengths after a fused append
+//   new_rows [B*H][2d + 32]    bytes: per workgroup slot of a fused int8
+//                              append (codes of the new K and V rows and
+//                              their 4-aligned scale groups); B*K*head_blocks
+//                              <= B*H slots are used
 struct DecodeWorkspace {
   float* part_acc;
   float* part_ml;
   int32_t* lens;
+  uint8_t* new_rows;
 };
 size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d);
-// (the workspace holds part_acc, part_ml and lens, each 256-byte aligned)
+// (the workspace holds part_acc, part_ml, lens and new_rows, each 256-byte aligned)
 DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d);
 
 // ---- launchers (each returns the hipGetLastError() of its launch) ----
@@ -92,11 +97,12 @@ hipError_t launch_kv_append_int8(const void* k_new, const void* v_new, void* k_c
                                  float* k_scales, float* v_scales, int32_t* seq_lens, int B, int K,
                                  int S_max, int d, bool bf16, hipStream_t stream);
 // Partition pass over an int8 cache (bf16 queries; S_max a multiple of 4).
-hipError_t launch_decode_split_int8(const void* q, const void* k_codes, const void* v_codes,
-                                    const float* k_scales, const float* v_scales,
-                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
-                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
-                                    float scale_log2, hipStream_t stream);
+// With k_new/v_new (bf16) non-null the quantising append is fused in.
+hipError_t launch_decode_split_int8(const void* q, void* k_codes, void* v_codes, float* k_scales,
+                                    float* v_scales, const int32_t* seq_lens,
+                                    const DecodeWorkspace& ws, const DecodePlan& plan, int B, int H,
+                                    int K, int S_max, int d, float scale_log2, const void* k_new,
+                                    const void* v_new, hipStream_t stream);
 
 // Combine pass: partials -> out (fp32 or bf16).  lens_from_ws: lengths come
 // from the workspace (fused append) and are published to seq_lens.

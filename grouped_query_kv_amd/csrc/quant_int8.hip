@@ -59,14 +59,10 @@ __device__ __forceinline__ uint2 quantize8(const float (&x)[8], float* scale) {
   for (int o = LPR / 2; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
   uint32_t w[2] = {0u, 0u};
   if (amax > 0.f) {
-    const float inv = __fdiv_rn(127.f, amax);
+    const float inv = int8_inv(amax);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float c = rintf(__fmul_rn(x[i], inv));
-      c = fminf(fmaxf(c, -127.f), 127.f);
-      w[i / 4] |= (uint32_t)((int)c & 0xff) << (8 * (i % 4));
-    }
-    *scale = __fdiv_rn(amax, 127.f);
+    for (int i = 0; i < 8; ++i) w[i / 4] |= (uint32_t)(int8_code(x[i], inv) & 0xff) << (8 * (i % 4));
+    *scale = int8_scale(amax);
   } else {
     *scale = 0.f;
   }

@@ -225,6 +225,23 @@ int gqa_decode_int8(const void* q, const void* k_codes, const void* v_codes, con
                     float scale, int q_dtype, int out_dtype, void* stream);
 
 /*
+ * One decode step with the quantising append fused in: the result of
+ * gqa_kv_append_int8(k_new, v_new, ...) followed by gqa_decode_int8(q, ...)
+ * on the grown cache -- the same codes, scales, lengths and output bits --
+ * in one partition pass and one combine pass.  (pinghaoyang.com.cn "GQA
+ * 完全拆解", decode memory ledger: each step writes the new token's K and V
+ * once per KV head and reads the cache; the int8 rule is the one above.)
+ * q, k_new, v_new are bf16 [B, H, d] / [B, K, d] (dtype must be GQA_BF16);
+ * max_seq_len bounds the lengths *after* the append.  Other arguments,
+ * alignment and workspace as gqa_decode_int8.
+ */
+int gqa_decode_append_int8(const void* q, const void* k_new, const void* v_new, void* k_codes,
+                           void* v_codes, float* k_scales, float* v_scales, int32_t* seq_lens,
+                           void* out, void* workspace, size_t workspace_bytes, int B, int H, int K,
+                           int S_max, int max_seq_len, int d, float scale, int dtype, int out_dtype,
+                           void* stream);
+
+/*
  * Causal GQA attention over a whole prefix (prefill):
  *   out[b, h, i, :] = sum_{j <= i} softmax_j(scale q[b,h,i,:] . k[b,h/G,j,:]) v[b,h/G,j,:]
  * for i in [0, S).  k and v are [B, K, S_max, d] with S <= S_max; rows >= S

@@ -229,6 +229,30 @@ def test_decode_int8_rejects(lib, kw, code):
     assert lib.gqa_last_error().decode().startswith("gqa_decode_int8")
 
 
+def _decode_append_int8(lib, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, sl=FAKE, out=FAKE, ws=FAKE,
+             wsb=1 << 30, B=2, H=32, K=8, S_max=128, max_seq_len=100, d=128, scale=0.088,
+             dtype=B.GQA_BF16, out_dtype=B.GQA_BF16)
+    a.update(kw)
+    return lib.gqa_decode_append_int8(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["ks"], a["vs"], a["sl"],
+                                      a["out"], a["ws"], a["wsb"], a["B"], a["H"], a["K"], a["S_max"],
+                                      a["max_seq_len"], a["d"], a["scale"], a["dtype"], a["out_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), B.GQA_ERR_INVALID),
+    (dict(vn=None), B.GQA_ERR_INVALID),
+    (dict(vn=FAKE + 8), B.GQA_ERR_INVALID),
+    (dict(dtype=B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    (dict(S_max=130, max_seq_len=100), B.GQA_ERR_INVALID),
+    (dict(d=96), B.GQA_ERR_UNSUPPORTED),
+    (dict(wsb=32), B.GQA_ERR_WORKSPACE),
+])
+def test_decode_append_int8_rejects(lib, kw, code):
+    assert _decode_append_int8(lib, **kw) == code
+    assert lib.gqa_last_error().decode().startswith("gqa_decode_append_int8")
+
+
 @pytest.mark.parametrize("args,code", [
     ((None, FAKE, FAKE, 10, 128, B.GQA_BF16), B.GQA_ERR_INVALID),
     ((FAKE, FAKE, FAKE, 0, 128, B.GQA_BF16), B.GQA_ERR_INVALID),

@@ -203,3 +203,58 @@ def test_int8_full_workload():
     r = report("int8 llama3_8b", f64(out), ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
     assert r["max_abs"] <= bf16_bound(ref, vmax)
+
+
+FUSED_CASES = [
+    # B, H, K, d, lens, s_max, steps
+    (3, 32, 8, 128, [1, 33, 1000], None, 1),
+    (4, 64, 8, 128, [0, 16, 17, 3000], None, 1),
+    (2, 16, 4, 64, [31, 2100], None, 1),
+    (2, 32, 1, 128, [129, 4100], None, 1),        # G = 32: two head blocks
+    (1, 71, 1, 64, [257], None, 1),               # G = 71: five head blocks
+    (4, 32, 8, 128, [64, 3, 4, 95], None, 1),     # new row at chunk / scale-group edges
+    (3, 32, 8, 128, [12, 5, 12], 12, 1),          # full caches: no append
+    (2, 32, 8, 128, [60, 3], 64, 8),              # eight steps; the first cache fills up
+]
+
+
+@pytest.mark.parametrize("B,H,K,d,lens,s_max,steps", FUSED_CASES)
+def test_int8_fused_append_matches_unfused(B, H, K, d, lens, s_max, steps):
+    """gqa_decode_append_int8 == gqa_kv_append_int8 + gqa_decode_int8: the
+    same codes, scales and lengths and the same output bits, step after step;
+    and the output within the bf16 bound of the oracle on the grown cache."""
+    note(f"int8 fused append B={B} H={H} K={K} d={d} lens={lens} s_max={s_max} steps={steps}")
+    inp, kc, vc, ks, vs = _int8_case(B, H, K, d, lens, seed=83, s_max=s_max)
+    S = kc.shape[2]
+    msl = min(max(lens) + steps, S)
+    fused = [t.to(DEV) for t in (kc, vc, ks, vs, inp["seq_lens"])]
+    split = [t.clone() for t in fused]
+    ref = [t.numpy().copy() for t in (kc, vc, ks, vs, inp["seq_lens"])]
+    nbytes = gqa.gqa_decode_workspace_bytes(B, H, K, msl, d)
+    ws_f = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    ws_s = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    g = torch.Generator().manual_seed(84)
+    for step in range(steps):
+        q = torch.randn((B, H, d), generator=g).to(torch.bfloat16)
+        kn = (torch.randn((B, K, d), generator=g) * 2).to(torch.bfloat16)
+        vn = torch.randn((B, K, d), generator=g).to(torch.bfloat16)
+        out_f = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+        out_s = torch.empty_like(out_f)
+        qd, knd, vnd = q.to(DEV), kn.to(DEV), vn.to(DEV)
+        gqa.gqa_decode_append_int8(qd, knd, vnd, *fused, out_f, ws_f, msl, scale=scale_of(d))
+        gqa.gqa_kv_append_int8(knd, vnd, *split)
+        gqa.gqa_decode_int8(qd, *split[:4], split[4], out_s, ws_s, msl, scale=scale_of(d))
+        torch.cuda.synchronize()
+        ref = list(kv_append_int8_ref(kn.float().numpy(), vn.float().numpy(), *ref))
+        got = [t.cpu().numpy() for t in fused]
+        assert got[4].tolist() == split[4].cpu().tolist() == list(ref[4])
+        for a, s2, r in zip(got[:2], split[:2], ref[:2]):
+            assert np.array_equal(a, s2.cpu().numpy()) and np.array_equal(a, r)
+        for a, s2, r in zip(got[2:4], split[2:4], ref[2:4]):
+            u = a.view(np.uint32)
+            assert np.array_equal(u, s2.cpu().numpy().view(np.uint32)) and np.array_equal(u, r.view(np.uint32))
+        assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+        o_ref = decode_int8_ref(f64(q), ref[0], ref[1], ref[2], ref[3], ref[4], scale_of(d))
+        r = report(f"int8 fused step {step}", f64(out_f), o_ref)
+        assert r["finite"] and r["max_abs"] <= bf16_bound(o_ref, _vmax(torch.from_numpy(ref[1]),
+                                                                       torch.from_numpy(ref[3]), ref[4]))
