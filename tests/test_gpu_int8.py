@@ -83,6 +83,9 @@ def _vmax(vc, vs, lens):
     return max(float(np.abs(v[b, :, :L]).max()) if L else 0.0 for b, L in enumerate(lens))
 
 
+# a large ragged batch (>= 256 sequence-head units), lengths 0..600
+RAGGED_40 = [0, 1, 600] + [int(x) for x in np.random.RandomState(5).randint(0, 601, 37)]
+
 CASES = [
     # B, H, K, d, lens
     (3, 32, 8, 128, [1, 33, 1000]),
@@ -92,6 +95,7 @@ CASES = [
     (2, 8, 8, 128, [2, 97]),           # K = H (MHA)
     (2, 32, 1, 128, [129, 4100]),      # K = 1 (MQA), G = 32
     (1, 71, 1, 64, [257]),             # G = 71: five head blocks
+    (40, 16, 8, 64, RAGGED_40),        # 320 units: one-dimensional grid, partition slowest
 ]
 
 
@@ -215,6 +219,7 @@ FUSED_CASES = [
     (4, 32, 8, 128, [64, 3, 4, 95], None, 1),     # new row at chunk / scale-group edges
     (3, 32, 8, 128, [12, 5, 12], 12, 1),          # full caches: no append
     (2, 32, 8, 128, [60, 3], 64, 8),              # eight steps; the first cache fills up
+    (40, 16, 8, 64, RAGGED_40, None, 2),          # 320 units: one-dimensional grid
 ]
 
 
