@@ -12,8 +12,9 @@ A step is one pass of the whole decode hot path over one batch: append the
 new token's K/V rows of every sequence and attend over the cache including
 them (gqa_decode_append: the append fused into the partition pass, then the
 combine pass -- the same work as gqa_kv_append followed by gqa_decode).  A
-paged workload (decode_paged_llama3_8b) runs gqa_kv_append_paged and then
-gqa_decode_paged over 16-row blocks in shuffled physical order; an int8
+paged workload (decode_paged_llama3_8b) runs gqa_decode_append_paged (the
+append through the block table fused into the paged decode) over 16-row
+blocks in shuffled physical order; an int8
 workload (decode_int8_llama3_8b) runs gqa_decode_append_int8 (the
 quantising append fused into the int8 partition pass) over the cache
 quantised once before timing (bytes counted as stored: d codes + one fp32
@@ -225,12 +226,14 @@ def bench_decode(args, w):
                                        max_len, scale=scale, stream=stream)
             host_lens[i % R] += 1
         elif paged:
-            # append through the block table, then decode (three kernel launches)
             if w.append:
-                gqa.gqa_kv_append_paged(kn, vn, c["k"], c["v"], bt, c["sl"], stream=stream)
+                # append through the block table fused into the paged decode (two launches)
+                gqa.gqa_decode_append_paged(q, kn, vn, c["k"], c["v"], bt, c["sl"], out, ws, max_len,
+                                            scale=scale, stream=stream)
                 host_lens[i % R] += 1
-            gqa.gqa_decode_paged(q, c["k"], c["v"], bt, c["sl"], out, ws, max_len, scale=scale,
-                                 stream=stream)
+            else:
+                gqa.gqa_decode_paged(q, c["k"], c["v"], bt, c["sl"], out, ws, max_len, scale=scale,
+                                     stream=stream)
         elif w.append:
             # append + decode as one fused call (two kernel launches)
             gqa.gqa_decode_append(q, kn, vn, c["k"], c["v"], c["sl"], out, ws, max_len,

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     gqa_decode,
     gqa_decode_append,
     gqa_decode_append_int8,
+    gqa_decode_append_paged,
     gqa_decode_int8,
     gqa_decode_paged,
     gqa_decode_paged_workspace_bytes,

@@ -40,6 +40,7 @@ _SIGNATURES = {
     "gqa_kv_append_paged": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_void_p]),
     "gqa_decode_paged_workspace_bytes": (_c_size_t, [_c_int] * 6),
     "gqa_decode_paged": (_c_int, [_c_void_p] * 7 + [_c_size_t] + [_c_int] * 8 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_decode_append_paged": (_c_int, [_c_void_p] * 9 + [_c_size_t] + [_c_int] * 8 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_kv_quantize_int8": (_c_int, [_c_void_p] * 3 + [_c_int64, _c_int, _c_int, _c_void_p]),
     "gqa_kv_append_int8": (_c_int, [_c_void_p] * 7 + [_c_int] * 5 + [_c_void_p]),
     "gqa_decode_int8": (_c_int, [_c_void_p] * 8 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
@@ -324,6 +325,33 @@ def gqa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, out, workspace, m
         seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K,
         num_blocks, block_size, block_table.shape[1], int(max_seq_len), d, float(scale),
         _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
+
+
+def gqa_decode_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, out, workspace,
+                            max_seq_len: int, scale: float | None = None, stream=None) -> None:
+    """gqa_kv_append_paged followed by gqa_decode_paged, fused into two kernel
+    launches.  max_seq_len bounds the lengths after the append."""
+    _need(q, "q", 3, (torch.bfloat16,))
+    _need_paged(k_pool, v_pool, block_table, seq_lens)
+    _need(out, "out", 3)
+    _need(workspace, "workspace", 1, (torch.uint8,))
+    B, H, d = q.shape
+    num_blocks, K, block_size, dk = k_pool.shape
+    if dk != d or block_table.shape[0] != B or tuple(out.shape) != (B, H, d):
+        raise ValueError("shape mismatch between q, pools, block_table and out")
+    if k_pool.dtype != q.dtype:
+        raise ValueError("q and pools must share a dtype")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, 3, (torch.bfloat16,))
+        if tuple(t.shape) != (B, K, d):
+            raise ValueError(f"{nm} must be [B,K,d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check("gqa_decode_append_paged", load_library().gqa_decode_append_paged(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel(), B, H, K, num_blocks, block_size, block_table.shape[1], int(max_seq_len), d,
+        float(scale), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def gqa_kv_quantize_int8(src, codes, scales, stream=None) -> None:

@@ -64,11 +64,13 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 }
 
 // APPEND: fused cache append.  The step's new K/V rows (k_new, v_new) sit at
-// position L_in = seq_lens[b] (when the cache has room): the partition that
-// covers it reads that row from k_new/v_new and writes it into the cache
-// (head block 0 only; nothing else reads that row in this launch), and the
-// lengths after the append go to `lens_out` for the combine pass, which
-// publishes them to seq_lens.
+// position L_in = seq_lens[b] (when the cache has room -- paged: when L_in is
+// below the table's capacity and the block id at L_in is a valid one, the
+// standalone paged append's rule): the partition that covers it reads that
+// row from k_new/v_new and writes it into the cache (head block 0 only;
+// nothing else reads that row in this launch), and the lengths after the
+// append go to `lens_out` for the combine pass, which publishes them to
+// seq_lens.
 //
 // PAGED: kc/vc are block pools [num_blocks, K, block_size, D] and position j
 // of sequence b lives in physical block block_table[b][j / block_size], row
@@ -84,7 +86,6 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
     float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
     int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
     const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, PagedArgs pg, int p_slowest) {
-  static_assert(!(APPEND && PAGED), "fused append is for contiguous caches");
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;        // contraction steps of Q.K
   constexpr int NTILES = D / 16;        // 16-wide output tiles of P.V
@@ -117,10 +118,16 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   const int k = y / head_blocks;
   const int hb = y - k * head_blocks;
   const int G = H / K;
-  const int L_in = PAGED ? min(seq_lens[b], pg.max_blocks * pg.block_size) : seq_lens[b];
+  const int cap = PAGED ? pg.max_blocks * pg.block_size : S_max;  // positions the cache holds
+  const int L_in = PAGED ? min(seq_lens[b], cap) : seq_lens[b];
   int L = L_in, newpos = -1;
   if (APPEND) {
-    if (L_in < S_max) {
+    bool room = L_in >= 0 && L_in < cap;
+    if (PAGED && room) {
+      const int id = pg.block_table[(size_t)b * pg.max_blocks + L_in / pg.block_size];
+      room = id >= 0 && id < pg.num_blocks;
+    }
+    if (room) {
       newpos = L_in;
       L = L_in + 1;
     }
@@ -269,10 +276,14 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
     __syncthreads();  // LDS reads done before the next chunk overwrites vt
   }
 
-  if (APPEND && hb == 0 && newpos >= t0 && newpos < t1 && lane < LANES_PER_ROW) {
+  if (APPEND && hb == 0 && newpos >= t0 && newpos < t1) {  // wave-uniform
     // the appended rows join the cache (bit copy)
-    *reinterpret_cast<u32x4*>(kbase + (size_t)newpos * D + 8 * lane) = ld16(knew_row + 8 * lane);
-    *reinterpret_cast<u32x4*>(vbase + (size_t)newpos * D + 8 * lane) = ld16(vnew_row + 8 * lane);
+    __bf16* kdst = row_of(kbase, newpos, newpos);
+    __bf16* vdst = row_of(vbase, newpos, newpos);
+    if (lane < LANES_PER_ROW) {
+      *reinterpret_cast<u32x4*>(kdst + 8 * lane) = ld16(knew_row + 8 * lane);
+      *reinterpret_cast<u32x4*>(vdst + 8 * lane) = ld16(vnew_row + 8 * lane);
+    }
   }
 
   // ---- write the partition's partial state ----
@@ -319,9 +330,11 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                      seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts, \
                      plan.head_blocks, scale_log2, kn, vn, ws.lens, pg, p_slowest ? 1 : 0)
 #define GQA_SPLIT_D(DD)                                                                           \
-  if (paged) GQA_SPLIT(DD, false, true);                                                          \
-  else if (k_new) GQA_SPLIT(DD, true, false);                                                     \
-  else GQA_SPLIT(DD, false, false);
+  if (paged) {                                                                                    \
+    if (k_new) GQA_SPLIT(DD, true, true); else GQA_SPLIT(DD, false, true);                        \
+  } else {                                                                                        \
+    if (k_new) GQA_SPLIT(DD, true, false); else GQA_SPLIT(DD, false, false);                      \
+  }
   if (d == 128) {
     GQA_SPLIT_D(128)
   } else {

@@ -277,11 +277,13 @@ size_t gqa_decode_paged_workspace_bytes(int B, int H, int K, int max_seq_len, in
   return gqa::decode_workspace_bytes(p, B, H, d);
 }
 
-int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
-                     const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
-                     int B, int H, int K, int num_blocks, int block_size, int max_blocks,
-                     int max_seq_len, int d, float scale, int dtype, int out_dtype, void* stream) {
-  const char* fn = "gqa_decode_paged";
+// Shared body of gqa_decode_paged and gqa_decode_append_paged (k_new == nullptr: no append).
+static int decode_paged_impl(const char* fn, const void* q, const void* k_new, const void* v_new,
+                             void* k_pool, void* v_pool, const int32_t* block_table,
+                             int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
+                             int B, int H, int K, int num_blocks, int block_size, int max_blocks,
+                             int max_seq_len, int d, float scale, int dtype, int out_dtype,
+                             void* stream) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out)
     return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
   if (int r = validate_heads(fn, B, H, K, d)) return r;
@@ -294,6 +296,7 @@ int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, cons
   if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
     return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out) ||
+      (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u))
     return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
   const gqa::DecodePlan plan =
@@ -308,16 +311,38 @@ int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, cons
   int r;
   {
     TimedRegion timed(s);
-    r = check_hip(gqa::launch_decode_split_bf16(q, const_cast<void*>(k_pool), const_cast<void*>(v_pool),
-                                                seq_lens, ws, plan, B, H, K, max_blocks * block_size, d,
-                                                scale * gqa::kLog2eHost, nullptr, nullptr, &pg, s),
+    r = check_hip(gqa::launch_decode_split_bf16(q, k_pool, v_pool, seq_lens, ws, plan, B, H, K,
+                                                max_blocks * block_size, d, scale * gqa::kLog2eHost,
+                                                k_new, v_new, &pg, s),
                   "partition-pass launch");
   }
   if (r) return r;
-  r = check_hip(gqa::launch_decode_combine(ws, const_cast<int32_t*>(seq_lens), out, plan, B, H, d,
-                                           out_dtype == GQA_BF16, false, s),
+  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16,
+                                           k_new != nullptr, s),
                 "combine-pass launch");
   return r ? r : ok();
+}
+
+int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                     const int32_t* seq_lens, void* out, void* workspace, size_t workspace_bytes,
+                     int B, int H, int K, int num_blocks, int block_size, int max_blocks,
+                     int max_seq_len, int d, float scale, int dtype, int out_dtype, void* stream) {
+  // read-only use of the pools and lengths (no append)
+  return decode_paged_impl("gqa_decode_paged", q, nullptr, nullptr, const_cast<void*>(k_pool),
+                           const_cast<void*>(v_pool), block_table, const_cast<int32_t*>(seq_lens),
+                           out, workspace, workspace_bytes, B, H, K, num_blocks, block_size,
+                           max_blocks, max_seq_len, d, scale, dtype, out_dtype, stream);
+}
+
+int gqa_decode_append_paged(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                            void* v_pool, const int32_t* block_table, int32_t* seq_lens, void* out,
+                            void* workspace, size_t workspace_bytes, int B, int H, int K,
+                            int num_blocks, int block_size, int max_blocks, int max_seq_len, int d,
+                            float scale, int dtype, int out_dtype, void* stream) {
+  if (!k_new || !v_new) return fail(GQA_ERR_INVALID, "gqa_decode_append_paged: null pointer");
+  return decode_paged_impl("gqa_decode_append_paged", q, k_new, v_new, k_pool, v_pool, block_table,
+                           seq_lens, out, workspace, workspace_bytes, B, H, K, num_blocks,
+                           block_size, max_blocks, max_seq_len, d, scale, dtype, out_dtype, stream);
 }
 
 int gqa_kv_quantize_int8(const void* src, void* codes, float* scales, int64_t rows, int d, int dtype,

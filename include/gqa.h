@@ -179,6 +179,27 @@ int gqa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                      float scale, int dtype, int out_dtype, void* stream);
 
 /*
+ * One paged decode step with the append fused in: the result of
+ * gqa_kv_append_paged(k_new, v_new, ...) followed by gqa_decode_paged(q, ...)
+ * on the grown cache -- the same pools, lengths and output bits -- in one
+ * partition pass and one combine pass.  The append rule is the standalone
+ * one: a sequence with L = seq_lens[b] < max_blocks * block_size whose block
+ * id block_table[b, L / block_size] lies in [0, num_blocks) gets the row at
+ * L and L + 1; any other sequence is attended as it is.  (pinghaoyang.com.cn
+ * "GQA 完全拆解", decode memory ledger: each step appends one K and V row per
+ * KV head and reads the cache; compassingai.com "分組查詢注意力", downstream
+ * schedulers: paged blocks hold K * s rows.)  q, k_new, v_new bf16 ([B, H,
+ * d] and [B, K, d]; dtype must be GQA_BF16); max_seq_len bounds the lengths
+ * *after* the append.  Other arguments, alignment and workspace
+ * (gqa_decode_paged_workspace_bytes) as gqa_decode_paged.
+ */
+int gqa_decode_append_paged(const void* q, const void* k_new, const void* v_new, void* k_pool,
+                            void* v_pool, const int32_t* block_table, int32_t* seq_lens, void* out,
+                            void* workspace, size_t workspace_bytes, int B, int H, int K,
+                            int num_blocks, int block_size, int max_blocks, int max_seq_len, int d,
+                            float scale, int dtype, int out_dtype, void* stream);
+
+/*
  * int8 KV cache.  Codes k_codes, v_codes are int8 [B, K, S_max, d]; scales
  * k_scales, v_scales are float [B, K, S_max], one per cached row; row
  * (b, k, j) reads back as codes[b, k, j, i] * scales[b, k, j].  The pages

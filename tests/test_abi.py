@@ -181,6 +181,32 @@ def test_decode_paged_rejects(lib, kw, code):
     assert lib.gqa_last_error().decode().startswith("gqa_decode_paged")
 
 
+def _decode_append_paged(lib, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30, B=2,
+             H=32, K=8, num_blocks=64, block_size=16, max_blocks=8, max_seq_len=128, d=128, scale=0.088,
+             dtype=B.GQA_BF16, out_dtype=B.GQA_BF16)
+    a.update(kw)
+    return lib.gqa_decode_append_paged(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["bt"], a["sl"], a["out"],
+                                       a["ws"], a["wsb"], a["B"], a["H"], a["K"], a["num_blocks"],
+                                       a["block_size"], a["max_blocks"], a["max_seq_len"], a["d"], a["scale"],
+                                       a["dtype"], a["out_dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), B.GQA_ERR_INVALID),
+    (dict(vn=None), B.GQA_ERR_INVALID),
+    (dict(kn=FAKE + 8), B.GQA_ERR_INVALID),
+    (dict(bt=None), B.GQA_ERR_INVALID),
+    (dict(block_size=24), B.GQA_ERR_UNSUPPORTED),
+    (dict(max_seq_len=129), B.GQA_ERR_INVALID),
+    (dict(dtype=B.GQA_F32, out_dtype=B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    (dict(wsb=64), B.GQA_ERR_WORKSPACE),
+])
+def test_decode_append_paged_rejects(lib, kw, code):
+    assert _decode_append_paged(lib, **kw) == code
+    assert lib.gqa_last_error().decode().startswith("gqa_decode_append_paged")
+
+
 def test_paged_workspace_bytes(lib):
     # partitions are capped at 63 blocks, so a long context with few heads
     # needs more partial rows than the contiguous plan

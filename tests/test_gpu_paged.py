@@ -198,3 +198,82 @@ def test_paged_full_workload():
     r = report("paged llama3_8b", f64(out), ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
     assert r["max_abs"] <= bf16_bound(ref, _vmax(p["v_pool"]))
+
+
+FUSED_CASES = [
+    # B, H, K, d, lens, block_size, s_max, steps
+    (3, 32, 8, 128, [1, 33, 1000], 16, None, 1),
+    (4, 64, 8, 128, [0, 16, 17, 3000], 16, None, 1),
+    (2, 16, 4, 64, [31, 2100], 32, None, 1),
+    (2, 32, 1, 128, [129, 4100], 48, None, 1),       # G = 32: two head blocks
+    (1, 71, 1, 64, [257], 16, None, 1),              # G = 71: five head blocks
+    (40, 8, 8, 64, [8000 + 37 * i for i in range(40)], 16, None, 1),  # 62-block partitions, 320 units
+    (2, 32, 8, 128, [60, 3], 16, 64, 8),             # eight steps; the first table fills up
+]
+
+
+def _fused_vs_unfused(inp, p, bt, lens_in, steps, seed):
+    """Run `steps` decode steps through gqa_decode_append_paged and through
+    gqa_kv_append_paged + gqa_decode_paged on copies of the same pools: the
+    pools, lengths and output bits must agree every step, and the output
+    must be within the bf16 bound of the oracle on the grown cache."""
+    B, H, d = inp["q"].shape
+    K, bs = p["k_pool"].shape[1], p["block_size"]
+    cap = bt.shape[1] * bs
+    msl = min(max(lens_in) + steps, cap)
+    fused = [p["k_pool"].to(DEV), p["v_pool"].to(DEV), torch.tensor(lens_in, dtype=torch.int32, device=DEV)]
+    split = [t.clone() for t in fused]
+    ref = [p["k_pool"].view(torch.int16).numpy().copy(), p["v_pool"].view(torch.int16).numpy().copy(),
+           np.array(lens_in, dtype=np.int32)]
+    btd = bt.to(DEV)
+    nbytes = gqa.gqa_decode_paged_workspace_bytes(B, H, K, msl, d, bs)
+    ws_f = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    ws_s = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    g = torch.Generator().manual_seed(seed)
+    for step in range(steps):
+        q = torch.randn((B, H, d), generator=g).to(torch.bfloat16)
+        kn = torch.randn((B, K, d), generator=g).to(torch.bfloat16)
+        vn = torch.randn((B, K, d), generator=g).to(torch.bfloat16)
+        qd, knd, vnd = q.to(DEV), kn.to(DEV), vn.to(DEV)
+        out_f = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+        out_s = torch.empty_like(out_f)
+        gqa.gqa_decode_append_paged(qd, knd, vnd, fused[0], fused[1], btd, fused[2], out_f, ws_f, msl,
+                                    scale=scale_of(d))
+        gqa.gqa_kv_append_paged(knd, vnd, split[0], split[1], btd, split[2])
+        gqa.gqa_decode_paged(qd, split[0], split[1], btd, split[2], out_s, ws_s, msl, scale=scale_of(d))
+        torch.cuda.synchronize()
+        ref = list(kv_append_paged_ref(kn.view(torch.int16).numpy(), vn.view(torch.int16).numpy(), ref[0], ref[1],
+                                       bt.numpy(), ref[2]))
+        assert fused[2].cpu().tolist() == split[2].cpu().tolist() == list(ref[2])
+        for i in range(2):
+            a = fused[i].cpu().view(torch.int16).numpy()
+            assert np.array_equal(a, split[i].cpu().view(torch.int16).numpy()) and np.array_equal(a, ref[i])
+        assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+        kf = torch.from_numpy(ref[0]).view(torch.bfloat16)
+        vf = torch.from_numpy(ref[1]).view(torch.bfloat16)
+        o_ref = decode_paged_ref(f64(q), _np(kf), _np(vf), bt.numpy(), ref[2], scale_of(d))
+        r = report(f"paged fused step {step}", f64(out_f), o_ref)
+        assert r["finite"] and r["max_abs"] <= bf16_bound(o_ref, _vmax(vf))
+
+
+@pytest.mark.parametrize("B,H,K,d,lens,bs,s_max,steps", FUSED_CASES)
+def test_paged_fused_append_matches_unfused(B, H, K, d, lens, bs, s_max, steps):
+    note(f"paged fused append B={B} H={H} K={K} d={d} max_len={max(lens)} bs={bs} steps={steps}")
+    inp = decode_inputs(B, H, K, d, "bf16", seed=71, lens=lens, s_max=s_max or max(lens) + steps)
+    p = paged_layout(inp, bs, seed=72, spare_blocks=2)
+    _fused_vs_unfused(inp, p, p["block_table"], lens, steps, seed=73)
+
+
+def test_paged_fused_append_full_table_and_invalid_id():
+    """A full table and an invalid block id at the append position: that
+    sequence is attended as it is and keeps its length, as in the
+    standalone append."""
+    B, H, K, d, bs = 4, 32, 8, 128, 16
+    lens = [0, 15, 32, 48]
+    inp = decode_inputs(B, H, K, d, "bf16", seed=74, lens=lens, s_max=48)
+    p = paged_layout(inp, bs, seed=75, spare_blocks=1)
+    assert p["block_table"].shape[1] * bs == 48  # sequence 3: table full
+    bt = p["block_table"].clone()
+    bt[2, 32 // bs] = -5                         # invalid id where sequence 2 would append
+    note("paged fused append: full table + invalid id")
+    _fused_vs_unfused(inp, p, bt, lens, 2, seed=76)
