@@ -1,6 +1,6 @@
 """Build libgqa.so (the HIP kernels + C ABI) in-tree for gfx950.
 
-    python -m grouped_query_kv_amd.build        # or __graft_entry__.build()
+    python -m grouped_query_kv_amd.build
 
 Every .hip file under csrc/ is compiled with hipcc for gfx950 and the objects
 are linked into grouped_query_kv_amd/libgqa.so.  Packed fp32 instructions are
