@@ -547,6 +547,80 @@ def cpu_baseline_project(inp, w, budget_s):
             "sample": f"{steps} whole projection steps, {t_used:.1f} s of fp64 NumPy on {cores} BLAS threads"}
 
 
+def bench_meanpool(args, w):
+    """Mean-pool conversion of one projection weight per step ([outer, H,
+    inner] -> [outer, K, inner]); the weights of a 24-layer checkpoint's K and
+    V projections (48 matrices, 1.6 GB) are visited in turn, so every step
+    reads its source from HBM."""
+    import grouped_query_kv_amd as gqa
+    from grouped_query_kv_amd.inputs import meanpool_inputs
+
+    dev = torch.device("cuda:0")
+    inner = w.d * w.extra["d_model"]
+    t_gen = time.perf_counter()
+    src0 = meanpool_inputs(1, w.H, inner, w.dtype, seed=args.seed)
+    t_gen = time.perf_counter() - t_gen
+    n = w.extra["matrices"]
+    srcs = [src0.to(dev)]
+    srcs += [srcs[0].clone() for _ in range(n - 1)]
+    dsts = [torch.empty((1, w.K, inner), dtype=src0.dtype, device=dev) for _ in range(n)]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        if ev is not None:
+            gqa.gqa_set_timing_events(*ev)
+        gqa.gqa_meanpool_convert(srcs[i % n], dsts[i % n], stream=stream)
+        if ev is not None:
+            gqa.gqa_set_timing_events(None, None)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [(gqa.HipEvent(), gqa.HipEvent()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, ev in enumerate(events):
+        step(args.warmup + i, ev)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = [a.elapsed_ms(b) for a, b in events]
+    kern_ms = float(np.mean(kern))
+    eb = src0.element_size()
+    byts = (w.H + w.K) * inner * eb          # every source element read once, every output written once
+    ms_per_step = elapsed * 1e3 / args.steps
+    res = {
+        "metric": "GQA mean-pool conversion GB/s (bytes read + written), 1\u00d7MI355X",
+        "value": round(byts / (ms_per_step * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "outer": 1, "H": w.H, "K": w.K, "inner": inner, "matrices": n,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "mean-pool conversion (meanpool_vec_kernel)", "bound": "hbm",
+                     "achieved": round(byts / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(byts / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_kernel_us": round(kern_ms * 1e3, 3),
+                     "kernel_us_p10_p50_p90": [round(float(x) * 1e3, 2) for x in np.percentile(kern, [10, 50, 90])]},
+        "input_gen_s": round(t_gen, 1),
+    }
+    return res, src0
+
+
+def cpu_baseline_meanpool(src, w, budget_s):
+    """The oracle's conversion of whole matrices on the host, repeated for
+    about `budget_s` seconds."""
+    from oracle import meanpool_convert_ref
+
+    x = src.double().numpy()
+    byts = (w.H + w.K) * x.shape[2] * src.element_size()
+    mats, t_used = 0, 0.0
+    while t_used < budget_s:
+        t0 = time.perf_counter()
+        meanpool_convert_ref(x, w.K)
+        t_used += time.perf_counter() - t0
+        mats += 1
+    return {"value": mats * byts / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{mats} whole matrices, {t_used:.1f} s of fp64 NumPy (element-wise: one thread)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -556,7 +630,11 @@ def main():
     from grouped_query_kv_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    if w.kind == "project":
+    if w.kind == "meanpool":
+        res, inp = bench_meanpool(args, w)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline_meanpool(inp, w, args.cpu_seconds)
+    elif w.kind == "project":
         res, inp = bench_project(args, w)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline_project(inp, w, args.cpu_seconds)

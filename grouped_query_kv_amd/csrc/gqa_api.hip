@@ -584,9 +584,13 @@ int gqa_meanpool_convert(const void* src, void* dst, int64_t outer, int H, int K
   if (K > H || H % K) return fail(GQA_ERR_INVALID, "gqa_meanpool_convert: H=%d not a multiple of K=%d", H, K);
   if (!elem_bytes(dtype)) return fail(GQA_ERR_UNSUPPORTED, "gqa_meanpool_convert: dtype %d", dtype);
   if (!aligned16(src) || !aligned16(dst)) return fail(GQA_ERR_INVALID, "gqa_meanpool_convert: misaligned pointer");
-  const int r = check_hip(gqa::launch_meanpool(src, dst, outer, H, K, inner, dtype == GQA_BF16,
-                                               static_cast<hipStream_t>(stream)),
-                          "gqa_meanpool_convert launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int r;
+  {
+    TimedRegion timed(s);
+    r = check_hip(gqa::launch_meanpool(src, dst, outer, H, K, inner, dtype == GQA_BF16, s),
+                  "gqa_meanpool_convert launch");
+  }
   return r ? r : ok();
 }
 

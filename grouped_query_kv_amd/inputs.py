@@ -34,7 +34,7 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str               # "decode", "prefill", "chunk", "cross" or "project"
+    kind: str               # "decode", "prefill", "chunk", "cross", "project" or "meanpool"
     B: int
     H: int
     K: int
@@ -80,6 +80,11 @@ WORKLOADS = {
         "kv_project_llama3_8b", "project", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
         note="fused K/V projection of one decode token per sequence, d_model 4096, appended at 8192",
         extra={"d_model": 4096, "T": 1}),
+    "meanpool_t5xxl": Workload(
+        "meanpool_t5xxl", "meanpool", B=1, H=64, K=8, d=64, dtype="bf16",
+        note="mean-pool conversion of a T5-XXL-shaped projection weight [64 heads x d_k 64, d_model 4096] "
+             "to 8 KV heads (outer 1, inner d_k * d_model = 262144)",
+        extra={"d_model": 4096, "matrices": 48}),
     "prefill_causal_4k": Workload(
         "prefill_causal_4k", "prefill", B=2, H=64, K=8, d=128, dtype="bf16", L=4096,
         note="causal prefill, S=4096, 64 query heads over 8 KV heads"),

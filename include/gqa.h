@@ -368,10 +368,12 @@ int gqa_meanpool_convert(const void* src, void* dst, int64_t outer, int H, int K
 uint64_t gqa_kv_cache_bytes(int layers, int K, int d, int elem_bytes, uint64_t tokens);
 
 /*
- * Benchmark timing hook.  While set (both non-NULL), gqa_decode,
- * gqa_decode_append and gqa_prefill_causal record `begin_event` on their stream immediately before
- * launching their main kernel and `end_event` immediately after it; the
- * events are hipEvent_t handles passed as void*, owned by the caller.
+ * Benchmark timing hook.  While set (both non-NULL), the decode entry
+ * points (around their partition pass), the prefill family, the projection
+ * entry points and the mean-pool conversion record `begin_event` on their
+ * stream immediately before launching that kernel and `end_event`
+ * immediately after it; the events are hipEvent_t handles passed as void*,
+ * owned by the caller.  The append-only entry points record nothing.
  * Applies to calls from the calling thread only; pass NULLs to clear.
  */
 int gqa_set_timing_events(void* begin_event, void* end_event);

@@ -93,3 +93,49 @@ def test_meanpool_g1_identity():
     gqa.gqa_meanpool_convert(src.to(DEV), dst)
     torch.cuda.synchronize()
     assert torch.equal(dst.cpu(), src)
+
+
+def _fp32_rule(src: torch.Tensor, K: int) -> torch.Tensor:
+    """The conversion's stated rounding rule on the host: fp32 sum over the
+    group's heads in head order, one IEEE fp32 division by G, then rounding
+    to the element type."""
+    x = src.float().numpy()
+    outer, H, inner = x.shape
+    G = H // K
+    xs = x.reshape(outer, K, G, inner)
+    s = np.zeros((outer, K, inner), dtype=np.float32)
+    for r in range(G):
+        s = s + xs[:, :, r]
+    return torch.from_numpy(s / np.float32(G)).to(src.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("outer,H,K,inner", [(2, 64, 8, 4104), (1, 71, 1, 1024), (3, 24, 2, 8), (4, 6, 3, 5)])
+def test_meanpool_rounding_rule_bit_exact(dtype, outer, H, K, inner):
+    """Bit for bit the stated rule, on shapes covering more than one block of
+    eight heads with a ragged tail (G = 71), tiny rows and the unvectorised
+    path (inner not a multiple of the 16-byte word)."""
+    src = meanpool_inputs(outer, H, inner, dtype, seed=32)
+    dst = torch.empty((outer, K, inner), dtype=src.dtype, device=DEV)
+    note(f"meanpool rule {dtype} {outer}x{H}->{K}x{inner}")
+    gqa.gqa_meanpool_convert(src.to(DEV), dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), _fp32_rule(src, K))
+
+
+def test_meanpool_full_workload():
+    """The T5-XXL-shaped projection weight the benchmark converts: against
+    the oracle (bound as above) and bit for bit against the stated rule."""
+    from grouped_query_kv_amd.inputs import WORKLOADS
+    w = WORKLOADS["meanpool_t5xxl"]
+    inner = w.d * w.extra["d_model"]
+    src = meanpool_inputs(1, w.H, inner, w.dtype, seed=0)
+    dst = torch.empty((1, w.K, inner), dtype=src.dtype, device=DEV)
+    note("meanpool full workload")
+    gqa.gqa_meanpool_convert(src.to(DEV), dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.cpu(), _fp32_rule(src, w.K))
+    ref = meanpool_convert_ref(f64(src), w.K)
+    got = f64(dst)
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-6 * float(np.abs(f64(src)).max())
+    assert np.all(np.abs(got - ref) <= bound)
