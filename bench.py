@@ -66,9 +66,10 @@ def parse():
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per launch recorded from rocprofv3 counters for `kernel`
-    (profiles/traffic.json), or None when the kernel's sources changed since."""
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch recorded from rocprofv3 counters for `kernel` on
+    `workload` (profiles/traffic.json), or None when nothing was recorded for
+    that pair or the kernel's sources changed since."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -76,6 +77,8 @@ def recorded_traffic(kernel: str):
         with open(path) as f:
             rec = json.load(f)[kernel]
     except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("workload") != workload:
         return None
     h = hashlib.sha256()
     for src in rec["sources"]:
@@ -113,7 +116,7 @@ def cpu_baseline_decode(inp, w, budget_s):
 
     paged = "block_size" in w.extra
     int8 = w.extra.get("kv_dtype") == "int8"
-    elem, row_extra = (1, 4) if int8 else (2, 0)
+    elem, row_extra = (1, 4) if int8 else ((4, 0) if w.dtype == "f32" else (2, 0))
     d = w.d
     scale = float(np.float32(1.0 / math.sqrt(d)))
     done_bytes, done_seqs, t_used = 0, 0, 0.0
@@ -180,7 +183,7 @@ def bench_decode(args, w):
     kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
     paged = "block_size" in w.extra
     int8 = w.extra.get("kv_dtype") == "int8"
-    elem, row_extra = (1, 4) if int8 else (2, 0)
+    elem, row_extra = (1, 4) if int8 else ((4, 0) if w.dtype == "f32" else (2, 0))
     copies = []
     if int8:
         # the workload's bf16 caches quantised once on the GPU (set-up, untimed)
@@ -212,7 +215,8 @@ def bench_decode(args, w):
                          dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, max_len, d), dtype=torch.uint8, device=dev)
-    out = torch.empty((B, H, d), dtype=torch.bfloat16, device=dev)
+    # fp32 caches produce fp32 outputs (the library's fp32 path), bf16 ones bf16
+    out = torch.empty((B, H, d), dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16, device=dev)
     scale = float(np.float32(1.0 / math.sqrt(d)))
     stream = torch.cuda.current_stream()
 
@@ -293,7 +297,7 @@ def bench_decode(args, w):
         "metric": "GQA decode KV-read GB/s (% of HBM peak) + attention tokens/s, 1\u00d7MI355X",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "K": K, "d": d,
                    "context": (int(w.L) if w.ragged is None else list(w.ragged)),
                    "append_per_step": bool(w.append), "cache_copies": R,
@@ -303,14 +307,18 @@ def bench_decode(args, w):
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(total_bytes / args.steps),
-        "roofline": {"kernel": ("int8 decode partition pass (decode_split_int8_kernel)" if int8 else
-                                "paged decode partition pass (decode_split_bf16_kernel, paged)" if paged else
-                                "decode partition pass with fused append (decode_split_bf16_kernel)"),
+        "roofline": {"kernel": ("int8 decode partition pass" + (" with fused append" if w.append else "") +
+                                " (decode_split_int8_kernel)" if int8 else
+                                "paged decode partition pass" + (" with fused append" if w.append else "") +
+                                " (decode_split_bf16_kernel, paged)" if paged else
+                                "fp32 decode partition pass (decode_split_f32_kernel)" if w.dtype == "f32" else
+                                "decode partition pass" + (" with fused append" if w.append else "") +
+                                " (decode_split_bf16_kernel)"),
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("decode_split_int8_kernel" if int8 else
-                                                 "decode_split_bf16_kernel" + ("_paged" if paged else "")),
+                                                 "decode_split_bf16_kernel" + ("_paged" if paged else ""), w.name),
                      "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled),
                      "kernel_us_p10_p50_p90": [round(p10 * 1e3, 2), round(p50 * 1e3, 2), round(p90 * 1e3, 2)],
                      "copy_ceiling_GBps": round(copy_gbs, 1),
@@ -456,7 +464,7 @@ def bench_prefill(args, w):
         "roofline": {"kernel": f"{w.kind} attention (prefill_kernel)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic("prefill_causal_kernel") if w.kind == "prefill" else None,
+                     "traffic": recorded_traffic("prefill_causal_kernel", w.name) if w.kind == "prefill" else None,
                      "avg_kernel_us": round(kern_ms * 1e3, 3)},
         "input_gen_s": round(t_gen, 1),
     }

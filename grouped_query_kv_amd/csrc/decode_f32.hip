@@ -7,13 +7,15 @@
 // matrix cores would round operands), which is what fp32 callers ask for.
 //
 // One 256-thread workgroup per (partition, KV head, head block, sequence);
-// positions are processed in chunks of 64:
-//   1. scores: thread (t, h0) dots position t's K row with heads h0, h0+4,
-//      h0+8, h0+12 (query rows broadcast from LDS);
+// positions are processed in chunks of CF (64 for d = 64, 32 for d = 128):
+//   0. the chunk's K and V rows are copied into LDS with every load of the
+//      chunk in flight at once (one memory round trip per chunk);
+//   1. scores: thread (t, hs) dots position t's K row with its heads
+//      (query rows broadcast from LDS);
 //   2. softmax: wave w updates (m, l) of heads w, w+4, w+8, w+12 with
 //      wavefront max/sum reductions, leaving probabilities in LDS;
 //   3. values: thread (dim c, head slice) accumulates p * V[t][c] for its
-//      heads, reading each V row coalesced.
+//      heads.
 // The group's K and V rows are read from memory once per workgroup and
 // serve every head of the block (pinghaoyang.com.cn "GQA 完全拆解", section
 // 工程实现: the group's KV block is loaded once for all its query heads).
@@ -24,7 +26,6 @@ namespace gqa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunkF = 64;
 constexpr int kHB = 16;  // heads per block
 
 // APPEND: fused cache append, as in decode_bf16.hip.
@@ -35,10 +36,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
     float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
     int head_blocks, float scale_log2, const float* __restrict__ k_new,
     const float* __restrict__ v_new, int32_t* __restrict__ lens_out) {
-  constexpr int HEADS_PER_THREAD = kHB * D / kThreads;  // 8 (D=128) or 4 (D=64)
+  constexpr int CF = D == 64 ? 64 : 32;                  // positions per chunk
+  constexpr int HEADS_PER_THREAD = kHB * D / kThreads;   // phase 3: 8 (D=128) or 4 (D=64)
+  constexpr int HPT1 = kHB * CF / kThreads;              // phase 1: 2 (D=128) or 4 (D=64)
+  constexpr int KROW = D + 4;  // padded K row: a 16-byte shift per row spreads the
+                               // phase-1 reads of consecutive rows over the banks
+  constexpr int ROW4 = D / 4;  // float4 per row
+  constexpr int LOADS = CF * ROW4 / kThreads;            // float4 per thread per tensor
 
-  __shared__ float qs[kHB][D];
-  __shared__ float ps[kHB][kChunkF];
+  __shared__ __attribute__((aligned(16))) float qs[kHB][D];
+  __shared__ __attribute__((aligned(16))) float ks[CF][KROW];
+  __shared__ __attribute__((aligned(16))) float vs[CF][D];
+  __shared__ __attribute__((aligned(16))) float ps[kHB][CF];
   __shared__ float alpha_s[kHB];
   __shared__ float m_s[kHB];
   __shared__ float l_s[kHB];
@@ -87,64 +96,119 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
   float acc[HEADS_PER_THREAD];
 #pragma unroll
   for (int j = 0; j < HEADS_PER_THREAD; ++j) acc[j] = 0.f;
-  __syncthreads();
 
-  for (int c0 = t0; c0 < t1; c0 += kChunkF) {
-    const int n_tok = min(kChunkF, t1 - c0);
+  for (int c0 = t0; c0 < t1; c0 += CF) {
+    const int n_tok = min(CF, t1 - c0);
+    // 0. stage the chunk's K and V rows (rows past the partition: zeros)
+    {
+      float4 kv4[LOADS], vv4[LOADS];
+#pragma unroll
+      for (int r = 0; r < LOADS; ++r) {
+        const int i = tid + r * kThreads;
+        const int row = i / ROW4, c4 = i - row * ROW4;
+        const int tok = c0 + row;
+        const bool ok = row < n_tok;
+        const float* kr = APPEND && tok == newpos ? knew_row : kbase + (size_t)tok * D;
+        const float* vr = APPEND && tok == newpos ? vnew_row : vbase + (size_t)tok * D;
+        kv4[r] = ok ? reinterpret_cast<const float4*>(kr)[c4] : float4{0.f, 0.f, 0.f, 0.f};
+        vv4[r] = ok ? reinterpret_cast<const float4*>(vr)[c4] : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int r = 0; r < LOADS; ++r) {
+        const int i = tid + r * kThreads;
+        const int row = i / ROW4, c4 = i - row * ROW4;
+        *reinterpret_cast<float4*>(&ks[row][4 * c4]) = kv4[r];
+        *reinterpret_cast<float4*>(&vs[row][4 * c4]) = vv4[r];
+      }
+    }
+    __syncthreads();
     // 1. scores
     {
-      const int t = tid & (kChunkF - 1);
-      const int h0 = tid / kChunkF;  // 0..3
-      float s[4] = {0.f, 0.f, 0.f, 0.f};
-      if (t < n_tok) {
-        const float* krow_p = APPEND && c0 + t == newpos ? knew_row : kbase + (size_t)(c0 + t) * D;
-        const float4* krow = reinterpret_cast<const float4*>(krow_p);
-#pragma unroll 4
-        for (int c4 = 0; c4 < D / 4; ++c4) {
-          const float4 kv = krow[c4];
+      const int t = tid % CF;
+      const int hs = tid / CF;  // heads hs, hs + 256/CF, ...
+      float s[HPT1];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float* qq = &qs[h0 + 4 * r][4 * c4];
-            s[r] = fmaf(kv.x, qq[0], s[r]);
-            s[r] = fmaf(kv.y, qq[1], s[r]);
-            s[r] = fmaf(kv.z, qq[2], s[r]);
-            s[r] = fmaf(kv.w, qq[3], s[r]);
-          }
+      for (int r = 0; r < HPT1; ++r) s[r] = 0.f;
+#pragma unroll 8
+      for (int c4 = 0; c4 < ROW4; ++c4) {
+        const float4 kv = *reinterpret_cast<const float4*>(&ks[t][4 * c4]);
+#pragma unroll
+        for (int r = 0; r < HPT1; ++r) {
+          const float* qq = &qs[hs + (kThreads / CF) * r][4 * c4];
+          s[r] = fmaf(kv.x, qq[0], s[r]);
+          s[r] = fmaf(kv.y, qq[1], s[r]);
+          s[r] = fmaf(kv.z, qq[2], s[r]);
+          s[r] = fmaf(kv.w, qq[3], s[r]);
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        ps[h0 + 4 * r][t] = t < n_tok ? s[r] * scale_log2 : -INFINITY;
+      for (int r = 0; r < HPT1; ++r)
+        ps[hs + (kThreads / CF) * r][t] = t < n_tok ? s[r] * scale_log2 : -INFINITY;
     }
     __syncthreads();
-    // 2. online softmax, wave w owns heads w, w+4, w+8, w+12
+    // 2. online softmax, wave w owns heads w, w+4, w+8, w+12 (lane = position);
+    // the four heads' reductions are interleaved (independent shuffle chains)
+    {
+      float x[4], mx[4], mnew[4], e[4], sum[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = wave + 4 * r;
-      const float x = ps[h][lane];
-      float mx = x;
+      for (int r = 0; r < 4; ++r) {
+        x[r] = lane < CF ? ps[wave + 4 * r][lane] : -INFINITY;
+        mx[r] = x[r];
+      }
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      const float m_old = m_s[h];
-      const float m_new = fmaxf(m_old, mx);
-      const float e = fast_exp2(x - m_new);
-      float sum = e;
+      for (int off = 32; off > 0; off >>= 1)
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-      ps[h][lane] = e;
+        for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], off));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mnew[r] = fmaxf(m_s[wave + 4 * r], mx[r]);
+        e[r] = fast_exp2(x[r] - mnew[r]);
+        sum[r] = e[r];
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sum[r] += __shfl_xor(sum[r], off);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (lane < CF) ps[wave + 4 * r][lane] = e[r];
       if (lane == 0) {
-        const float a = fast_exp2(m_old - m_new);
-        alpha_s[h] = a;
-        l_s[h] = l_s[h] * a + sum;
-        m_s[h] = m_new;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = wave + 4 * r;
+          const float a = fast_exp2(m_s[h] - mnew[r]);
+          alpha_s[h] = a;
+          l_s[h] = l_s[h] * a + sum[r];
+          m_s[h] = mnew[r];
+        }
       }
     }
     __syncthreads();
     // 3. values
 #pragma unroll
     for (int j = 0; j < HEADS_PER_THREAD; ++j) acc[j] *= alpha_s[slice * HEADS_PER_THREAD + j];
-    for (int t = 0; t < n_tok; ++t) {
-      const float v = APPEND && c0 + t == newpos ? vnew_row[c_own] : vbase[(size_t)(c0 + t) * D + c_own];
+    // eight positions per step, their LDS reads issued together
+    int t = 0;
+    for (; t + 8 <= n_tok; t += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = vs[t + u][c_own];
+#pragma unroll
+      for (int j = 0; j < HEADS_PER_THREAD; ++j) {
+        const float4 pa = *reinterpret_cast<const float4*>(&ps[slice * HEADS_PER_THREAD + j][t]);
+        const float4 pb = *reinterpret_cast<const float4*>(&ps[slice * HEADS_PER_THREAD + j][t + 4]);
+        acc[j] = fmaf(pa.x, v[0], acc[j]);
+        acc[j] = fmaf(pa.y, v[1], acc[j]);
+        acc[j] = fmaf(pa.z, v[2], acc[j]);
+        acc[j] = fmaf(pa.w, v[3], acc[j]);
+        acc[j] = fmaf(pb.x, v[4], acc[j]);
+        acc[j] = fmaf(pb.y, v[5], acc[j]);
+        acc[j] = fmaf(pb.z, v[6], acc[j]);
+        acc[j] = fmaf(pb.w, v[7], acc[j]);
+      }
+    }
+    for (; t < n_tok; ++t) {
+      const float v = vs[t][c_own];
 #pragma unroll
       for (int j = 0; j < HEADS_PER_THREAD; ++j)
         acc[j] = fmaf(ps[slice * HEADS_PER_THREAD + j][t], v, acc[j]);
