@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   const __bf16* vnew_row = APPEND ? v_new + ((size_t)b * K + k) * D : nullptr;
 
   float m_run = -INFINITY;  // running max of head n (replicated over g)
-  float l_run = 0.f;        // running sum of head n
+  float l_run = 0.f;        // this lane's share of the running sum of head n
   f32x4 acc[NTILES];
 #pragma unroll
   for (int t = 0; t < NTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -188,21 +188,28 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 
   u32x4 ka[2][KSTEPS];
   u32x4 vr[VLOADS];
+  // Rows past the partition are fetched from its last row instead (valid
+  // memory; their scores are masked and their weights are zero), so no load
+  // is predicated.  A clamped row stays in the clamped load group, so a
+  // paged group still lies in one block.
+  const int last = t1 - 1;
   auto load_k = [&](int c0) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int tok = c0 + 16 * mt + n;
-      const __bf16* krow = (APPEND && tok == newpos ? knew_row : row_of(kbase, c0 + 16 * mt, tok)) + 8 * g;
+      const int tok0 = min(c0 + 16 * mt, last & ~15);
+      const int tok = min(c0 + 16 * mt + n, last);
+      const __bf16* krow = (APPEND && tok == newpos ? knew_row : row_of(kbase, tok0, tok)) + 8 * g;
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = tok < t1 ? ld16_stream(krow + 32 * s) : zero_u32x4();
+      for (int s = 0; s < KSTEPS; ++s) ka[mt][s] = ld16_stream(krow + 32 * s);
     }
   };
   auto load_v = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int tok = c0 + i * ROWS_PER_LOAD + vrow;
-      const __bf16* vrow_p = APPEND && tok == newpos ? vnew_row : row_of(vbase, c0 + i * ROWS_PER_LOAD, tok);
-      vr[i] = tok < t1 ? ld16_stream(vrow_p + vcol) : zero_u32x4();
+      const int tok0 = min(c0 + i * ROWS_PER_LOAD, last & ~(ROWS_PER_LOAD - 1));
+      const int tok = min(c0 + i * ROWS_PER_LOAD + vrow, last);
+      const __bf16* vrow_p = APPEND && tok == newpos ? vnew_row : row_of(vbase, tok0, tok);
+      vr[i] = ld16_stream(vrow_p + vcol);
     }
   };
   load_k(t0);
@@ -222,8 +229,15 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
     if (more) load_k(c0 + kChunk);  // next chunk's K streams during this chunk
 
     // ---- online softmax for head n over positions {16mt + 4g + i} ----
+    // A head's running max is raised (and its accumulators rescaled) only
+    // when some score of the chunk exceeds it by more than 2^kLazy;
+    // otherwise the stale max stays, the weights stay below 2^kLazy, and
+    // numerator and denominator share it (the combine pass takes any max).
+    // l_run holds this lane's share of the denominator (its positions); the
+    // shares are summed over the lane groups once, after the loop.
+    constexpr float kLazy = 8.f;
     float sv[8];
-    float cmax = -INFINITY;
+    float lmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -231,32 +245,30 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
         const int tok = c0 + 16 * mt + 4 * g + i;
         const float x = tok < t1 ? st[mt][i] * scale_log2 : -INFINITY;
         sv[4 * mt + i] = x;
-        cmax = fmaxf(cmax, x);
+        lmax = fmaxf(lmax, x);
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);  // finite: the chunk has >= 1 position
-    const float alpha = fast_exp2(m_run - m_new);
-    float psum = 0.f;
+    if (__any(lmax > m_run + kLazy)) {  // always on the first chunk (m_run = -inf)
+      float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);  // finite: the chunk has >= 1 position
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      // acc rows are heads 4g+i; their rescale factors live in lanes 4g+i.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
+      }
+    }
     uint32_t pw[4];
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const float e0 = fast_exp2(sv[j] - m_new);
-      const float e1 = fast_exp2(sv[j + 1] - m_new);
-      psum += e0 + e1;
+      const float e0 = fast_exp2(sv[j] - m_run);
+      const float e1 = fast_exp2(sv[j + 1] - m_run);
+      l_run += e0 + e1;
       pw[j / 2] = pack_bf16x2(e0, e1);
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    // acc rows are heads 4g+i; their rescale factors live in lanes 4g+i.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
     }
 
     // ---- V chunk -> LDS (row-major), then transposed reads as B operand ----
@@ -285,6 +297,9 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       *reinterpret_cast<u32x4*>(vdst + 8 * lane) = ld16(vnew_row + 8 * lane);
     }
   }
+
+  l_run += __shfl_xor(l_run, 16);  // the head's denominator: sum of the lane groups' shares
+  l_run += __shfl_xor(l_run, 32);
 
   // ---- write the partition's partial state ----
   const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;

@@ -177,30 +177,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
   u32x4 ka[2][KWORDS];
   u32x4 vr[VLOADS];
   f32x4 ksv[2], vsv[2];
+  // Rows past the partition are fetched from its last row instead (valid
+  // memory, finite codes; their scores and weights are masked below), so no
+  // load is predicated.
+  const int last = t1 - 1;
   auto load_k = [&](int c0) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int tok = c0 + 16 * mt + n;
+      const int tok = min(c0 + 16 * mt + n, last);
       const int8_t* krow = (APPEND && tok == newpos ? slot : kbase + (size_t)tok * D) + KSEG * g;
 #pragma unroll
-      for (int w = 0; w < KWORDS; ++w) ka[mt][w] = tok < t1 ? ld16_stream(krow + 16 * w) : zero_u32x4();
+      for (int w = 0; w < KWORDS; ++w) ka[mt][w] = ld16_stream(krow + 16 * w);
       // scales of the positions this lane's scores belong to: 16mt + 4g + i
-      const int s0 = c0 + 16 * mt + 4 * g;
+      const int s0 = min(c0 + 16 * mt + 4 * g, last & ~3);
       const bool sc_new = APPEND && s0 == s0_new;
-      const float* kss = sc_new ? slot_sc : ksb + s0;
-      const float* vss = sc_new ? slot_sc + 4 : vsb + s0;
-      ksv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(kss) : f32x4{0.f, 0.f, 0.f, 0.f};
-      vsv[mt] = s0 < t1 ? *reinterpret_cast<const f32x4*>(vss) : f32x4{0.f, 0.f, 0.f, 0.f};
+      ksv[mt] = *reinterpret_cast<const f32x4*>(sc_new ? slot_sc : ksb + s0);
+      vsv[mt] = *reinterpret_cast<const f32x4*>(sc_new ? slot_sc + 4 : vsb + s0);
     }
   };
   auto load_v = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int tok = c0 + i * ROWS_PER_LOAD + vrow;
+      const int tok = min(c0 + i * ROWS_PER_LOAD + vrow, last);
       const int8_t* vrow_p = APPEND && tok == newpos ? slot + D : vbase + (size_t)tok * D;
-      vr[i] = tok < t1 ? ld16_stream(vrow_p + vcol) : zero_u32x4();
+      vr[i] = ld16_stream(vrow_p + vcol);
     }
   };
+  // A head's running max is raised (and its accumulators rescaled) only
+  // when some score of the chunk exceeds it by more than 2^kLazy; otherwise
+  // the stale max stays, the weights stay below 2^kLazy, and numerator and
+  // denominator share it (the combine pass takes any max).  l_run holds this
+  // lane's share of the denominator (its positions); the shares are summed
+  // over the lane groups once, after the loop.
+  constexpr float kLazy = 8.f;
   load_k(t0);
   load_v(t0);
 
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
 
     // ---- online softmax for head n over positions {16mt + 4g + i} ----
     float x[8];
-    float cmax = -INFINITY;
+    float lmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -240,31 +249,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
         const float xv = ok ? st[mt][i] * (sk[4 * mt + i] * scale_log2) : -INFINITY;
         x[4 * mt + i] = xv;
         sv[4 * mt + i] = ok ? sv[4 * mt + i] : 0.f;  // rows past the end never reach the sum
-        cmax = fmaxf(cmax, xv);
+        lmax = fmaxf(lmax, xv);
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = fast_exp2(m_run - m_new);
-    float psum = 0.f;
+    if (__any(lmax > m_run + kLazy)) {
+      float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
+      }
+    }
     uint32_t pw[4];
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const float e0 = fast_exp2(x[j] - m_new);
-      const float e1 = fast_exp2(x[j + 1] - m_new);
-      psum += e0 + e1;
+      const float e0 = fast_exp2(x[j] - m_run);
+      const float e1 = fast_exp2(x[j + 1] - m_run);
+      l_run += e0 + e1;
       pw[j / 2] = pack_bf16x2(e0 * sv[j], e1 * sv[j + 1]);
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = __shfl(alpha, 4 * g + i);
-#pragma unroll
-      for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
     }
 
     // ---- V codes -> bf16 rows in LDS, then transposed reads ----
@@ -290,6 +297,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
     }
     __syncthreads();
   }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
 
   if (APPEND && has_new && hb == 0) {  // the appended rows join the cache
     if (lane < 2 * (D / 16)) {
