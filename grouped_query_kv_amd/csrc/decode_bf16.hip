@@ -186,14 +186,17 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   // dims 16t + 4*(n%4)
   const uint16_t* tr_src = &vt[(4 * g + (n >> 2)) * LDS_ROW + 4 * (n & 3)];
 
-  u32x4 ka[2][KSTEPS];
+  // K operands of two chunks, used in turn (the loop is unrolled by two), so
+  // the prefetch of chunk c+1 is never copied between registers; measured
+  // 1.5-2% faster on the decode workloads than one set
+  u32x4 ka0[2][KSTEPS], ka1[2][KSTEPS];
   u32x4 vr[VLOADS];
   // Rows past the partition are fetched from its last row instead (valid
   // memory; their scores are masked and their weights are zero), so no load
   // is predicated.  A clamped row stays in the clamped load group, so a
   // paged group still lies in one block.
   const int last = t1 - 1;
-  auto load_k = [&](int c0) {
+  auto load_k = [&](u32x4 (&ka)[2][KSTEPS], int c0) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int tok0 = min(c0 + 16 * mt, last & ~15);
@@ -212,10 +215,10 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       vr[i] = ld16_stream(vrow_p + vcol);
     }
   };
-  load_k(t0);
+  load_k(ka0, t0);
   load_v(t0);
 
-  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+  auto chunk = [&](u32x4 (&ka)[2][KSTEPS], u32x4 (&ka_next)[2][KSTEPS], int c0) {
     const bool more = c0 + kChunk < t1;
     // ---- S^T = K . Q^T for the two 16-position tiles ----
     f32x4 st[2];
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
       for (int s = 0; s < KSTEPS; ++s)
         st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[mt][s]), qf[s], st[mt], 0, 0, 0);
     }
-    if (more) load_k(c0 + kChunk);  // next chunk's K streams during this chunk
+    if (more) load_k(ka_next, c0 + kChunk);  // next chunk's K streams during this chunk
 
     // ---- online softmax for head n over positions {16mt + 4g + i} ----
     // A head's running max is raised (and its accumulators rescaled) only
@@ -286,6 +289,13 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
                                                        acc[t], 0, 0, 0);
     }
     __syncthreads();  // LDS reads done before the next chunk overwrites vt
+  };
+
+  for (int c0 = t0;; c0 += 2 * kChunk) {
+    chunk(ka0, ka1, c0);
+    if (c0 + kChunk >= t1) break;
+    chunk(ka1, ka0, c0 + kChunk);
+    if (c0 + 2 * kChunk >= t1) break;
   }
 
   if (APPEND && hb == 0 && newpos >= t0 && newpos < t1) {  // wave-uniform
