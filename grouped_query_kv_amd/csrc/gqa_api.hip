@@ -45,8 +45,8 @@ int part_tokens_override() {
   static const int v = [] {
     const char* s = std::getenv("GQA_DECODE_PART_TOKENS");
     if (!s) return 0;
-    const int x = std::atoi(s);
-    return x >= 64 ? (x + 31) / 32 * 32 : 0;
+    const long x = std::strtol(s, nullptr, 10);
+    return x >= 64 && x <= (1L << 24) ? (int)((x + 31) / 32 * 32) : 0;  // else ignored
   }();
   return v;
 }
@@ -74,9 +74,11 @@ DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, int max_part
   const int L = max_seq_len > 0 ? max_seq_len : 1;
   int pt = part_tokens_override();
   if (pt == 0) {
-    // One single-wave workgroup per partition.  Aim at about one full round
-    // of resident waves over the 256 CUs (3 per SIMD at the partition pass's
-    // register budget), with equal partitions of a multiple of 32 positions.
+    // One single-wave workgroup per partition.  Aim at 3072 workgroups over
+    // the 256 CUs -- one round of the int8 pass's three resident waves per
+    // SIMD, one and a half of the bf16 pass's two (sweeps of the partition
+    // length put this within a few percent of the best fixed length on every
+    // decode workload) -- with equal partitions of a multiple of 32 positions.
     const long long target = 256LL * 4 * 3;
     long long parts = target / (units > 0 ? units : 1);
     if (parts < 1) parts = 1;
