@@ -336,6 +336,9 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
                                     float scale_log2, const void* k_new, const void* v_new,
                                     const PagedArgs* paged, hipStream_t stream) {
+  if (decode_wide_supported(plan.head_blocks))  // G > 16: one KV read for all head blocks
+    return launch_decode_wide_bf16(q, k_cache, v_cache, seq_lens, ws, plan, B, H, K, S_max, d,
+                                   scale_log2, k_new, v_new, paged, stream);
   // many (sequence, head) units -- a large batch -- : one-dimensional grid,
   // partition slowest (measured on the ragged 70B layer, 512 units: 4%
   // faster; on the Llama-3-8B layer, 128 units, the three-dimensional order

@@ -1,0 +1,294 @@
+// Decode partition pass for groups of more than 16 query heads (bf16).
+//
+// The one-wave pass (decode_bf16.hip) multiplies a K chunk held in registers
+// by the 16 query heads one matrix-core instruction covers; a group of G > 16
+// heads (MQA shapes: one KV head for 32, 64 or 71 query heads) would need
+// ceil(G / 16) such waves, each reading the same K and V rows from memory.
+// The pages' engineering rule is that a group's shared KV block is loaded
+// once for all of its heads (pinghaoyang.com.cn "GQA 完全拆解", section 工程实现;
+// its MQA section: all heads share one K/V head).  So here one workgroup of W
+// waves (W >= the number of 16-head blocks) owns a partition of one KV head:
+// the waves load the chunk's K and V rows together into LDS, once, and each
+// wave multiplies them with its own 16 heads.  Waves beyond the group's head
+// blocks only help load.
+//
+// Per chunk of 32 positions: store the prefetched K and V rows into LDS,
+// barrier, prefetch the next chunk into registers, then per wave S^T =
+// K_chunk . Q_hb^T (K operands read from LDS, same operand layout and
+// contraction relabelling as the one-wave pass), the lazy base-2 online
+// softmax, and O += P . V_chunk (V read transposed from LDS), barrier.  The
+// partial state written per head is the one-wave pass's, so the same
+// combine pass merges it.
+#include "common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kChunk = 32;   // positions per inner iteration
+constexpr int kVPad = 16;    // bf16 elements of padding per V row (as the one-wave pass)
+constexpr int kKPad = 8;     // bf16 elements of padding per K row
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+template <int D, bool APPEND, bool PAGED, int W>
+__global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
+    const __bf16* __restrict__ q, __bf16* __restrict__ kc, __bf16* __restrict__ vc,
+    const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
+    float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
+    int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, PagedArgs pg) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int KSTEPS = D / 32;
+  constexpr int NTILES = D / 16;
+  constexpr int LPR = D / 8;                   // 16-byte words per row
+  constexpr int RPW = 64 / LPR;                // rows one wave instruction covers
+  constexpr int NI = (kChunk * LPR + 64 * W - 1) / (64 * W);  // loads per lane per tensor
+  constexpr int KROW = D + kKPad;
+  constexpr int VROW = D + kVPad;
+
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * VROW];
+
+  const int p = blockIdx.x;
+  const int k = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = H / K;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int hb = wave;                       // this wave's block of 16 heads
+  const bool computes = hb < head_blocks;    // wave-uniform
+
+  const int cap = PAGED ? pg.max_blocks * pg.block_size : S_max;
+  const int L_in = PAGED ? min(seq_lens[b], cap) : seq_lens[b];
+  int L = L_in, newpos = -1;
+  if (APPEND) {
+    bool room = L_in >= 0 && L_in < cap;
+    if (PAGED && room) {
+      const int id = pg.block_table[(size_t)b * pg.max_blocks + L_in / pg.block_size];
+      room = id >= 0 && id < pg.num_blocks;
+    }
+    if (room) {
+      newpos = L_in;
+      L = L_in + 1;
+    }
+    if (p == 0 && k == 0 && threadIdx.x == 0) lens_out[b] = L;
+  }
+  const int pt_b = balanced_part_tokens(L, part_tokens);
+  const int t0 = p * pt_b;
+  if (t0 >= L) return;  // uniform over the workgroup
+  const int t1 = min(t0 + pt_b, L);
+  const int last = t1 - 1;
+
+  const int hq = hb * 16 + n;
+  const bool hq_ok = computes && hq < G;
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = as_bf16x8(hq_ok ? ld16(qrow + 32 * s + 8 * g) : zero_u32x4());
+  }
+
+  const size_t head_base = PAGED ? 0 : ((size_t)b * K + k) * (size_t)S_max * D;
+  __bf16* kbase = kc + head_base;
+  __bf16* vbase = vc + head_base;
+  const int lb0 = PAGED ? t0 / pg.block_size : 0;
+  int blk_id = 0;
+  if (PAGED) {
+    const int nb = (t1 - 1) / pg.block_size - lb0 + 1;  // <= 64 by the split plan
+    if (lane < nb)
+      blk_id = min(max(pg.block_table[(size_t)b * pg.max_blocks + lb0 + lane], 0), pg.num_blocks - 1);
+  }
+  // first element of cache row `tok`; `tok0` is a wave-uniform position of
+  // the same RPW-row group (inside one block: block_size is a multiple of 16)
+  auto row_of = [&](__bf16* base, int tok0, int tok) -> __bf16* {
+    if (!PAGED) return base + (size_t)tok * D;
+    const int blk = __builtin_amdgcn_readlane(blk_id, tok0 / pg.block_size - lb0);
+    return base + (((size_t)blk * K + k) * pg.block_size + (tok - (tok0 / pg.block_size) * pg.block_size)) * D;
+  };
+  const __bf16* knew_row = APPEND ? k_new + ((size_t)b * K + k) * D : nullptr;
+  const __bf16* vnew_row = APPEND ? v_new + ((size_t)b * K + k) * D : nullptr;
+
+  // Thread `tid` moves word (tid + i * 64W) % LPR of row (tid + i * 64W) / LPR
+  // of the chunk; a wave instruction covers RPW whole rows.  Rows past the
+  // partition end are fetched from its last row (valid memory; masked).
+  const int col = (threadIdx.x % LPR) * 8;
+  u32x4 kr[NI], vr[NI];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (threadIdx.x + i * 64 * W) / LPR;
+      if (row < kChunk) {  // uniform per wave instruction
+        const int tok0 = min(c0 + (i * 64 * W + 64 * wave) / LPR, last & ~(RPW - 1));
+        const int tok = min(c0 + row, last);
+        const __bf16* krow = APPEND && tok == newpos ? knew_row : row_of(kbase, tok0, tok);
+        const __bf16* vrow = APPEND && tok == newpos ? vnew_row : row_of(vbase, tok0, tok);
+        kr[i] = ld16_stream(krow + col);
+        vr[i] = ld16_stream(vrow + col);
+      }
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (threadIdx.x + i * 64 * W) / LPR;
+      if (row < kChunk) {
+        *reinterpret_cast<u32x4*>(&kt[row * KROW + col]) = kr[i];
+        *reinterpret_cast<u32x4*>(&vt[row * VROW + col]) = vr[i];
+      }
+    }
+  };
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;  // this lane's share of the running sum of head n
+  f32x4 acc[NTILES];
+#pragma unroll
+  for (int t = 0; t < NTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* tr_src = &vt[(4 * g + (n >> 2)) * VROW + 4 * (n & 3)];
+  constexpr float kLazy = 8.f;  // see the one-wave pass: lazy running max
+
+  load(t0);
+  for (int c0 = t0; c0 < t1; c0 += kChunk) {
+    stage();
+    __syncthreads();  // the chunk is in LDS
+    if (c0 + kChunk < t1) load(c0 + kChunk);  // the next chunk streams during this one
+    if (computes) {
+      // ---- S^T = K . Q^T (K operands from LDS) ----
+      f32x4 st[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[(16 * mt + n) * KROW + 32 * s + 8 * g]);
+          st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[s], st[mt], 0, 0, 0);
+        }
+      }
+      // ---- online softmax for head n over positions {16mt + 4g + i} ----
+      float sv[8];
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = c0 + 16 * mt + 4 * g + i < t1 ? st[mt][i] * scale_log2 : -INFINITY;
+          sv[4 * mt + i] = x;
+          lmax = fmaxf(lmax, x);
+        }
+      if (__any(lmax > m_run + kLazy)) {
+        float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        const float m_new = fmaxf(m_run, cmax);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = __shfl(alpha, 4 * g + i);
+#pragma unroll
+          for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
+        }
+      }
+      uint32_t pw[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float e0 = fast_exp2(sv[j] - m_run);
+        const float e1 = fast_exp2(sv[j + 1] - m_run);
+        l_run += e0 + e1;
+        pw[j / 2] = pack_bf16x2(e0, e1);
+      }
+      // ---- O += P . V (V read transposed from LDS) ----
+      const bf16x8 pa = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) {
+        const uint2 lo = lds_read_tr16(tr_src + 16 * t);
+        const uint2 hi = lds_read_tr16(tr_src + 16 * VROW + 16 * t);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                                         acc[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with the chunk before it is overwritten
+  }
+
+  if (APPEND && wave == 0 && newpos >= t0 && newpos < t1) {  // the appended rows join the cache
+    __bf16* kdst = row_of(kbase, newpos, newpos);
+    __bf16* vdst = row_of(vbase, newpos, newpos);
+    if (lane < LPR) {
+      *reinterpret_cast<u32x4*>(kdst + 8 * lane) = ld16(knew_row + 8 * lane);
+      *reinterpret_cast<u32x4*>(vdst + 8 * lane) = ld16(vnew_row + 8 * lane);
+    }
+  }
+  if (!computes) return;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * g + i;
+    if (hb * 16 + hl < G) {
+      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
+    }
+  }
+  if (g == 0 && hq_ok) {
+    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    ml[0] = m_run;
+    ml[1] = l_run;
+  }
+}
+
+}  // namespace
+
+bool decode_wide_supported(int head_blocks) { return head_blocks > 1 && head_blocks <= 8; }
+
+hipError_t launch_decode_wide_bf16(const void* q, void* k_cache, void* v_cache,
+                                   const int32_t* seq_lens, const DecodeWorkspace& ws,
+                                   const DecodePlan& plan, int B, int H, int K, int S_max, int d,
+                                   float scale_log2, const void* k_new, const void* v_new,
+                                   const PagedArgs* paged, hipStream_t stream) {
+  const dim3 grid(plan.parts, K, B);
+  auto qp = static_cast<const __bf16*>(q);
+  auto kp = static_cast<__bf16*>(k_cache);
+  auto vp = static_cast<__bf16*>(v_cache);
+  auto kn = static_cast<const __bf16*>(k_new);
+  auto vn = static_cast<const __bf16*>(v_new);
+  const PagedArgs pg = paged ? *paged : PagedArgs{nullptr, 16, 0, 1};
+  const int hbk = plan.head_blocks;
+#define GQA_WIDE(DD, AP, PG, WW)                                                                  \
+  hipLaunchKernelGGL((decode_wide_bf16_kernel<DD, AP, PG, WW>), grid, dim3(64 * WW), 0, stream,    \
+                     qp, kp, vp, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, \
+                     plan.parts, plan.head_blocks, scale_log2, kn, vn, ws.lens, pg)
+#define GQA_WIDE_W(DD, AP, PG)                                                                   \
+  if (hbk <= 2) GQA_WIDE(DD, AP, PG, 2);                                                          \
+  else if (hbk <= 4) GQA_WIDE(DD, AP, PG, 4);                                                     \
+  else GQA_WIDE(DD, AP, PG, 8);
+#define GQA_WIDE_D(DD)                                                                           \
+  if (paged) {                                                                                    \
+    if (k_new) { GQA_WIDE_W(DD, true, true) } else { GQA_WIDE_W(DD, false, true) }                \
+  } else {                                                                                        \
+    if (k_new) { GQA_WIDE_W(DD, true, false) } else { GQA_WIDE_W(DD, false, false) }              \
+  }
+  if (d == 128) {
+    GQA_WIDE_D(128)
+  } else {
+    GQA_WIDE_D(64)
+  }
+#undef GQA_WIDE_D
+#undef GQA_WIDE_W
+#undef GQA_WIDE
+  return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -77,6 +77,17 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     float scale_log2, const void* k_new, const void* v_new,
                                     const PagedArgs* paged, hipStream_t stream);
 
+// Partition pass for groups of 2 to 8 blocks of 16 query heads (bf16): one
+// workgroup of waves per (partition, KV head) loads each K/V chunk once into
+// LDS for all of the group's heads.  Same arguments and partial state as
+// launch_decode_split_bf16, which routes such groups here.
+bool decode_wide_supported(int head_blocks);
+hipError_t launch_decode_wide_bf16(const void* q, void* k_cache, void* v_cache,
+                                   const int32_t* seq_lens, const DecodeWorkspace& ws,
+                                   const DecodePlan& plan, int B, int H, int K, int S_max, int d,
+                                   float scale_log2, const void* k_new, const void* v_new,
+                                   const PagedArgs* paged, hipStream_t stream);
+
 // Append into a paged cache: row seq_lens[b] goes to block
 // block_table[b][L / block_size], row L % block_size.
 hipError_t launch_kv_append_paged(const void* k_new, const void* v_new, void* k_pool, void* v_pool,

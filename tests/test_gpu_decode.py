@@ -52,6 +52,9 @@ CASES = [
     (1, 71, 1, 64, [257], "bf16"),             # G = 71: five head blocks
     (2, 8, 8, 128, [2, 97], "bf16"),           # K = H (MHA)
     (2, 32, 1, 128, [129, 64], "bf16"),        # K = 1 (MQA), G = 32
+    (2, 48, 1, 128, [777, 31], "bf16"),        # G = 48: three head blocks in a four-wave group
+    (1, 128, 1, 64, [1500], "bf16"),           # G = 128: eight head blocks
+    (3, 64, 2, 128, [0, 2049, 64], "bf16"),    # G = 32 on two KV heads, an empty sequence
     (4, 64, 8, 128, [0, 1, 640, 641], "bf16"),  # empty sequence, partition edges
     (2, 12, 4, 128, [70, 3], "f32"),
     (1, 71, 1, 128, [200], "f32"),

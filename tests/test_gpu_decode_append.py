@@ -46,6 +46,9 @@ CASES = [
     (2, 64, 8, 128, [511, 2048], 2049, "bf16"),
     (2, 56, 8, 128, [300, 300], 300, "bf16"),           # full caches: no append
     (2, 71, 1, 64, [100, 257], 300, "bf16"),
+    (2, 48, 1, 128, [0, 999], 1000, "bf16"),            # G = 48; the last free row
+    (1, 128, 2, 64, [333], 400, "bf16"),                # G = 64
+    (2, 40, 1, 128, [500, 500], 500, "bf16"),           # G = 40, full caches: no append
     (3, 12, 4, 128, [0, 63, 200], 256, "f32"),
     (2, 16, 16, 64, [64, 64], 64, "f32"),               # full caches, fp32
 ]

@@ -50,6 +50,8 @@ CASES = [
     (2, 8, 8, 128, [2, 97], 16),              # K = H (MHA)
     (2, 32, 1, 128, [129, 4100], 48),         # K = 1 (MQA), G = 32, block_size 48
     (1, 71, 1, 64, [257], 16),                # G = 71: five head blocks
+    (2, 48, 1, 128, [777, 31], 32),           # G = 48: three head blocks
+    (1, 128, 2, 64, [1500], 16),              # G = 64: four head blocks
     # partitions capped at 62 blocks of 16 rows (992 positions)
     (40, 8, 8, 64, [8000 + 37 * i for i in range(40)], 16),
 ]
@@ -112,6 +114,34 @@ def test_paged_matches_contiguous_decode():
     b = bf16_bound(ref, _vmax(p["v_pool"]))
     assert report("paged", f64(out_p), ref)["max_abs"] <= b
     assert report("contiguous", f64(out_c), ref)["max_abs"] <= b
+
+
+def test_paged_wide_groups_at_the_block_cap():
+    """Groups of 48 query heads (three 16-head blocks sharing each K/V chunk)
+    over long ragged sequences, where the paged partitions reach their cap
+    of 62 blocks of 16 rows (the contiguous decode of the same cache splits
+    it into longer partitions): sampled sequences of both match the oracle."""
+    B, H, K, d = 64, 96, 2, 64
+    lens = [7900 + 3 * i for i in range(B)]
+    note(f"paged wide groups at the block cap B={B} H={H} K={K} d={d}")
+    inp = decode_inputs(B, H, K, d, "bf16", seed=47, lens=lens)
+    p = paged_layout(inp, 16, seed=48)
+    msl = max(lens)
+    out_p = _run(p, msl)
+    q, kc, vc, sl = (inp[n].to(DEV) for n in ("q", "k_cache", "v_cache", "seq_lens"))
+    ws = torch.empty(gqa.gqa_decode_workspace_bytes(B, H, K, msl, d), dtype=torch.uint8, device=DEV)
+    out_c = torch.empty_like(out_p)
+    gqa.gqa_decode(q, kc, vc, sl, out_c, ws, msl, scale=scale_of(d))
+    torch.cuda.synchronize()
+    for b in (0, 37, B - 1):
+        sub = paged_layout({"k_cache": inp["k_cache"][b:b + 1], "v_cache": inp["v_cache"][b:b + 1]}, 16,
+                           shuffle=False)
+        ref = decode_paged_ref(f64(inp["q"][b:b + 1]), _np(sub["k_pool"]), _np(sub["v_pool"]),
+                               sub["block_table"].numpy(), np.array([lens[b]]), scale_of(d))
+        bound = bf16_bound(ref, _vmax(sub["v_pool"]))
+        for name, out in (("paged", out_p), ("contiguous", out_c)):
+            r = report(f"wide {name} b={b}", f64(out[b:b + 1]), ref)
+            assert r["finite"] and r["max_abs"] <= TOL["bf16"] and r["max_abs"] <= bound
 
 
 @pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f32", 32)])
@@ -207,6 +237,8 @@ FUSED_CASES = [
     (2, 16, 4, 64, [31, 2100], 32, None, 1),
     (2, 32, 1, 128, [129, 4100], 48, None, 1),       # G = 32: two head blocks
     (1, 71, 1, 64, [257], 16, None, 1),              # G = 71: five head blocks
+    (2, 48, 1, 128, [777, 31], 32, None, 2),         # G = 48: three head blocks, two steps
+    (1, 128, 2, 64, [1500], 16, None, 3),            # G = 64: four head blocks, three steps
     (40, 8, 8, 64, [8000 + 37 * i for i in range(40)], 16, None, 1),  # 62-block partitions, 320 units
     (2, 32, 8, 128, [60, 3], 16, 64, 8),             # eight steps; the first table fills up
 ]
