@@ -17,12 +17,16 @@ pytestmark = pytest.mark.gpu
 N_CASES = 12
 
 
-def _cases(seed):
+SMALL_GROUPS = [1, 2, 3, 4, 5, 8, 16]
+LARGE_GROUPS = [17, 24, 33, 48, 64, 71, 100, 128]   # several 16-head blocks per group
+
+
+def _cases(seed, groups=SMALL_GROUPS):
     r = np.random.default_rng(seed)
     out = []
     for _ in range(N_CASES):
         K = int(r.choice([1, 2, 4, 8]))
-        G = int(r.choice([1, 2, 3, 4, 5, 8, 16]))
+        G = int(r.choice(groups))
         B = int(r.integers(1, 5))
         d = int(r.choice([64, 128]))
         lens = [int(x) for x in r.integers(0, 1500, B)]
@@ -34,7 +38,15 @@ def _cases(seed):
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_random_decode_contiguous_paged_int8(case):
-    B, H, K, d, lens = _cases(2024)[case]
+    _check_decode(case, *_cases(2024)[case])
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_decode_large_groups(case):
+    _check_decode(case, *_cases(2026, LARGE_GROUPS)[case])
+
+
+def _check_decode(case, B, H, K, d, lens):
     note(f"random decode B={B} H={H} K={K} d={d} lens={lens}")
     s_max = (max(lens) + 4) // 4 * 4
     inp = decode_inputs(B, H, K, d, "bf16", seed=500 + case, lens=lens, s_max=s_max, nan_tail=False)
