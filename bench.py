@@ -18,7 +18,9 @@ blocks in shuffled physical order; an int8
 workload (decode_int8_llama3_8b) runs gqa_decode_append_int8 (the
 quantising append fused into the int8 partition pass) over the cache
 quantised once before timing (bytes counted as stored: d codes + one fp32
-scale per row).  The default workload is
+scale per row).  decode_mqa_71h is a multi-query layer (71 query heads on
+one KV head, d=64, 32768 cached tokens), whose groups of more than 16 heads
+take the one-workgroup-per-group partition pass.  The default workload is
 the Llama-3-8B-shaped layer: B=16 sequences at 8192 cached tokens, 32 query
 heads over 8 KV heads, d=128, bf16 (synthetic N(0,1) data).
 
@@ -162,7 +164,7 @@ def cpu_baseline_decode(inp, w, budget_s):
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "tokens_per_s": done_seqs / t_used,
             "sample": f"{done_seqs} whole sequences of the workload ({'paged ' if paged else 'int8 ' if int8 else ''}append + decode over "
-                      f"{int(inp['seq_lens'][0]) + (1 if w.append else 0)} positions, all 32 heads), "
+                      f"{int(inp['seq_lens'][0]) + (1 if w.append else 0)} positions, all {w.H} heads), "
                       f"{t_used:.1f} s of fp64 NumPy on {cores} BLAS threads"}
 
 
@@ -183,6 +185,8 @@ def bench_decode(args, w):
     kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
     paged = "block_size" in w.extra
     int8 = w.extra.get("kv_dtype") == "int8"
+    # groups of more than 16 query heads take the one-workgroup-per-group bf16 pass
+    wide = w.dtype == "bf16" and not int8 and (H // K + 15) // 16 > 1
     elem, row_extra = (1, 4) if int8 else ((4, 0) if w.dtype == "f32" else (2, 0))
     copies = []
     if int8:
@@ -313,11 +317,12 @@ def bench_decode(args, w):
                                 " (decode_split_bf16_kernel, paged)" if paged else
                                 "fp32 decode partition pass (decode_split_f32_kernel)" if w.dtype == "f32" else
                                 "decode partition pass" + (" with fused append" if w.append else "") +
-                                " (decode_split_bf16_kernel)"),
+                                (" (decode_wide_bf16_kernel)" if wide else " (decode_split_bf16_kernel)")),
                      "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("decode_split_int8_kernel" if int8 else
+                                                 "decode_wide_bf16_kernel" if wide else
                                                  "decode_split_bf16_kernel" + ("_paged" if paged else ""), w.name),
                      "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled),
                      "kernel_us_p10_p50_p90": [round(p10 * 1e3, 2), round(p50 * 1e3, 2), round(p90 * 1e3, 2)],

@@ -43,6 +43,21 @@ def _compile(src: Path) -> Path:
     return obj
 
 
+def _check_launch_stubs(lib: Path) -> None:
+    """Fail when a kernel's host launch stub is referenced but not defined.
+
+    hipcc's host pass can drop a kernel's stub without a diagnostic (seen with
+    a __bf16 source pointer passed to the global-to-LDS load builtin); the
+    library then links but cannot be loaded."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    r = subprocess.run([nm, "-u", str(lib)], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        raise RuntimeError(f"{len(missing)} kernel launch stubs are undefined in {lib.name}, e.g. {missing[0]}")
+
+
 def build(verbose: bool = True) -> Path:
     """Compile every source and link libgqa.so (always rebuilds)."""
     if not shutil.which(HIPCC) and not Path(HIPCC).exists():
@@ -56,6 +71,7 @@ def build(verbose: bool = True) -> Path:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    _check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", file=sys.stderr)

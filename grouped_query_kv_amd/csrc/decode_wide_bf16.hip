@@ -7,27 +7,43 @@
 // The pages' engineering rule is that a group's shared KV block is loaded
 // once for all of its heads (pinghaoyang.com.cn "GQA 完全拆解", section 工程实现;
 // its MQA section: all heads share one K/V head).  So here one workgroup of W
-// waves (W >= the number of 16-head blocks) owns a partition of one KV head:
-// the waves load the chunk's K and V rows together into LDS, once, and each
-// wave multiplies them with its own 16 heads.  Waves beyond the group's head
-// blocks only help load.
+// waves, one per 16-head block of the group (the last may hold fewer heads),
+// owns a partition of one KV head: the waves copy the partition's K and V
+// rows together into LDS, once, and each wave multiplies them with its own
+// heads.
 //
-// Per chunk of 32 positions: store the prefetched K and V rows into LDS,
-// barrier, prefetch the next chunk into registers, then per wave S^T =
+// Rows are staged in blocks of 32*SUB positions through a ring of NS LDS
+// buffers, filled by direct global-to-LDS copies (global_load_lds_dwordx4:
+// lane i of a wave instruction lands its 16 bytes at LDS base + 16 i, no
+// registers involved), so NS-1 blocks are in flight per workgroup at no
+// register cost.  Per block: wait for this wave's copies
+// of the block, barrier, issue the copies of block j+NS-1 into the buffer
+// the previous block used, then per 32-position chunk and per wave S^T =
 // K_chunk . Q_hb^T (K operands read from LDS, same operand layout and
 // contraction relabelling as the one-wave pass), the lazy base-2 online
-// softmax, and O += P . V_chunk (V read transposed from LDS), barrier.  The
-// partial state written per head is the one-wave pass's, so the same
-// combine pass merges it.
+// softmax, and O += P . V_chunk (V read transposed from LDS).  The partial
+// state written per head is the one-wave pass's, so the same combine pass
+// merges it.
+//
+// LDS layout of a staged tensor: whole unpadded rows of D bf16 whose 16-byte
+// chunks are XOR-swizzled by row, K: chunk ^ (row % (D/8)), V: chunk ^
+// 2 (row % (D/16)) (the prefill kernel's layout: conflict-free 16-byte
+// operand reads and transposed 8-byte reads).  Each lane fetches the global
+// chunk that belongs in its LDS slot.
 #include "common.h"
 #include "gqa_internal.h"
 
 namespace gqa {
 namespace {
 
-constexpr int kChunk = 32;   // positions per inner iteration
-constexpr int kVPad = 16;    // bf16 elements of padding per V row (as the one-wave pass)
-constexpr int kKPad = 8;     // bf16 elements of padding per K row
+constexpr int kChunk = 32;  // positions per inner iteration
+// LDS buffers in the ring and 32-position chunks per block.  Measured on
+// five multi-query shapes (d = 64 and 128, 2 to 5 head blocks, 67-537 MB of
+// cache): two buffers of one chunk -- 16 KB of K and V at d = 128, 8 KB at
+// d = 64, so that many workgroups fit a CU's LDS -- beat three or four
+// buffers (3-25% slower) and two-chunk blocks at d = 64 (0-6% slower).
+constexpr int kRing = 2;
+constexpr int kSub = 1;
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -38,35 +54,44 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-template <int D, bool APPEND, bool PAGED, int W>
+// s_waitcnt immediate (gfx9 encoding): vector-memory count <= vm, LDS count 0
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (((vm >> 4) & 3) << 14); }
+
+template <int D, bool APPEND, bool PAGED, int W, int SUB, int NS>
 __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
     const __bf16* __restrict__ q, __bf16* __restrict__ kc, __bf16* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
-    int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, PagedArgs pg) {
+    float scale_log2, const __bf16* __restrict__ k_new, const __bf16* __restrict__ v_new,
+    int32_t* __restrict__ lens_out, PagedArgs pg) {
   static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
   constexpr int KSTEPS = D / 32;
   constexpr int NTILES = D / 16;
-  constexpr int LPR = D / 8;                   // 16-byte words per row
-  constexpr int RPW = 64 / LPR;                // rows one wave instruction covers
-  constexpr int NI = (kChunk * LPR + 64 * W - 1) / (64 * W);  // loads per lane per tensor
-  constexpr int KROW = D + kKPad;
-  constexpr int VROW = D + kVPad;
+  constexpr int LPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPW = 64 / LPR;               // rows per wave instruction
+  constexpr int RCH = kChunk * SUB;           // rows per staged block
+  constexpr int TILE = RCH * D;               // bf16 elements per staged tensor
+  constexpr int NINST = RCH / RPW;            // 1 KB copies per tensor and block
+  constexpr int NI = (NINST + W - 1) / W;     // copies per wave per tensor and block
+  constexpr bool SURPLUS = NINST % W != 0;    // some waves have one copy too many
+  static_assert(NINST * 512 == TILE, "copies cover a staged tensor");
+  static_assert(2 * NI * (NS - 2) < 64, "vector-memory counter range");
 
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * VROW];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NS][2][TILE];  // [buffer][K|V]
+  // target of the surplus copies (they repeat a real copy; their bytes are
+  // never read), so every wave issues the same number of copies per block
+  __shared__ __attribute__((aligned(16))) uint16_t sink[SURPLUS ? 512 : 8];
 
   const int p = blockIdx.x;
   const int k = blockIdx.y;
   const int b = blockIdx.z;
   const int G = H / K;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int hb = wave;                       // this wave's block of 16 heads
-  const bool computes = hb < head_blocks;    // wave-uniform
+  const int hb = wave;  // this wave's block of 16 heads
 
   const int cap = PAGED ? pg.max_blocks * pg.block_size : S_max;
   const int L_in = PAGED ? min(seq_lens[b], cap) : seq_lens[b];
@@ -90,7 +115,7 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
   const int last = t1 - 1;
 
   const int hq = hb * 16 + n;
-  const bool hq_ok = computes && hq < G;
+  const bool hq_ok = hq < G;
   bf16x8 qf[KSTEPS];
   {
     const __bf16* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D;
@@ -119,50 +144,68 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
   const __bf16* knew_row = APPEND ? k_new + ((size_t)b * K + k) * D : nullptr;
   const __bf16* vnew_row = APPEND ? v_new + ((size_t)b * K + k) * D : nullptr;
 
-  // Thread `tid` moves word (tid + i * 64W) % LPR of row (tid + i * 64W) / LPR
-  // of the chunk; a wave instruction covers RPW whole rows.  Rows past the
-  // partition end are fetched from its last row (valid memory; masked).
-  const int col = (threadIdx.x % LPR) * 8;
-  u32x4 kr[NI], vr[NI];
-  auto load = [&](int c0) {
+  // Copy slot c of this wave is instruction i = wave + c W of the block (the
+  // surplus slots, i >= NINST, repeat instruction i - NINST into the sink):
+  // lane l fills LDS chunk 64 i + l = row r, physical chunk l % LPR, with the
+  // logical chunk that the swizzle puts there.  Rows past the partition end
+  // are fetched from its last row (valid memory; masked).
+  int crow[NI], ck[NI], cv[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = (threadIdx.x + i * 64 * W) / LPR;
-      if (row < kChunk) {  // uniform per wave instruction
-        const int tok0 = min(c0 + (i * 64 * W + 64 * wave) / LPR, last & ~(RPW - 1));
-        const int tok = min(c0 + row, last);
-        const __bf16* krow = APPEND && tok == newpos ? knew_row : row_of(kbase, tok0, tok);
-        const __bf16* vrow = APPEND && tok == newpos ? vnew_row : row_of(vbase, tok0, tok);
-        kr[i] = ld16_stream(krow + col);
-        vr[i] = ld16_stream(vrow + col);
-      }
+  for (int c = 0; c < NI; ++c) {
+    const int i = (wave + c * W) % NINST;
+    const int r = (64 * i + lane) / LPR, ph = lane % LPR;
+    crow[c] = r;
+    ck[c] = (ph ^ (r & (LPR - 1))) * 8;
+    cv[c] = (ph ^ ((r & (LPR / 2 - 1)) << 1)) * 8;
+  }
+  auto copy_block = [&](int b0, int buf) {
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      const int i = wave + c * W;  // uniform
+      const int ir = i % NINST;
+      const int tok0 = min(b0 + ir * RPW, last & ~(RPW - 1));
+      const int tok = min(b0 + crow[c], last);
+      const __bf16* kp = APPEND && tok == newpos ? knew_row : row_of(kbase, tok0, tok);
+      const __bf16* vp = APPEND && tok == newpos ? vnew_row : row_of(vbase, tok0, tok);
+      uint16_t* kd = i < NINST ? &lds[buf][0][i * 512] : sink;
+      uint16_t* vd = i < NINST ? &lds[buf][1][i * 512] : sink;
+      // (a char source pointer: with a __bf16 one the host pass drops the
+      // kernel's launch stub without a diagnostic)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(kp + ck[c]),
+                                       (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vp + cv[c]),
+                                       (__attribute__((address_space(3))) void*)vd, 16, 0, 0);
     }
   };
-  auto stage = [&]() {
+
+  // loop-invariant LDS offsets (elements): K operand of k-step s is row
+  // 16mt + n of a chunk, logical chunk 4s + g; the transposed V read of dim
+  // block t is row 4g + n/4 (+16), logical chunk 2t + (n%4)/2, half n%2
+  int ka_off[KSTEPS], vb_off[NTILES];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = (threadIdx.x + i * 64 * W) / LPR;
-      if (row < kChunk) {
-        *reinterpret_cast<u32x4*>(&kt[row * KROW + col]) = kr[i];
-        *reinterpret_cast<u32x4*>(&vt[row * VROW + col]) = vr[i];
-      }
-    }
-  };
+  for (int s = 0; s < KSTEPS; ++s) ka_off[s] = n * D + (((4 * s + g) ^ (n & (LPR - 1))) * 8);
+  {
+    const int tr_row = 4 * g + (n >> 2);
+    const int swz = (tr_row & (LPR / 2 - 1)) << 1;
+#pragma unroll
+    for (int t = 0; t < NTILES; ++t)
+      vb_off[t] = tr_row * D + (((2 * t + ((n & 3) >> 1)) ^ swz) * 8) + 4 * (n & 1);
+  }
 
   float m_run = -INFINITY;
   float l_run = 0.f;  // this lane's share of the running sum of head n
   f32x4 acc[NTILES];
 #pragma unroll
   for (int t = 0; t < NTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* tr_src = &vt[(4 * g + (n >> 2)) * VROW + 4 * (n & 3)];
   constexpr float kLazy = 8.f;  // see the one-wave pass: lazy running max
 
-  load(t0);
-  for (int c0 = t0; c0 < t1; c0 += kChunk) {
-    stage();
-    __syncthreads();  // the chunk is in LDS
-    if (c0 + kChunk < t1) load(c0 + kChunk);  // the next chunk streams during this one
-    if (computes) {
+  auto compute_block = [&](int b0, int buf) {
+#pragma unroll
+    for (int sc = 0; sc < SUB; ++sc) {
+      const int c0 = b0 + kChunk * sc;
+      if (c0 >= t1) break;  // uniform
+      const uint16_t* kt = &lds[buf][0][kChunk * sc * D];
+      const uint16_t* vt = &lds[buf][1][kChunk * sc * D];
       // ---- S^T = K . Q^T (K operands from LDS) ----
       f32x4 st[2];
 #pragma unroll
@@ -170,7 +213,7 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
         st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[(16 * mt + n) * KROW + 32 * s + 8 * g]);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[16 * mt * D + ka_off[s]]);
           st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[s], st[mt], 0, 0, 0);
         }
       }
@@ -211,13 +254,38 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
       const bf16x8 pa = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
       for (int t = 0; t < NTILES; ++t) {
-        const uint2 lo = lds_read_tr16(tr_src + 16 * t);
-        const uint2 hi = lds_read_tr16(tr_src + 16 * VROW + 16 * t);
+        const uint2 lo = lds_read_tr16(vt + vb_off[t]);
+        const uint2 hi = lds_read_tr16(vt + vb_off[t] + 16 * D);
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}),
                                                          acc[t], 0, 0, 0);
       }
     }
-    __syncthreads();  // every wave is done with the chunk before it is overwritten
+  };
+
+  // ---- the ring: NS-1 blocks in flight ----
+  const int nblk = (t1 - t0 + RCH - 1) / RCH;
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nblk) copy_block(t0 + j * RCH, j);
+  for (int j = 0; j < nblk; ++j) {
+    // this wave's copies of block j have landed once at most the copies of
+    // the blocks issued after it are outstanding (2 NI per block)
+    const int ahead = min(NS - 2, nblk - 1 - j);
+    if (NS >= 4 && ahead >= 2) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(4 * NI));
+    } else if (NS >= 3 && ahead >= 1) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * NI));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+    }
+    // block j is in LDS for every wave, and every wave is done reading block
+    // j-1 (its buffer is refilled next).  A bare s_barrier: a workgroup fence
+    // would also wait for the copies still in flight.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + NS - 1 < nblk) copy_block(t0 + (j + NS - 1) * RCH, (j + NS - 1) % NS);
+    compute_block(t0 + j * RCH, j % NS);
   }
 
   if (APPEND && wave == 0 && newpos >= t0 && newpos < t1) {  // the appended rows join the cache
@@ -228,7 +296,6 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
       *reinterpret_cast<u32x4*>(vdst + 8 * lane) = ld16(vnew_row + 8 * lane);
     }
   }
-  if (!computes) return;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
@@ -265,15 +332,21 @@ hipError_t launch_decode_wide_bf16(const void* q, void* k_cache, void* v_cache,
   auto kn = static_cast<const __bf16*>(k_new);
   auto vn = static_cast<const __bf16*>(v_new);
   const PagedArgs pg = paged ? *paged : PagedArgs{nullptr, 16, 0, 1};
-  const int hbk = plan.head_blocks;
+  // one wave per 16-head block
 #define GQA_WIDE(DD, AP, PG, WW)                                                                  \
-  hipLaunchKernelGGL((decode_wide_bf16_kernel<DD, AP, PG, WW>), grid, dim3(64 * WW), 0, stream,    \
-                     qp, kp, vp, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, \
-                     plan.parts, plan.head_blocks, scale_log2, kn, vn, ws.lens, pg)
+  hipLaunchKernelGGL((decode_wide_bf16_kernel<DD, AP, PG, WW, kSub, kRing>), grid,               \
+                     dim3(64 * WW), 0, stream, qp, kp, vp, seq_lens, ws.part_acc, ws.part_ml, H, K, \
+                     S_max, plan.part_tokens, plan.parts, scale_log2, kn, vn, ws.lens, pg)
 #define GQA_WIDE_W(DD, AP, PG)                                                                   \
-  if (hbk <= 2) GQA_WIDE(DD, AP, PG, 2);                                                          \
-  else if (hbk <= 4) GQA_WIDE(DD, AP, PG, 4);                                                     \
-  else GQA_WIDE(DD, AP, PG, 8);
+  switch (plan.head_blocks) {                                                                     \
+    case 2: GQA_WIDE(DD, AP, PG, 2); break;                                                       \
+    case 3: GQA_WIDE(DD, AP, PG, 3); break;                                                       \
+    case 4: GQA_WIDE(DD, AP, PG, 4); break;                                                       \
+    case 5: GQA_WIDE(DD, AP, PG, 5); break;                                                       \
+    case 6: GQA_WIDE(DD, AP, PG, 6); break;                                                       \
+    case 7: GQA_WIDE(DD, AP, PG, 7); break;                                                       \
+    default: GQA_WIDE(DD, AP, PG, 8); break;                                                      \
+  }
 #define GQA_WIDE_D(DD)                                                                           \
   if (paged) {                                                                                    \
     if (k_new) { GQA_WIDE_W(DD, true, true) } else { GQA_WIDE_W(DD, false, true) }                \

@@ -61,6 +61,10 @@ WORKLOADS = {
     "decode_long_131k": Workload(
         "decode_long_131k", "decode", B=4, H=32, K=8, d=128, dtype="bf16", L=131072,
         q_scale=2.0, note="131072-token context, q scaled by 2"),
+    "decode_mqa_71h": Workload(
+        "decode_mqa_71h", "decode", B=32, H=71, K=1, d=64, dtype="bf16", L=32768,
+        append=True, note="multi-query layer: 71 query heads sharing one KV head (the Falcon-7B head "
+                          "layout), d=64, 32768 cached tokens + 1 appended"),
     "decode_paged_llama3_8b": Workload(
         "decode_paged_llama3_8b", "decode", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
         append=True, note="decode_llama3_8b over a paged cache: 16-token blocks in shuffled order",

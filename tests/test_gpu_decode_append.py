@@ -96,6 +96,27 @@ def test_fused_step_full_workload():
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
 
 
+def test_fused_step_mqa_workload():
+    """The multi-query workload (71 query heads on one KV head, d = 64, 32768
+    cached rows) in the launch configuration the benchmark times: the fused
+    append + decode through the one-workgroup-per-group pass; every appended
+    row checked, sampled sequences against the oracle."""
+    w = WORKLOADS["decode_mqa_71h"]
+    inp = workload_inputs(w, seed=0)
+    note("fused step on the 71-head multi-query layer")
+    out, kc, vc, sl = _fused(inp, w.L + 1)
+    assert sl.cpu().tolist() == [w.L + 1] * w.B
+    assert torch.equal(kc[:, :, w.L].cpu(), inp["k_new"]) and torch.equal(vc[:, :, w.L].cpu(), inp["v_new"])
+    for b in (0, 13, w.B - 1):
+        k2, v2, s2 = kv_append_ref(inp["k_new"][b:b + 1].float().numpy(), inp["v_new"][b:b + 1].float().numpy(),
+                                   inp["k_cache"][b:b + 1].float().numpy(), inp["v_cache"][b:b + 1].float().numpy(),
+                                   inp["seq_lens"][b:b + 1].numpy())
+        ref = decode_ref(f64(inp["q"][b:b + 1]), k2, v2, s2, scale_of(w.d))
+        r = report(f"fused mqa b={b}", f64(out[b:b + 1]), ref)
+        assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+        assert r["max_abs"] <= bf16_bound(ref, float(np.abs(v2[0, :, :w.L + 1]).max()))
+
+
 def test_many_fused_steps_until_a_cache_fills():
     """40 consecutive fused decode steps on a ragged batch whose shortest
     cache fills up on the way: after every step the lengths match the
