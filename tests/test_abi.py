@@ -389,3 +389,28 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         B.load_library(tmp_path / "nope.so")
+
+
+def test_library_has_every_kernel_launch_stub(lib):
+    """No kernel's host launch stub is left undefined in the built library."""
+    import subprocess
+    from grouped_query_kv_amd.build import LIB
+    r = subprocess.run(["nm", "-u", str(LIB)], capture_output=True, text=True, check=True)
+    assert "__device_stub__" not in r.stdout
+
+
+def test_build_rejects_undefined_launch_stub(tmp_path):
+    """The build's link check fails on a library that references a launch
+    stub it does not define (what a silently dropped host stub looks like)."""
+    import shutil
+    import subprocess
+    from grouped_query_kv_amd.build import _check_launch_stubs
+    if shutil.which("gcc") is None or shutil.which("nm") is None:
+        pytest.skip("gcc / nm not available")
+    src = tmp_path / "stub.c"
+    src.write_text("extern void _ZN3gqa20__device_stub__probeEv(void);\n"
+                   "void call_it(void) { _ZN3gqa20__device_stub__probeEv(); }\n")
+    so = tmp_path / "libstub.so"
+    subprocess.run(["gcc", "-shared", "-fPIC", "-o", str(so), str(src)], check=True)
+    with pytest.raises(RuntimeError, match="launch stubs are undefined"):
+        _check_launch_stubs(so)
