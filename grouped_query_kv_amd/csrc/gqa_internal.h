@@ -70,7 +70,8 @@ struct PagedArgs {
 
 // Partition pass, bf16 inputs, matrix-core (MFMA) contraction.  With
 // k_new/v_new non-null the step's append is fused in (caches are written);
-// with `paged` non-null the caches are block pools (no fused append).
+// with `paged` non-null the caches are block pools (with or without the
+// fused append).  Groups of more than 16 query heads go to the wide pass.
 hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const int32_t* seq_lens, const DecodeWorkspace& ws,
                                     const DecodePlan& plan, int B, int H, int K, int S_max, int d,
@@ -78,9 +79,10 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
                                     const PagedArgs* paged, hipStream_t stream);
 
 // Partition pass for groups of 2 to 8 blocks of 16 query heads (bf16): one
-// workgroup of waves per (partition, KV head) loads each K/V chunk once into
-// LDS for all of the group's heads.  Same arguments and partial state as
-// launch_decode_split_bf16, which routes such groups here.
+// workgroup per (partition, KV head, sequence), one wave per head block,
+// copies each K/V chunk once into LDS for all of the group's heads.  Same
+// arguments and partial state as launch_decode_split_bf16, which routes such
+// groups here.
 bool decode_wide_supported(int head_blocks);
 hipError_t launch_decode_wide_bf16(const void* q, void* k_cache, void* v_cache,
                                    const int32_t* seq_lens, const DecodeWorkspace& ws,
