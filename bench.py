@@ -68,12 +68,28 @@ def parse():
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
+def sources_code_sha256(paths) -> str:
+    """SHA-256 of the code in the given source files (repository-relative),
+    with C/C++ comments removed and whitespace runs collapsed, so that an
+    edit of comments alone leaves it unchanged."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for src in paths:
+        with open(os.path.join(ROOT, src), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch recorded from rocprofv3 counters for `kernel` on
     `workload` (profiles/traffic.json), or None when nothing was recorded for
-    that pair or the kernel's sources changed since."""
-    import hashlib
-
+    that pair or the code of the kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -82,11 +98,7 @@ def recorded_traffic(kernel: str, workload: str):
         return None
     if rec.get("workload") != workload:
         return None
-    h = hashlib.sha256()
-    for src in rec["sources"]:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != rec["sources_sha256"]:
+    if sources_code_sha256(rec["sources"]) != rec["sources_code_sha256"]:
         return None
     return int(rec["read_bytes"] + rec["write_bytes"])
 

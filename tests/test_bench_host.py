@@ -1,0 +1,39 @@
+"""Host-side logic of bench.py that needs no GPU: the key under which HBM
+traffic counters are recorded (profiles/traffic.json)."""
+import json
+import sys
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent.parent
+sys.path.insert(0, str(ROOT))
+import bench  # noqa: E402
+
+
+def test_code_hash_ignores_comments_and_whitespace(tmp_path):
+    a = tmp_path / "a.hip"
+    a.write_text("// header\nint f(int x) {  /* twice */ return 2 * x; }\n")
+    h0 = bench.sources_code_sha256([str(a)])
+    a.write_text("// a different header\n\nint f(int x) {\n  // doubled\n  return 2 * x;\n}\n")
+    assert bench.sources_code_sha256([str(a)]) == h0
+    a.write_text("int f(int x) { return 3 * x; }\n")
+    assert bench.sources_code_sha256([str(a)]) != h0
+
+
+def test_code_hash_separates_files(tmp_path):
+    a, b = tmp_path / "a.h", tmp_path / "b.h"
+    a.write_text("int x;")
+    b.write_text("int y;")
+    assert bench.sources_code_sha256([str(a), str(b)]) != bench.sources_code_sha256([str(b), str(a)])
+
+
+def test_traffic_records_are_well_formed():
+    """Each record names its workload, existing source files, a code hash
+    and byte counts; a record is only reported for its own workload."""
+    recs = json.loads((ROOT / "profiles" / "traffic.json").read_text())
+    for kernel, rec in recs.items():
+        if not isinstance(rec, dict):
+            continue
+        assert all((ROOT / s).is_file() for s in rec["sources"])
+        assert len(rec["sources_code_sha256"]) == 64
+        assert rec["read_bytes"] > 0 and rec["write_bytes"] > 0
+        assert bench.recorded_traffic(kernel, "no_such_workload") is None
