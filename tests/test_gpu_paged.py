@@ -296,11 +296,12 @@ def test_paged_fused_append_matches_unfused(B, H, K, d, lens, bs, s_max, steps):
     _fused_vs_unfused(inp, p, p["block_table"], lens, steps, seed=73)
 
 
-def test_paged_fused_append_full_table_and_invalid_id():
+@pytest.mark.parametrize("H,K", [(32, 8), (96, 2)])   # G = 4; G = 48 (the wide pass)
+def test_paged_fused_append_full_table_and_invalid_id(H, K):
     """A full table and an invalid block id at the append position: that
     sequence is attended as it is and keeps its length, as in the
     standalone append."""
-    B, H, K, d, bs = 4, 32, 8, 128, 16
+    B, d, bs = 4, 128, 16
     lens = [0, 15, 32, 48]
     inp = decode_inputs(B, H, K, d, "bf16", seed=74, lens=lens, s_max=48)
     p = paged_layout(inp, bs, seed=75, spare_blocks=1)
