@@ -35,6 +35,8 @@ CASES = [
     (1, 10, 5, 150, 128, 150),   # G = 2: four 16-position blocks per workgroup
     (2, 10, 2, 90, 64, 96),      # G = 5: three idle row tiles
     (1, 4, 4, 300, 128, 300),    # G = 1 (MHA): eight blocks per workgroup, S not a multiple of 128
+    (1, 71, 1, 90, 64, 96),      # G = 71 (MQA): nine head chunks, the last holding 7 heads
+    (1, 48, 2, 70, 128, 70),     # G = 24: three head chunks
 ]
 
 
