@@ -334,6 +334,9 @@ hipError_t launch_decode_split_int8(const void* q, void* k_codes, void* v_codes,
                                     const DecodeWorkspace& ws, const DecodePlan& plan, int B, int H,
                                     int K, int S_max, int d, float scale_log2, const void* k_new,
                                     const void* v_new, hipStream_t stream) {
+  if (decode_wide_supported(plan.head_blocks))  // G > 16: one code read for all head blocks
+    return launch_decode_wide_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, ws, plan, B,
+                                   H, K, S_max, d, scale_log2, k_new, v_new, stream);
   const dim3 grid(plan.parts, K * plan.head_blocks, B);
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<int8_t*>(k_codes);

@@ -1,0 +1,365 @@
+// Decode partition pass over an int8 KV cache for groups of more than 16
+// query heads.
+//
+// The int8 pass (decode_int8.hip) runs one wave per 16-head block of a group,
+// so a group of G > 16 heads (multi-query shapes) would read every K/V code
+// ceil(G / 16) times.  As in the wide bf16 pass (decode_wide_bf16.hip; the
+// pages' rule that a group's shared KV block is loaded once for all of its
+// heads, pinghaoyang.com.cn "GQA 完全拆解", section 工程实现), one workgroup
+// with one wave per head block owns a partition of one KV head; the waves
+// copy each 32-position chunk of codes and scales once into LDS, straight
+// from HBM (global_load_lds_dwordx4), through a ring of two buffers, and each
+// wave multiplies it with its own heads.  The arithmetic is the int8 pass's:
+//     s_j  = scale * (q . c^K_j) * sk_j,
+//     acc += sum_j 2^(s_j - m) * sv_j * c^V_j,   l += sum_j 2^(s_j - m),
+// with codes converted to bf16 in registers (exact) and the value scale
+// folded into each position's bf16 weight, and the same quantising append
+// (the new rows go through a workspace slot).
+//
+// Operands from LDS:
+//  * K: lane (n, g) at k-step s carries head dimensions (d/4) g + 8 s .. +7
+//    of row 16 mt + n (the int8 pass's relabelling of the contraction index,
+//    applied to Q alike): one 16-byte read covers two k-steps.
+//  * V: ds_read_b64_tr_b8 -- within each 16-lane group, lanes 2e and 2e+1
+//    supply the two 8-byte halves of row e of an 8 x 16-byte block and lane i
+//    receives byte i of every row.  Row e points at the lane's contraction
+//    slot e (positions 4g + e and 16 + 4g + e - 4) and dims 16t .. 16t+15, so
+//    one read gives lane (n, g) the codes of dim 16t + n for all eight of its
+//    slots: the whole B operand.
+// The 16-byte pieces of each LDS code row are XOR-swizzled by row (each lane
+// copies the global piece that belongs in its slot) so that the rows one
+// transposed read touches fall in distinct banks.
+#include "common.h"
+#include "gqa_internal.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kChunk = 32;
+
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+__device__ __forceinline__ uint2 lds_read_tr8(const int8_t* p) {
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2*)(__attribute__((address_space(3))) void*)(const_cast<int8_t*>(p)));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Eight int8 codes (two little-endian dwords) -> one bf16x8 operand (exact).
+__device__ __forceinline__ bf16x8 codes_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const float f0 = (float)((int32_t)(lo << 24) >> 24), f1 = (float)((int32_t)(lo << 16) >> 24);
+  const float f2 = (float)((int32_t)(lo << 8) >> 24), f3 = (float)((int32_t)lo >> 24);
+  const float f4 = (float)((int32_t)(hi << 24) >> 24), f5 = (float)((int32_t)(hi << 16) >> 24);
+  const float f6 = (float)((int32_t)(hi << 8) >> 24), f7 = (float)((int32_t)hi >> 24);
+  return as_bf16x8(u32x4{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3), pack_bf16x2(f4, f5), pack_bf16x2(f6, f7)});
+}
+
+// Physical 16-byte piece of logical piece c in LDS row r is c ^ piece_swizzle(r):
+// the rows {4g .. 4g+3, 16+4g .. 16+4g+3} of one transposed read get distinct
+// pieces (and two such groups distinct (row parity, piece) pairs).
+template <int D>
+__device__ __forceinline__ int piece_swizzle(int r) {
+  if (D == 128) return ((r & 3) ^ ((r >> 2) & 1) ^ (((r >> 4) & 1) << 2)) & 7;
+  return (((r >> 1) ^ (r >> 2)) & 1) | (((r >> 4) & 1) << 1);
+}
+
+template <int D, bool APPEND, int W>
+__global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
+    const __bf16* __restrict__ q, int8_t* __restrict__ kc, int8_t* __restrict__ vc,
+    float* __restrict__ ks, float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ part_acc, float* __restrict__ part_ml, int H, int K, int S_max,
+    int part_tokens, int parts, float scale_log2, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, uint8_t* __restrict__ slots) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int KSTEPS = D / 32;
+  constexpr int NTILES = D / 16;
+  constexpr int KSEG = D / 4;               // bytes of a K row per lane
+  constexpr int KPIECES = KSEG / 16;        // 16-byte pieces of that segment
+  constexpr int CPR = D / 16;               // 16-byte pieces per code row
+  constexpr int TILE = kChunk * D;          // bytes of a staged code tile
+  constexpr int NINST = TILE / 1024;        // 1 KB copies per tensor and chunk
+  constexpr int NI = (NINST + W - 1) / W;   // copies per wave per tensor and chunk
+  constexpr bool SURPLUS = NINST % W != 0;
+
+  __shared__ __attribute__((aligned(16))) int8_t kq[2][TILE];
+  __shared__ __attribute__((aligned(16))) int8_t vq[2][TILE];
+  __shared__ __attribute__((aligned(16))) float ksc[2][kChunk];
+  __shared__ __attribute__((aligned(16))) float vsc[2][kChunk];
+  // target of the surplus copies (they repeat a real copy; never read)
+  __shared__ __attribute__((aligned(16))) int8_t sink[SURPLUS ? 1024 : 16];
+
+  const int p = blockIdx.x;
+  const int k = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = H / K;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int hb = wave;  // this wave's block of 16 heads
+
+  const int L_in = seq_lens[b];
+  int L = L_in, newpos = -1;
+  if (APPEND) {
+    if (L_in < S_max) {
+      newpos = L_in;
+      L = L_in + 1;
+    }
+    if (p == 0 && k == 0 && threadIdx.x == 0) lens_out[b] = L;
+  }
+  const int pt_b = balanced_part_tokens(L, part_tokens);
+  const int t0 = p * pt_b;
+  if (t0 >= L) return;  // uniform over the workgroup
+  const int t1 = min(t0 + pt_b, L);
+  const int last = t1 - 1;
+
+  const int hq = hb * 16 + n;
+  const bool hq_ok = hq < G;
+  bf16x8 qf[KSTEPS];
+  {
+    const __bf16* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D + KSEG * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(hq_ok ? ld16(qrow + 8 * s) : zero_u32x4());
+  }
+
+  const size_t head_row0 = ((size_t)b * K + k) * (size_t)S_max;  // first row of (b, k)
+  int8_t* kbase = kc + head_row0 * D;
+  int8_t* vbase = vc + head_row0 * D;
+  float* ksb = ks + head_row0;
+  float* vsb = vs + head_row0;
+
+  // The new rows (fused append): quantised by the first wave into this
+  // workgroup's workspace slot = [K codes (D) | V codes (D) | K scales (4) |
+  // V scales (4)], the scale groups being the 4-aligned group around the new
+  // position; the copies take the slot instead of the cache for it.
+  const bool has_new = APPEND && newpos >= t0 && newpos < t1;  // uniform
+  const int s0_new = has_new ? (newpos & ~3) : -4;
+  int8_t* slot = reinterpret_cast<int8_t*>(slots) + (APPEND ? ((size_t)b * K + k) * (2 * D + 32) : 0);
+  float* slot_sc = reinterpret_cast<float*>(slot + 2 * D);
+  if (has_new) {
+    if (wave == 0) {
+      constexpr int E = D / 64;  // elements per lane
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const __bf16* src = (r == 0 ? k_new : v_new) + ((size_t)b * K + k) * D + E * lane;
+        float x[E];
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          x[e] = static_cast<float>(src[e]);
+          amax = fmaxf(amax, fabsf(x[e]));
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float inv = amax > 0.f ? int8_inv(amax) : 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) slot[r * D + E * lane + e] = amax > 0.f ? (int8_t)int8_code(x[e], inv) : 0;
+        if (lane < 4) {  // cached scales before the new position, 0 after it
+          const int pos = s0_new + lane;
+          const float* rs = r == 0 ? ksb : vsb;
+          slot_sc[4 * r + lane] = pos < newpos ? rs[pos] : pos == newpos ? (amax > 0.f ? int8_scale(amax) : 0.f) : 0.f;
+        }
+      }
+    }
+    __syncthreads();  // the slot is written before any wave copies from it
+  }
+
+  // Copy slot c of this wave: instruction i = wave + c W of a chunk (surplus
+  // slots, i >= NINST, repeat instruction i - NINST into the sink); lane l
+  // fills LDS piece 64 i + l = row crow, physical piece l % CPR.
+  int crow[NI], ckoff[NI], cvoff[NI];
+#pragma unroll
+  for (int c = 0; c < NI; ++c) {
+    const int i = (wave + c * W) % NINST;
+    const int pc = 64 * i + lane;
+    crow[c] = pc / CPR;
+    const int ph = pc % CPR, sw = piece_swizzle<D>(crow[c]);
+    ckoff[c] = 16 * (ph ^ sw);
+    cvoff[c] = 16 * (ph ^ sw);
+  }
+  auto copy_chunk = [&](int c0, int buf) {
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      const int i = wave + c * W;  // uniform
+      const int tok = min(c0 + crow[c], last);
+      const bool nw = APPEND && tok == newpos;
+      const int8_t* ksrc = (nw ? slot : kbase + (size_t)tok * D) + ckoff[c];
+      const int8_t* vsrc = (nw ? slot + D : vbase + (size_t)tok * D) + cvoff[c];
+      int8_t* kd = i < NINST ? &kq[buf][1024 * i] : sink;
+      int8_t* vd = i < NINST ? &vq[buf][1024 * i] : sink;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(ksrc),
+                                       (__attribute__((address_space(3))) void*)kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(vsrc),
+                                       (__attribute__((address_space(3))) void*)vd, 16, 0, 0);
+    }
+    // scales: lanes 0..7 of waves 0 (K) and 1 (V) copy the chunk's 32 scales,
+    // 4 per lane (groups past the partition end repeat its last group)
+    if (wave < 2 && lane < kChunk / 4) {
+      const int s0 = min(c0 + 4 * lane, last & ~3);
+      const float* src = APPEND && s0 == s0_new ? slot_sc + 4 * wave : (wave == 0 ? ksb : vsb) + s0;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src),
+                                       (__attribute__((address_space(3))) void*)(wave == 0 ? ksc[buf] : vsc[buf]),
+                                       16, 0, 0);
+    }
+  };
+
+  // loop-invariant LDS offsets: K piece w of row 16mt + n; transposed V row
+  // of contraction slot e = n / 2 of the lane's group
+  int ka_off[2][KPIECES];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int w = 0; w < KPIECES; ++w) {
+      const int r = 16 * mt + n;
+      ka_off[mt][w] = r * D + 16 * ((KPIECES * g + w) ^ piece_swizzle<D>(r));
+    }
+  const int tr_e = n >> 1;
+  const int tr_row = tr_e < 4 ? 4 * g + tr_e : 12 + 4 * g + tr_e;
+  const int tr_sw = piece_swizzle<D>(tr_row);
+  const int tr_off = tr_row * D + 8 * (n & 1);
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;  // this lane's share of head n's denominator
+  f32x4 acc[NTILES];
+#pragma unroll
+  for (int t = 0; t < NTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr float kLazy = 8.f;  // see the bf16 pass: lazy running max
+
+  copy_chunk(t0, 0);
+  int buf = 0;
+  for (int c0 = t0; c0 < t1; c0 += kChunk, buf ^= 1) {
+    // this wave's copies of the chunk have landed; after the barrier every
+    // wave's have, and every wave is done with the other buffer
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (c0 + kChunk < t1) copy_chunk(c0 + kChunk, buf ^ 1);
+
+    // ---- S^T = K . Q^T (codes from LDS) ----
+    f32x4 st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < KPIECES; ++w) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&kq[buf][ka_off[mt][w]]);
+        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(a[0], a[1]), qf[2 * w], st[mt], 0, 0, 0);
+        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(a[2], a[3]), qf[2 * w + 1], st[mt], 0, 0, 0);
+      }
+    }
+    // ---- online softmax for head n over positions {16mt + 4g + i} ----
+    float x[8], sv[8];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const f32x4 skv = *reinterpret_cast<const f32x4*>(&ksc[buf][16 * mt + 4 * g]);
+      const f32x4 svv = *reinterpret_cast<const f32x4*>(&vsc[buf][16 * mt + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = c0 + 16 * mt + 4 * g + i < t1;
+        const float xv = ok ? st[mt][i] * (skv[i] * scale_log2) : -INFINITY;
+        x[4 * mt + i] = xv;
+        sv[4 * mt + i] = ok ? svv[i] : 0.f;  // rows past the end never reach the sum
+        lmax = fmaxf(lmax, xv);
+      }
+    }
+    if (__any(lmax > m_run + kLazy)) {
+      float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
+      }
+    }
+    uint32_t pw[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const float e0 = fast_exp2(x[j] - m_run);
+      const float e1 = fast_exp2(x[j + 1] - m_run);
+      l_run += e0 + e1;
+      pw[j / 2] = pack_bf16x2(e0 * sv[j], e1 * sv[j + 1]);
+    }
+    // ---- O += P . V: transposed code reads, converted to bf16 operands ----
+    const bf16x8 pa = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+    for (int t = 0; t < NTILES; ++t) {
+      const uint2 wv = lds_read_tr8(&vq[buf][tr_off + 16 * (t ^ tr_sw)]);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, codes_to_bf16x8(wv.x, wv.y), acc[t], 0, 0, 0);
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  if (APPEND && has_new && wave == 0) {  // the appended rows join the cache
+    if (lane < 2 * (D / 16)) {
+      const int r = lane / (D / 16), w = lane % (D / 16);
+      *reinterpret_cast<u32x4*>((r == 0 ? kbase : vbase) + (size_t)newpos * D + 16 * w) =
+          ld16(slot + r * D + 16 * w);
+    }
+    if (lane < 2) (lane == 0 ? ksb : vsb)[newpos] = slot_sc[4 * lane + (newpos - s0_new)];
+  }
+
+  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hl = 4 * g + i;
+    if (hb * 16 + hl < G) {
+      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+#pragma unroll
+      for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
+    }
+  }
+  if (g == 0 && hq_ok) {
+    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    ml[0] = m_run;
+    ml[1] = l_run;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_wide_int8(const void* q, void* k_codes, void* v_codes, float* k_scales,
+                                   float* v_scales, const int32_t* seq_lens,
+                                   const DecodeWorkspace& ws, const DecodePlan& plan, int B, int H,
+                                   int K, int S_max, int d, float scale_log2, const void* k_new,
+                                   const void* v_new, hipStream_t stream) {
+  const dim3 grid(plan.parts, K, B);
+  auto qp = static_cast<const __bf16*>(q);
+  auto kp = static_cast<int8_t*>(k_codes);
+  auto vp = static_cast<int8_t*>(v_codes);
+  auto kn = static_cast<const __bf16*>(k_new);
+  auto vn = static_cast<const __bf16*>(v_new);
+#define GQA_WI8(DD, AP, WW)                                                                      \
+  hipLaunchKernelGGL((decode_wide_int8_kernel<DD, AP, WW>), grid, dim3(64 * WW), 0, stream, qp,  \
+                     kp, vp, k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, \
+                     plan.part_tokens, plan.parts, scale_log2, kn, vn, ws.lens, ws.new_rows)
+#define GQA_WI8_W(DD, AP)                                                                        \
+  switch (plan.head_blocks) {                                                                     \
+    case 2: GQA_WI8(DD, AP, 2); break;                                                            \
+    case 3: GQA_WI8(DD, AP, 3); break;                                                            \
+    case 4: GQA_WI8(DD, AP, 4); break;                                                            \
+    case 5: GQA_WI8(DD, AP, 5); break;                                                            \
+    case 6: GQA_WI8(DD, AP, 6); break;                                                            \
+    case 7: GQA_WI8(DD, AP, 7); break;                                                            \
+    default: GQA_WI8(DD, AP, 8); break;                                                           \
+  }
+  if (d == 128) {
+    if (k_new) { GQA_WI8_W(128, true) } else { GQA_WI8_W(128, false) }
+  } else {
+    if (k_new) { GQA_WI8_W(64, true) } else { GQA_WI8_W(64, false) }
+  }
+#undef GQA_WI8_W
+#undef GQA_WI8
+  return hipGetLastError();
+}
+
+}  // namespace gqa

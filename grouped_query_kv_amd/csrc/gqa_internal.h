@@ -117,6 +117,17 @@ hipError_t launch_decode_split_int8(const void* q, void* k_codes, void* v_codes,
                                     int K, int S_max, int d, float scale_log2, const void* k_new,
                                     const void* v_new, hipStream_t stream);
 
+// The int8 partition pass for groups of 2 to 8 blocks of 16 query heads:
+// one workgroup per (partition, KV head, sequence), one wave per head block,
+// codes and scales copied once into LDS for all of the group's heads.  Same
+// arguments and partial state as launch_decode_split_int8, which routes such
+// groups here.
+hipError_t launch_decode_wide_int8(const void* q, void* k_codes, void* v_codes, float* k_scales,
+                                   float* v_scales, const int32_t* seq_lens,
+                                   const DecodeWorkspace& ws, const DecodePlan& plan, int B, int H,
+                                   int K, int S_max, int d, float scale_log2, const void* k_new,
+                                   const void* v_new, hipStream_t stream);
+
 // Combine pass: partials -> out (fp32 or bf16).  lens_from_ws: lengths come
 // from the workspace (fused append) and are published to seq_lens.
 hipError_t launch_decode_combine(const DecodeWorkspace& ws, int32_t* seq_lens, void* out,
