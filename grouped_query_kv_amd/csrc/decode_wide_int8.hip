@@ -16,19 +16,14 @@
 // folded into each position's bf16 weight, and the same quantising append
 // (the new rows go through a workspace slot).
 //
-// Operands from LDS:
-//  * K: lane (n, g) at k-step s carries head dimensions (d/4) g + 8 s .. +7
-//    of row 16 mt + n (the int8 pass's relabelling of the contraction index,
-//    applied to Q alike): one 16-byte read covers two k-steps.
-//  * V: ds_read_b64_tr_b8 -- within each 16-lane group, lanes 2e and 2e+1
-//    supply the two 8-byte halves of row e of an 8 x 16-byte block and lane i
-//    receives byte i of every row.  Row e points at the lane's contraction
-//    slot e (positions 4g + e and 16 + 4g + e - 4) and dims 16t .. 16t+15, so
-//    one read gives lane (n, g) the codes of dim 16t + n for all eight of its
-//    slots: the whole B operand.
-// The 16-byte pieces of each LDS code row are XOR-swizzled by row (each lane
-// copies the global piece that belongs in its slot) so that the rows one
-// transposed read touches fall in distinct banks.
+// Each chunk's codes are converted to bf16 once, by all threads of the
+// workgroup together (each thread a share of the 16-byte pieces), into bf16
+// tiles in LDS laid out as in the wide bf16 pass; every wave then reads its
+// operands from there exactly as that pass does (K as 16-byte operand reads,
+// V with transposed ds_read_b64_tr_b16 reads), so the conversion work is not
+// repeated per head block.  The 16-byte pieces of the staged int8 rows and
+// the 16-byte chunks of the bf16 rows are XOR-swizzled by row (each lane
+// copies the global piece that belongs in its slot).
 #include "common.h"
 #include "gqa_internal.h"
 
@@ -37,31 +32,26 @@ namespace {
 
 constexpr int kChunk = 32;
 
-typedef __attribute__((ext_vector_type(2))) int i32x2;
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-__device__ __forceinline__ uint2 lds_read_tr8(const int8_t* p) {
-  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (lds_i32x2*)(__attribute__((address_space(3))) void*)(const_cast<int8_t*>(p)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) void*)(const_cast<uint16_t*>(p)));
   return __builtin_bit_cast(uint2, r);
 }
 
-// Eight int8 codes (two little-endian dwords) -> one bf16x8 operand (exact).
-__device__ __forceinline__ bf16x8 codes_to_bf16x8(uint32_t lo, uint32_t hi) {
-  const float f0 = (float)((int32_t)(lo << 24) >> 24), f1 = (float)((int32_t)(lo << 16) >> 24);
-  const float f2 = (float)((int32_t)(lo << 8) >> 24), f3 = (float)((int32_t)lo >> 24);
-  const float f4 = (float)((int32_t)(hi << 24) >> 24), f5 = (float)((int32_t)(hi << 16) >> 24);
-  const float f6 = (float)((int32_t)(hi << 8) >> 24), f7 = (float)((int32_t)hi >> 24);
-  return as_bf16x8(u32x4{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3), pack_bf16x2(f4, f5), pack_bf16x2(f6, f7)});
+// Four int8 codes (one little-endian dword) -> four bf16 values (exact).
+__device__ __forceinline__ uint2 codes_to_bf16x4(uint32_t w) {
+  const float f0 = (float)((int32_t)(w << 24) >> 24), f1 = (float)((int32_t)(w << 16) >> 24);
+  const float f2 = (float)((int32_t)(w << 8) >> 24), f3 = (float)((int32_t)w >> 24);
+  return uint2{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
 }
 
-// Physical 16-byte piece of logical piece c in LDS row r is c ^ piece_swizzle(r):
-// the rows {4g .. 4g+3, 16+4g .. 16+4g+3} of one transposed read get distinct
-// pieces (and two such groups distinct (row parity, piece) pairs).
+// Physical 16-byte piece of logical piece c in a staged int8 row r.
 template <int D>
 __device__ __forceinline__ int piece_swizzle(int r) {
-  if (D == 128) return ((r & 3) ^ ((r >> 2) & 1) ^ (((r >> 4) & 1) << 2)) & 7;
-  return (((r >> 1) ^ (r >> 2)) & 1) | (((r >> 4) & 1) << 1);
+  return r & (D / 16 - 1);
 }
 
 template <int D, bool APPEND, int W>
@@ -74,9 +64,10 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;
   constexpr int NTILES = D / 16;
-  constexpr int KSEG = D / 4;               // bytes of a K row per lane
-  constexpr int KPIECES = KSEG / 16;        // 16-byte pieces of that segment
+  constexpr int LPR = D / 8;                // 16-byte chunks per bf16 row
   constexpr int CPR = D / 16;               // 16-byte pieces per code row
+  constexpr int NPIECE = kChunk * CPR;      // pieces per staged code tile
+  constexpr int NCONV = (NPIECE + 64 * W - 1) / (64 * W);  // pieces per thread per tensor
   constexpr int TILE = kChunk * D;          // bytes of a staged code tile
   constexpr int NINST = TILE / 1024;        // 1 KB copies per tensor and chunk
   constexpr int NI = (NINST + W - 1) / W;   // copies per wave per tensor and chunk
@@ -86,6 +77,9 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   __shared__ __attribute__((aligned(16))) int8_t vq[2][TILE];
   __shared__ __attribute__((aligned(16))) float ksc[2][kChunk];
   __shared__ __attribute__((aligned(16))) float vsc[2][kChunk];
+  // the current chunk as bf16: K chunk c ^ (row % (D/8)), V chunk ^ 2 (row % (D/16))
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * D];
   // target of the surplus copies (they repeat a real copy; never read)
   __shared__ __attribute__((aligned(16))) int8_t sink[SURPLUS ? 1024 : 16];
 
@@ -118,9 +112,10 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   const bool hq_ok = hq < G;
   bf16x8 qf[KSTEPS];
   {
-    const __bf16* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D + KSEG * g;
+    const __bf16* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) qf[s] = as_bf16x8(hq_ok ? ld16(qrow + 8 * s) : zero_u32x4());
+    for (int s = 0; s < KSTEPS; ++s)
+      qf[s] = as_bf16x8(hq_ok ? ld16(qrow + 32 * s + 8 * g) : zero_u32x4());
   }
 
   const size_t head_row0 = ((size_t)b * K + k) * (size_t)S_max;  // first row of (b, k)
@@ -204,20 +199,45 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     }
   };
 
-  // loop-invariant LDS offsets: K piece w of row 16mt + n; transposed V row
-  // of contraction slot e = n / 2 of the lane's group
-  int ka_off[2][KPIECES];
+  // conversion share of this thread: staged piece pc = tid + 64 W i
+  // (row pc / CPR, logical piece pc % CPR) -> bf16 chunks 2 lp, 2 lp + 1
+  int cv_src[NCONV], cv_k[NCONV], cv_v[NCONV];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int i = 0; i < NCONV; ++i) {
+    const int pc = min((int)threadIdx.x + 64 * W * i, NPIECE - 1);  // extra threads redo the last piece
+    const int r = pc / CPR, lp = pc % CPR;
+    cv_src[i] = r * D + 16 * (lp ^ piece_swizzle<D>(r));
+    cv_k[i] = r * D + 8 * ((2 * lp) ^ (r & (LPR - 1)));        // chunk 2 lp; 2 lp + 1 is chunk ^ 1
+    cv_v[i] = r * D + 8 * ((2 * lp) ^ ((r & (LPR / 2 - 1)) << 1));
+  }
+  auto convert = [&](int buf) {
 #pragma unroll
-    for (int w = 0; w < KPIECES; ++w) {
-      const int r = 16 * mt + n;
-      ka_off[mt][w] = r * D + 16 * ((KPIECES * g + w) ^ piece_swizzle<D>(r));
+    for (int i = 0; i < NCONV; ++i) {
+      const u32x4 ck = *reinterpret_cast<const u32x4*>(&kq[buf][cv_src[i]]);
+      const u32x4 cvv = *reinterpret_cast<const u32x4*>(&vq[buf][cv_src[i]]);
+      const uint2 k0 = codes_to_bf16x4(ck[0]), k1 = codes_to_bf16x4(ck[1]);
+      const uint2 k2 = codes_to_bf16x4(ck[2]), k3 = codes_to_bf16x4(ck[3]);
+      const uint2 v0 = codes_to_bf16x4(cvv[0]), v1 = codes_to_bf16x4(cvv[1]);
+      const uint2 v2 = codes_to_bf16x4(cvv[2]), v3 = codes_to_bf16x4(cvv[3]);
+      // chunk 2lp ^ s lands at s, chunk 2lp+1 at s ^ 8 elements (the swizzle
+      // flips whole 16-byte chunks and keeps pairs (2c, 2c+1) together)
+      *reinterpret_cast<u32x4*>(&kt[cv_k[i]]) = u32x4{k0.x, k0.y, k1.x, k1.y};
+      *reinterpret_cast<u32x4*>(&kt[cv_k[i] ^ 8]) = u32x4{k2.x, k2.y, k3.x, k3.y};
+      *reinterpret_cast<u32x4*>(&vt[cv_v[i]]) = u32x4{v0.x, v0.y, v1.x, v1.y};
+      *reinterpret_cast<u32x4*>(&vt[cv_v[i] ^ 8]) = u32x4{v2.x, v2.y, v3.x, v3.y};
     }
-  const int tr_e = n >> 1;
-  const int tr_row = tr_e < 4 ? 4 * g + tr_e : 12 + 4 * g + tr_e;
-  const int tr_sw = piece_swizzle<D>(tr_row);
-  const int tr_off = tr_row * D + 8 * (n & 1);
+  };
+  // bf16 operand offsets, as in the wide bf16 pass
+  int ka_off[KSTEPS], vb_off[NTILES];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) ka_off[s] = n * D + (((4 * s + g) ^ (n & (LPR - 1))) * 8);
+  {
+    const int tr_row = 4 * g + (n >> 2);
+    const int swz = (tr_row & (LPR / 2 - 1)) << 1;
+#pragma unroll
+    for (int t = 0; t < NTILES; ++t)
+      vb_off[t] = tr_row * D + (((2 * t + ((n & 3) >> 1)) ^ swz) * 8) + 4 * (n & 1);
+  }
 
   float m_run = -INFINITY;
   float l_run = 0.f;  // this lane's share of head n's denominator
@@ -236,17 +256,21 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (c0 + kChunk < t1) copy_chunk(c0 + kChunk, buf ^ 1);
+    convert(buf);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's bf16 stores are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();        // the bf16 tiles are complete
+    asm volatile("" ::: "memory");
 
-    // ---- S^T = K . Q^T (codes from LDS) ----
+    // ---- S^T = K . Q^T (bf16 operands from LDS) ----
     f32x4 st[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < KPIECES; ++w) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&kq[buf][ka_off[mt][w]]);
-        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(a[0], a[1]), qf[2 * w], st[mt], 0, 0, 0);
-        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_to_bf16x8(a[2], a[3]), qf[2 * w + 1], st[mt], 0, 0, 0);
+      for (int s = 0; s < KSTEPS; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&kt[16 * mt * D + ka_off[s]]);
+        st[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), qf[s], st[mt], 0, 0, 0);
       }
     }
     // ---- online softmax for head n over positions {16mt + 4g + i} ----
@@ -287,12 +311,14 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
       l_run += e0 + e1;
       pw[j / 2] = pack_bf16x2(e0 * sv[j], e1 * sv[j + 1]);
     }
-    // ---- O += P . V: transposed code reads, converted to bf16 operands ----
+    // ---- O += P . V (bf16 V read transposed from LDS) ----
     const bf16x8 pa = as_bf16x8(u32x4{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
     for (int t = 0; t < NTILES; ++t) {
-      const uint2 wv = lds_read_tr8(&vq[buf][tr_off + 16 * (t ^ tr_sw)]);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, codes_to_bf16x8(wv.x, wv.y), acc[t], 0, 0, 0);
+      const uint2 lo = lds_read_tr16(vt + vb_off[t]);
+      const uint2 hi = lds_read_tr16(vt + vb_off[t] + 16 * D);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y}),
+                                                       acc[t], 0, 0, 0);
     }
   }
 
