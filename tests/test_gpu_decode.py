@@ -54,6 +54,7 @@ CASES = [
     (2, 32, 1, 128, [129, 64], "bf16"),        # K = 1 (MQA), G = 32
     (2, 48, 1, 128, [777, 31], "bf16"),        # G = 48: three head blocks in a four-wave group
     (1, 128, 1, 64, [1500], "bf16"),           # G = 128: eight head blocks
+    (1, 144, 1, 64, [300], "bf16"),            # G = 144: nine head blocks (one wave per block)
     (3, 64, 2, 128, [0, 2049, 64], "bf16"),    # G = 32 on two KV heads, an empty sequence
     (4, 64, 8, 128, [0, 1, 640, 641], "bf16"),  # empty sequence, partition edges
     (2, 12, 4, 128, [70, 3], "f32"),

@@ -95,6 +95,7 @@ CASES = [
     (2, 8, 8, 128, [2, 97]),           # K = H (MHA)
     (2, 32, 1, 128, [129, 4100]),      # K = 1 (MQA), G = 32
     (1, 71, 1, 64, [257]),             # G = 71: five head blocks
+    (1, 144, 1, 64, [300]),            # G = 144: nine head blocks (one wave per block)
     (40, 16, 8, 64, RAGGED_40),        # 320 units: one-dimensional grid, partition slowest
 ]
 
