@@ -12,7 +12,7 @@
 // wave multiplies it with its own heads.  The arithmetic is the int8 pass's:
 //     s_j  = scale * (q . c^K_j) * sk_j,
 //     acc += sum_j 2^(s_j - m) * sv_j * c^V_j,   l += sum_j 2^(s_j - m),
-// with codes converted to bf16 in registers (exact) and the value scale
+// with codes converted to bf16 (exact; see below) and the value scale
 // folded into each position's bf16 weight, and the same quantising append
 // (the new rows go through a workspace slot).
 //
