@@ -222,6 +222,9 @@ FUSED_CASES = [
     (3, 32, 8, 128, [12, 5, 12], 12, 1),          # full caches: no append
     (2, 32, 8, 128, [60, 3], 64, 8),              # eight steps; the first cache fills up
     (40, 16, 8, 64, RAGGED_40, None, 2),          # 320 units: one-dimensional grid
+    (3, 96, 2, 128, [95, 0, 60], 104, 10),        # G = 48 (one workgroup per group): ten steps,
+                                                  # the first cache fills up, new rows at group edges
+    (2, 71, 1, 64, [31, 32], None, 3),            # G = 71, d = 64: chunk edges, three steps
 ]
 
 
