@@ -48,6 +48,12 @@ __device__ __forceinline__ uint2 codes_to_bf16x4(uint32_t w) {
   return uint2{pack_bf16x2(f0, f1), pack_bf16x2(f2, f3)};
 }
 
+// bf16 V chunk swizzle, as in the wide bf16 pass
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return D == 64 ? ((r >> 1) & 3) << 1 : (r & 7) << 1;
+}
+
 // Physical 16-byte piece of logical piece c in a staged int8 row r.
 template <int D>
 __device__ __forceinline__ int piece_swizzle(int r) {
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   __shared__ __attribute__((aligned(16))) int8_t vq[2][TILE];
   __shared__ __attribute__((aligned(16))) float ksc[2][kChunk];
   __shared__ __attribute__((aligned(16))) float vsc[2][kChunk];
-  // the current chunk as bf16: K chunk c ^ (row % (D/8)), V chunk ^ 2 (row % (D/16))
+  // the current chunk as bf16 (the wide bf16 pass's layout)
   __shared__ __attribute__((aligned(16))) uint16_t kt[kChunk * D];
   __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * D];
   // target of the surplus copies (they repeat a real copy; never read)
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     const int r = pc / CPR, lp = pc % CPR;
     cv_src[i] = r * D + 16 * (lp ^ piece_swizzle<D>(r));
     cv_k[i] = r * D + 8 * ((2 * lp) ^ (r & (LPR - 1)));        // chunk 2 lp; 2 lp + 1 is chunk ^ 1
-    cv_v[i] = r * D + 8 * ((2 * lp) ^ ((r & (LPR / 2 - 1)) << 1));
+    cv_v[i] = r * D + 8 * ((2 * lp) ^ v_swizzle<D>(r));
   }
   auto convert = [&](int buf) {
 #pragma unroll
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   for (int s = 0; s < KSTEPS; ++s) ka_off[s] = n * D + (((4 * s + g) ^ (n & (LPR - 1))) * 8);
   {
     const int tr_row = 4 * g + (n >> 2);
-    const int swz = (tr_row & (LPR / 2 - 1)) << 1;
+    const int swz = v_swizzle<D>(tr_row);
 #pragma unroll
     for (int t = 0; t < NTILES; ++t)
       vb_off[t] = tr_row * D + (((2 * t + ((n & 3) >> 1)) ^ swz) * 8) + 4 * (n & 1);

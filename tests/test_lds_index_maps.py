@@ -13,7 +13,7 @@ def _bf16_k_swizzle(D, r):
 
 
 def _bf16_v_swizzle(D, r):
-    return (r & (D // 16 - 1)) << 1
+    return ((r >> 1) & 3) << 1 if D == 64 else (r & 7) << 1
 
 
 def _check_bf16_reads(D, kt, vt):
