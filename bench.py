@@ -70,20 +70,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 def sources_code_sha256(paths) -> str:
     """SHA-256 of the code in the given source files (repository-relative),
-    with C/C++ comments removed and whitespace runs collapsed, so that an
-    edit of comments alone leaves it unchanged."""
-    import hashlib
-    import re
+    with C/C++ comments removed and whitespace runs collapsed (the library's
+    build-id hash), so that an edit of comments alone leaves it unchanged."""
+    from grouped_query_kv_amd.build import code_sha256
 
-    h = hashlib.sha256()
-    for src in paths:
-        with open(os.path.join(ROOT, src), encoding="utf-8") as f:
-            text = f.read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(re.sub(r"\s+", " ", text).strip().encode())
-        h.update(b"\0")
-    return h.hexdigest()
+    return code_sha256(paths)
 
 
 def recorded_traffic(kernel: str, workload: str):

@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     GQAError,
     HipEvent,
     gqa_abi_version,
+    gqa_build_id,
     gqa_cross_attention,
     gqa_decode,
     gqa_decode_append,

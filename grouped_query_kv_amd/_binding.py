@@ -10,7 +10,6 @@ another way.
 from __future__ import annotations
 
 import ctypes
-import math
 import re
 from pathlib import Path
 
@@ -30,6 +29,7 @@ _c_void_p, _c_int, _c_int64, _c_size_t, _c_float = (
 
 _SIGNATURES = {
     "gqa_abi_version": (_c_int, []),
+    "gqa_build_id": (ctypes.c_char_p, []),
     "gqa_last_error": (ctypes.c_char_p, []),
     "gqa_set_timing_events": (_c_int, [_c_void_p, _c_void_p]),
     "gqa_kv_cache_bytes": (ctypes.c_uint64, [_c_int, _c_int, _c_int, _c_int, ctypes.c_uint64]),
@@ -85,6 +85,13 @@ def load_library(path: Path | str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    from .build import build_id
+
+    built, here = lib.gqa_build_id().decode(), build_id()
+    if built != here:
+        raise RuntimeError(
+            f"{path} was built from other sources (code hash {built[:16]}..., the sources here "
+            f"hash to {here[:16]}...): rebuild it (python -m grouped_query_kv_amd.build)")
     _lib = lib
     return lib
 
@@ -118,6 +125,10 @@ def _need(t: torch.Tensor, name: str, ndim: int, dtypes=(torch.float32, torch.bf
 # ---------------------------------------------------------------------------
 def gqa_abi_version() -> int:
     return load_library().gqa_abi_version()
+
+
+def gqa_build_id() -> str:
+    return load_library().gqa_build_id().decode()
 
 
 def gqa_last_error() -> str:
@@ -210,7 +221,7 @@ def gqa_decode_workspace_bytes(B: int, H: int, K: int, max_seq_len: int, d: int)
 
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, out, workspace, max_seq_len: int,
-               scale: float | None = None, stream=None) -> None:
+               scale: float, stream=None) -> None:
     """One decode step: out [B,H,d] = GQA of q [B,H,d] over rows [0, seq_lens[b])
     of the caches [B,K,S_max,d].  workspace: uint8 GPU tensor of at least
     gqa_decode_workspace_bytes(...) bytes."""
@@ -228,8 +239,6 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, out, workspace, max_seq_len: int,
         raise ValueError("q and caches must share a dtype")
     if seq_lens.numel() != B:
         raise ValueError("seq_lens must have B entries")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     lib = load_library()
     _check("gqa_decode", lib.gqa_decode(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
@@ -238,7 +247,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, out, workspace, max_seq_len: int,
 
 
 def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, out, workspace,
-                      max_seq_len: int, scale: float | None = None, stream=None) -> None:
+                      max_seq_len: int, scale: float, stream=None) -> None:
     """gqa_kv_append followed by gqa_decode, fused into two kernel launches.
     max_seq_len bounds the lengths after the append."""
     _need(q, "q", 3)
@@ -259,8 +268,6 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, out, workspac
         raise ValueError("q and caches must share a dtype")
     if seq_lens.numel() != B:
         raise ValueError("seq_lens must have B entries")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     lib = load_library()
     _check("gqa_decode_append", lib.gqa_decode_append(
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
@@ -304,7 +311,7 @@ def gqa_decode_paged_workspace_bytes(B: int, H: int, K: int, max_seq_len: int, d
 
 
 def gqa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, out, workspace, max_seq_len: int,
-                     scale: float | None = None, stream=None) -> None:
+                     scale: float, stream=None) -> None:
     """One decode step over a paged cache: out [B,H,d] = GQA of q [B,H,d]
     over logical rows [0, seq_lens[b]) gathered through block_table."""
     _need(q, "q", 3, (torch.bfloat16,))
@@ -317,8 +324,6 @@ def gqa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, out, workspace, m
         raise ValueError("shape mismatch between q, pools, block_table and out")
     if k_pool.dtype != q.dtype:
         raise ValueError("q and pools must share a dtype")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     lib = load_library()
     _check("gqa_decode_paged", lib.gqa_decode_paged(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
@@ -328,7 +333,7 @@ def gqa_decode_paged(q, k_pool, v_pool, block_table, seq_lens, out, workspace, m
 
 
 def gqa_decode_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_lens, out, workspace,
-                            max_seq_len: int, scale: float | None = None, stream=None) -> None:
+                            max_seq_len: int, scale: float, stream=None) -> None:
     """gqa_kv_append_paged followed by gqa_decode_paged, fused into two kernel
     launches.  max_seq_len bounds the lengths after the append."""
     _need(q, "q", 3, (torch.bfloat16,))
@@ -345,8 +350,6 @@ def gqa_decode_append_paged(q, k_new, v_new, k_pool, v_pool, block_table, seq_le
         _need(t, nm, 3, (torch.bfloat16,))
         if tuple(t.shape) != (B, K, d):
             raise ValueError(f"{nm} must be [B,K,d]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     _check("gqa_decode_append_paged", load_library().gqa_decode_append_paged(
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(),
@@ -401,7 +404,7 @@ def gqa_kv_append_int8(k_new, v_new, k_codes, v_codes, k_scales, v_scales, seq_l
 
 
 def gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, out, workspace,
-                    max_seq_len: int, scale: float | None = None, stream=None) -> None:
+                    max_seq_len: int, scale: float, stream=None) -> None:
     """One decode step over an int8 cache: out [B,H,d] = GQA of the bf16 q
     [B,H,d] over the dequantised rows [0, seq_lens[b])."""
     _need(q, "q", 3, (torch.bfloat16,))
@@ -413,8 +416,6 @@ def gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, out, work
     Bk, K, S_max, dk = k_codes.shape
     if Bk != B or dk != d or tuple(out.shape) != (B, H, d) or seq_lens.numel() != B:
         raise ValueError("shape mismatch between q, cache, seq_lens and out")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     _check("gqa_decode_int8", load_library().gqa_decode_int8(
         q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),
         seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K, S_max,
@@ -422,7 +423,7 @@ def gqa_decode_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, out, work
 
 
 def gqa_decode_append_int8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales, seq_lens, out,
-                           workspace, max_seq_len: int, scale: float | None = None, stream=None) -> None:
+                           workspace, max_seq_len: int, scale: float, stream=None) -> None:
     """gqa_kv_append_int8 followed by gqa_decode_int8, fused into two kernel
     launches (bf16 q, k_new, v_new).  max_seq_len bounds the lengths after
     the append."""
@@ -439,8 +440,6 @@ def gqa_decode_append_int8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales
         _need(t, nm, 3, (torch.bfloat16,))
         if tuple(t.shape) != (B, K, d):
             raise ValueError(f"{nm} must be [B,K,d]")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     _check("gqa_decode_append_int8", load_library().gqa_decode_append_int8(
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
         k_scales.data_ptr(), v_scales.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
@@ -448,7 +447,7 @@ def gqa_decode_append_int8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales
         GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
-def gqa_prefill_causal(q, k, v, out, scale: float | None = None, stream=None) -> None:
+def gqa_prefill_causal(q, k, v, out, scale: float, stream=None) -> None:
     """Causal GQA over a prefix: q/out [B,H,S,d], k/v [B,K,S_max,d] (rows < S used)."""
     _need(q, "q", 4, (torch.bfloat16,))
     _need(k, "k", 4, (torch.bfloat16,))
@@ -458,8 +457,6 @@ def gqa_prefill_causal(q, k, v, out, scale: float | None = None, stream=None) ->
     Bk, K, S_max, dk = k.shape
     if Bk != B or dk != d or v.shape != k.shape or tuple(out.shape) != (B, H, S, d):
         raise ValueError("shape mismatch between q, k, v and out")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     lib = load_library()
     _check("gqa_prefill_causal", lib.gqa_prefill_causal(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, K, S, S_max, d,
@@ -478,29 +475,25 @@ def _prefill_shapes(q, k, v, out):
     return B, H, S, d, K, S_max
 
 
-def gqa_prefill_chunk(q, k_cache, v_cache, seq_lens, out, scale: float | None = None, stream=None) -> None:
+def gqa_prefill_chunk(q, k_cache, v_cache, seq_lens, out, scale: float, stream=None) -> None:
     """Causal attention of the last S positions (q/out [B,H,S,d]) over caches
     [B,K,S_max,d] holding seq_lens[b] rows, the chunk included."""
     B, H, S, d, K, S_max = _prefill_shapes(q, k_cache, v_cache, out)
     _need(seq_lens, "seq_lens", 1, (torch.int32,))
     if seq_lens.numel() != B:
         raise ValueError("seq_lens must have B entries")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     _check("gqa_prefill_chunk", load_library().gqa_prefill_chunk(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
         B, H, K, S, S_max, d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
-def gqa_cross_attention(q, k, v, kv_lens, out, scale: float | None = None, stream=None) -> None:
+def gqa_cross_attention(q, k, v, kv_lens, out, scale: float, stream=None) -> None:
     """Non-causal attention of q/out [B,H,S_q,d] over rows [0, kv_lens[b]) of
     k, v [B,K,S_max,d]."""
     B, H, S, d, K, S_max = _prefill_shapes(q, k, v, out)
     _need(kv_lens, "kv_lens", 1, (torch.int32,))
     if kv_lens.numel() != B:
         raise ValueError("kv_lens must have B entries")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
     _check("gqa_cross_attention", load_library().gqa_cross_attention(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_lens.data_ptr(), out.data_ptr(),
         B, H, K, S, S_max, d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))

@@ -5,10 +5,17 @@
 Every .hip file under csrc/ is compiled with hipcc for gfx950 and the objects
 are linked into grouped_query_kv_amd/libgqa.so.  Packed fp32 instructions are
 disabled for all device code.
+
+The library carries the SHA-256 of the code it was built from (every source
+under csrc/ and include/gqa.h, comments and whitespace removed), returned by
+gqa_build_id(); the binding refuses to load a library whose code hash
+differs from that of the sources next to it.
 """
 from __future__ import annotations
 
+import hashlib
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,9 +41,34 @@ def sources() -> list[Path]:
     return sorted(CSRC.glob("*.hip"))
 
 
-def _compile(src: Path) -> Path:
+def code_sha256(paths) -> str:
+    """SHA-256 of the code in the given files (absolute, or relative to the
+    repository root), C/C++ comments removed and whitespace runs collapsed,
+    so that an edit of comments alone leaves it unchanged."""
+    h = hashlib.sha256()
+    for src in paths:
+        text = (ROOT / src).read_text(encoding="utf-8")
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
+def hashed_sources() -> list[str]:
+    """The files whose code defines the library (repository-relative)."""
+    files = sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.h")) + [ROOT / "include" / "gqa.h"]
+    return [str(f.relative_to(ROOT)) for f in files]
+
+
+def build_id() -> str:
+    """Code hash of the sources in this tree (what gqa_build_id() must return)."""
+    return code_sha256(hashed_sources())
+
+
+def _compile(src: Path, bid: str) -> Path:
     obj = BUILD / (src.stem + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", str(src), "-o", str(obj)]
+    cmd = [HIPCC, *CFLAGS, f'-DGQA_BUILD_ID="{bid}"', "-c", str(src), "-o", str(obj)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src.name}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -64,8 +96,9 @@ def build(verbose: bool = True) -> Path:
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     BUILD.mkdir(exist_ok=True)
     srcs = sources()
+    bid = build_id()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda src: _compile(src, bid), srcs))
     tmp = LIB.with_suffix(".so.tmp")
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -13,8 +13,17 @@
 //     s_j  = scale * (q . c^K_j) * sk_j,
 //     acc += sum_j 2^(s_j - m) * sv_j * c^V_j,   l += sum_j 2^(s_j - m),
 // with codes converted to bf16 (exact; see below) and the value scale
-// folded into each position's bf16 weight, and the same quantising append
-// (the new rows go through a workspace slot).
+// folded into each position's bf16 weight, and the same quantising append.
+//
+// Fused append: the first wave quantises the step's new K and V rows into
+// its registers (the int8 pass's fp32 rule, shared helpers).  The new row is
+// the last position of its sequence, so it lies in the last chunk of the
+// last partition; that chunk's copies fetch the (not yet written) cache row,
+// and once every wave's copies have landed the first wave overwrites the
+// row's staged codes and its two scales in LDS, and a barrier orders that
+// before the conversion.  No other wave reads data another wave wrote to
+// global memory in this launch.  After the loop the first wave writes the
+// codes and scales into the cache.
 //
 // Each chunk's codes are converted to bf16 once, by all threads of the
 // workgroup together (each thread a share of the 16-byte pieces), into bf16
@@ -66,7 +75,7 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     float* __restrict__ ks, float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
     float* __restrict__ part_acc, float* __restrict__ part_ml, int H, int K, int S_max,
     int part_tokens, int parts, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, uint8_t* __restrict__ slots) {
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;
   constexpr int NTILES = D / 16;
@@ -130,40 +139,33 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   float* ksb = ks + head_row0;
   float* vsb = vs + head_row0;
 
-  // The new rows (fused append): quantised by the first wave into this
-  // workgroup's workspace slot = [K codes (D) | V codes (D) | K scales (4) |
-  // V scales (4)], the scale groups being the 4-aligned group around the new
-  // position; the copies take the slot instead of the cache for it.
+  // The new rows (fused append): wave 0 quantises them into registers,
+  // lane l holding the codes of elements E l .. E l + E - 1 of each row.
+  constexpr int E = D / 64;  // elements per lane
   const bool has_new = APPEND && newpos >= t0 && newpos < t1;  // uniform
-  const int s0_new = has_new ? (newpos & ~3) : -4;
-  int8_t* slot = reinterpret_cast<int8_t*>(slots) + (APPEND ? ((size_t)b * K + k) * (2 * D + 32) : 0);
-  float* slot_sc = reinterpret_cast<float*>(slot + 2 * D);
-  if (has_new) {
-    if (wave == 0) {
-      constexpr int E = D / 64;  // elements per lane
+  uint32_t new_codes[2] = {0u, 0u};  // K, V: E code bytes, little-endian
+  float new_scale[2] = {0.f, 0.f};
+  if (has_new && wave == 0) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const __bf16* src = (r == 0 ? k_new : v_new) + ((size_t)b * K + k) * D + E * lane;
-        float x[E];
-        float amax = 0.f;
+    for (int r = 0; r < 2; ++r) {
+      const __bf16* src = (r == 0 ? k_new : v_new) + ((size_t)b * K + k) * D + E * lane;
+      float x[E];
+      float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          x[e] = static_cast<float>(src[e]);
-          amax = fmaxf(amax, fabsf(x[e]));
-        }
-#pragma unroll
-        for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
-        const float inv = amax > 0.f ? int8_inv(amax) : 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) slot[r * D + E * lane + e] = amax > 0.f ? (int8_t)int8_code(x[e], inv) : 0;
-        if (lane < 4) {  // cached scales before the new position, 0 after it
-          const int pos = s0_new + lane;
-          const float* rs = r == 0 ? ksb : vsb;
-          slot_sc[4 * r + lane] = pos < newpos ? rs[pos] : pos == newpos ? (amax > 0.f ? int8_scale(amax) : 0.f) : 0.f;
-        }
+      for (int e = 0; e < E; ++e) {
+        x[e] = static_cast<float>(src[e]);
+        amax = fmaxf(amax, fabsf(x[e]));
       }
+#pragma unroll
+      for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const float inv = amax > 0.f ? int8_inv(amax) : 0.f;
+      uint32_t w = 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        w |= (uint32_t)(uint8_t)(amax > 0.f ? (int8_t)int8_code(x[e], inv) : (int8_t)0) << (8 * e);
+      new_codes[r] = w;
+      new_scale[r] = amax > 0.f ? int8_scale(amax) : 0.f;
     }
-    __syncthreads();  // the slot is written before any wave copies from it
   }
 
   // Copy slot c of this wave: instruction i = wave + c W of a chunk (surplus
@@ -184,9 +186,8 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     for (int c = 0; c < NI; ++c) {
       const int i = wave + c * W;  // uniform
       const int tok = min(c0 + crow[c], last);
-      const bool nw = APPEND && tok == newpos;
-      const int8_t* ksrc = (nw ? slot : kbase + (size_t)tok * D) + ckoff[c];
-      const int8_t* vsrc = (nw ? slot + D : vbase + (size_t)tok * D) + cvoff[c];
+      const int8_t* ksrc = kbase + (size_t)tok * D + ckoff[c];
+      const int8_t* vsrc = vbase + (size_t)tok * D + cvoff[c];
       int8_t* kd = i < NINST ? &kq[buf][1024 * i] : sink;
       int8_t* vd = i < NINST ? &vq[buf][1024 * i] : sink;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(ksrc),
@@ -195,10 +196,11 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
                                        (__attribute__((address_space(3))) void*)vd, 16, 0, 0);
     }
     // scales: lanes 0..7 of waves 0 (K) and 1 (V) copy the chunk's 32 scales,
-    // 4 per lane (groups past the partition end repeat its last group)
+    // 4 per lane (groups past the partition end repeat its last group; S_max
+    // is a multiple of 4, so a group never leaves the cache)
     if (wave < 2 && lane < kChunk / 4) {
       const int s0 = min(c0 + 4 * lane, last & ~3);
-      const float* src = APPEND && s0 == s0_new ? slot_sc + 4 * wave : (wave == 0 ? ksb : vsb) + s0;
+      const float* src = (wave == 0 ? ksb : vsb) + s0;
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src),
                                        (__attribute__((address_space(3))) void*)(wave == 0 ? ksc[buf] : vsc[buf]),
                                        16, 0, 0);
@@ -262,6 +264,30 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (c0 + kChunk < t1) copy_chunk(c0 + kChunk, buf ^ 1);
+    if (has_new && c0 + kChunk >= t1) {  // uniform: the chunk holding the new row
+      // every copy of this chunk has landed (the barrier above); replace the
+      // new row's staged codes and scales, then order that before convert
+      if (wave == 0) {
+        const int rn = newpos - c0;
+        const int x = E * lane;  // first element of this lane (E <= 2: one piece)
+        const int off = rn * D + 16 * ((x >> 4) ^ piece_swizzle<D>(rn)) + (x & 15);
+        if (E == 2) {
+          *reinterpret_cast<uint16_t*>(&kq[buf][off]) = (uint16_t)new_codes[0];
+          *reinterpret_cast<uint16_t*>(&vq[buf][off]) = (uint16_t)new_codes[1];
+        } else {
+          kq[buf][off] = (int8_t)new_codes[0];
+          vq[buf][off] = (int8_t)new_codes[1];
+        }
+        if (lane == 0) {
+          ksc[buf][rn] = new_scale[0];
+          vsc[buf][rn] = new_scale[1];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
     convert(buf);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's bf16 stores are done
     asm volatile("" ::: "memory");
@@ -332,12 +358,19 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   l_run += __shfl_xor(l_run, 32);
 
   if (APPEND && has_new && wave == 0) {  // the appended rows join the cache
-    if (lane < 2 * (D / 16)) {
-      const int r = lane / (D / 16), w = lane % (D / 16);
-      *reinterpret_cast<u32x4*>((r == 0 ? kbase : vbase) + (size_t)newpos * D + 16 * w) =
-          ld16(slot + r * D + 16 * w);
+    int8_t* kd = kbase + (size_t)newpos * D + E * lane;
+    int8_t* vd = vbase + (size_t)newpos * D + E * lane;
+    if (E == 2) {
+      *reinterpret_cast<uint16_t*>(kd) = (uint16_t)new_codes[0];
+      *reinterpret_cast<uint16_t*>(vd) = (uint16_t)new_codes[1];
+    } else {
+      *kd = (int8_t)new_codes[0];
+      *vd = (int8_t)new_codes[1];
     }
-    if (lane < 2) (lane == 0 ? ksb : vsb)[newpos] = slot_sc[4 * lane + (newpos - s0_new)];
+    if (lane == 0) {
+      ksb[newpos] = new_scale[0];
+      vsb[newpos] = new_scale[1];
+    }
   }
 
   const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
@@ -373,7 +406,7 @@ hipError_t launch_decode_wide_int8(const void* q, void* k_codes, void* v_codes, 
 #define GQA_WI8(DD, AP, WW)                                                                      \
   hipLaunchKernelGGL((decode_wide_int8_kernel<DD, AP, WW>), grid, dim3(64 * WW), 0, stream, qp,  \
                      kp, vp, k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, \
-                     plan.part_tokens, plan.parts, scale_log2, kn, vn, ws.lens, ws.new_rows)
+                     plan.part_tokens, plan.parts, scale_log2, kn, vn, ws.lens)
 #define GQA_WI8_W(DD, AP)                                                                        \
   switch (plan.head_blocks) {                                                                     \
     case 2: GQA_WI8(DD, AP, 2); break;                                                            \

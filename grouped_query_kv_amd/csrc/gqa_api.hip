@@ -3,7 +3,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <cstdlib>
 #include <string>
 
 #include "gqa.h"
@@ -39,18 +38,6 @@ int check_hip(hipError_t e, const char* what) {
   return GQA_OK;
 }
 
-// Partition length override for tuning (rounded up to a multiple of 32
-// positions, at least 64); 0 = automatic.
-int part_tokens_override() {
-  static const int v = [] {
-    const char* s = std::getenv("GQA_DECODE_PART_TOKENS");
-    if (!s) return 0;
-    const long x = std::strtol(s, nullptr, 10);
-    return x >= 64 && x <= (1L << 24) ? (int)((x + 31) / 32 * 32) : 0;  // else ignored
-  }();
-  return v;
-}
-
 // Launch with optional timing events around the main kernel.
 struct TimedRegion {
   hipStream_t s;
@@ -72,20 +59,17 @@ DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, int max_part
   p.head_blocks = (G + 15) / 16;
   const long long units = (long long)B * K * p.head_blocks;
   const int L = max_seq_len > 0 ? max_seq_len : 1;
-  int pt = part_tokens_override();
-  if (pt == 0) {
-    // One single-wave workgroup per partition.  Aim at 3072 workgroups over
-    // the 256 CUs -- one round of the int8 pass's three resident waves per
-    // SIMD, one and a half of the bf16 pass's two (sweeps of the partition
-    // length put this within a few percent of the best fixed length on every
-    // decode workload) -- with equal partitions of a multiple of 32 positions.
-    const long long target = 256LL * 4 * 3;
-    long long parts = target / (units > 0 ? units : 1);
-    if (parts < 1) parts = 1;
-    long long t = (L + parts - 1) / parts;
-    t = (t + 31) / 32 * 32;
-    pt = (int)(t < 64 ? 64 : t);
-  }
+  // One single-wave workgroup per partition.  Aim at 3072 workgroups over
+  // the 256 CUs -- one round of the int8 pass's three resident waves per
+  // SIMD, one and a half of the bf16 pass's two (sweeps of the partition
+  // length put this within a few percent of the best fixed length on every
+  // decode workload) -- with equal partitions of a multiple of 32 positions.
+  const long long target = 256LL * 4 * 3;
+  long long parts = target / (units > 0 ? units : 1);
+  if (parts < 1) parts = 1;
+  long long t = (L + parts - 1) / parts;
+  t = (t + 31) / 32 * 32;
+  int pt = (int)(t < 64 ? 64 : t);
   // Partition starts that are multiples of 64 KiB of cache rows make every
   // partition of a head begin on the same HBM channel; measured on the ragged
   // 70B layer: 512- and 768-position partitions (bf16, d = 128) are 8-15%
@@ -124,6 +108,11 @@ DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, i
 extern "C" {
 
 int gqa_abi_version(void) { return 1; }
+
+#ifndef GQA_BUILD_ID
+#error "GQA_BUILD_ID (the code hash of the sources) must be defined by the build"
+#endif
+const char* gqa_build_id(void) { return GQA_BUILD_ID; }
 
 const char* gqa_last_error(void) { return g_last_error.c_str(); }
 

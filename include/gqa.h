@@ -63,6 +63,15 @@ enum {
 int gqa_abi_version(void);
 
 /*
+ * Identity of the code this library was built from: the lowercase hex
+ * SHA-256 of its sources (every kernel and header source and this header,
+ * with comments removed and whitespace runs collapsed), fixed at build time.
+ * A caller compares it with the hash of the sources it expects, so that a
+ * library built from other sources is never used.  The string is static.
+ */
+const char* gqa_build_id(void);
+
+/*
  * Append one token per sequence: for every b with L = seq_lens[b] < S_max
  *   k_cache[b, k, L, :] = k_new[b, k, :],  v_cache[b, k, L, :] = v_new[b, k, :]
  * for all k, then seq_lens[b] = L + 1.  A sequence whose cache is full

@@ -382,7 +382,47 @@ def test_binding_refuses_cpu_tensors():
         gqa.gqa_meanpool_convert(torch.zeros(2, 8, 4), torch.zeros(2, 2, 4))
     with pytest.raises(ValueError):
         gqa.gqa_decode(x, x[:, None], x[:, None], torch.zeros(2, dtype=torch.int32), x,
-                       torch.zeros(16, dtype=torch.uint8), 8)
+                       torch.zeros(16, dtype=torch.uint8), 8, scale=0.1)
+
+
+def test_binding_needs_an_explicit_scale():
+    """The binding passes the caller's scale through; it never derives one."""
+    import inspect
+    for fn in (gqa.gqa_decode, gqa.gqa_decode_append, gqa.gqa_decode_paged, gqa.gqa_decode_append_paged,
+               gqa.gqa_decode_int8, gqa.gqa_decode_append_int8, gqa.gqa_prefill_causal,
+               gqa.gqa_prefill_chunk, gqa.gqa_cross_attention):
+        p = inspect.signature(fn).parameters["scale"]
+        assert p.default is inspect.Parameter.empty, fn.__name__
+
+
+def test_build_id_matches_the_sources(lib):
+    """The loaded library was built from the sources in this tree."""
+    from grouped_query_kv_amd.build import build_id
+    assert lib.gqa_build_id().decode() == build_id()
+    assert len(build_id()) == 64
+
+
+def test_stale_library_is_refused(monkeypatch):
+    """A library whose code hash differs from the tree's sources is not used."""
+    import grouped_query_kv_amd.build as bld
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(bld, "build_id", lambda: "0" * 64)
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        B.load_library()
+    monkeypatch.undo()
+    B._lib = None
+    B.load_library()
+
+
+def test_build_id_ignores_comments_only(tmp_path):
+    from grouped_query_kv_amd.build import code_sha256
+    a = tmp_path / "a.hip"
+    a.write_text("int f() { return 1; }  // one\n")
+    h0 = code_sha256([a])
+    a.write_text("/* note */ int f() {\n  return 1;\n}\n")
+    assert code_sha256([a]) == h0
+    a.write_text("int f() { return 2; }\n")
+    assert code_sha256([a]) != h0
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
