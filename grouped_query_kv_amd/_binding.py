@@ -37,6 +37,7 @@ _SIGNATURES = {
     "gqa_decode_workspace_bytes": (_c_size_t, [_c_int] * 5),
     "gqa_decode": (_c_int, [_c_void_p] * 6 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_decode_append": (_c_int, [_c_void_p] * 8 + [_c_size_t] + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
+    "gqa_decode_append_noalloc": (_c_int, [_c_void_p] * 7 + [_c_int] * 6 + [_c_float, _c_int, _c_int, _c_void_p]),
     "gqa_kv_append_paged": (_c_int, [_c_void_p] * 6 + [_c_int] * 7 + [_c_void_p]),
     "gqa_decode_paged_workspace_bytes": (_c_size_t, [_c_int] * 6),
     "gqa_decode_paged": (_c_int, [_c_void_p] * 7 + [_c_size_t] + [_c_int] * 8 + [_c_float, _c_int, _c_int, _c_void_p]),
@@ -274,6 +275,34 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, out, workspac
         seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, K,
         S_max, int(max_seq_len), d, float(scale), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype],
         _stream(stream)))
+
+
+def gqa_decode_append_noalloc(q, k_new, v_new, k_cache, v_cache, seq_lens, out, max_seq_len: int,
+                              scale: float, stream=None) -> None:
+    """gqa_decode_append without a workspace: the library's static device
+    scratch holds the partials (for callers that cannot allocate; calls that
+    overlap on one GPU race)."""
+    _need(q, "q", 3)
+    _need(k_cache, "k_cache", 4)
+    _need(v_cache, "v_cache", 4)
+    _need(out, "out", 3)
+    _need(seq_lens, "seq_lens", 1, (torch.int32,))
+    B, H, d = q.shape
+    Bk, K, S_max, dk = k_cache.shape
+    if Bk != B or dk != d or v_cache.shape != k_cache.shape or tuple(out.shape) != (B, H, d):
+        raise ValueError("shape mismatch between q, caches and out")
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, 3)
+        if tuple(t.shape) != (B, K, d) or t.dtype != k_cache.dtype:
+            raise ValueError(f"{nm} must be [B,K,d] of the cache dtype")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and caches must share a dtype")
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    _check("gqa_decode_append_noalloc", load_library().gqa_decode_append_noalloc(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), B, H, K, S_max, int(max_seq_len), d, float(scale),
+        _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def _need_paged(k_pool, v_pool, block_table, seq_lens):

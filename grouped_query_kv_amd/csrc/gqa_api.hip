@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "gqa.h"
@@ -160,10 +161,16 @@ size_t gqa_decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d) {
 }
 
 // Shared body of gqa_decode and gqa_decode_append (k_new == nullptr: no append).
+static int static_scratch(void** ptr);
+static constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+
+// workspace == nullptr with use_static: the partials go to the library's
+// static scratch array of the current device (no allocation).
 static int decode_impl(const char* fn, const void* q, const void* k_new, const void* v_new,
                        void* k_cache, void* v_cache, int32_t* seq_lens, void* out, void* workspace,
                        size_t workspace_bytes, int B, int H, int K, int S_max, int max_seq_len,
-                       int d, float scale, int dtype, int out_dtype, void* stream) {
+                       int d, float scale, int dtype, int out_dtype, void* stream,
+                       bool use_static = false) {
   if (!q || !k_cache || !v_cache || !seq_lens || !out) return fail(GQA_ERR_INVALID, "%s: null pointer", fn);
   if (int r = validate_heads(fn, B, H, K, d)) return r;
   if (S_max < 1 || max_seq_len < 0 || max_seq_len > S_max)
@@ -184,6 +191,14 @@ static int decode_impl(const char* fn, const void* q, const void* k_new, const v
     return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
   const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d);
   const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
+  if (use_static) {
+    if (need > kStaticScratchBytes)
+      return fail(GQA_ERR_WORKSPACE,
+                  "%s: these sizes need %zu bytes of scratch; the static scratch holds %zu "
+                  "(use gqa_decode_append with a caller workspace)", fn, need, kStaticScratchBytes);
+    if (int r = static_scratch(&workspace)) return r;
+    workspace_bytes = kStaticScratchBytes;
+  }
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
                 need, workspace ? workspace_bytes : (size_t)0);
@@ -225,6 +240,48 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   return decode_impl("gqa_decode_append", q, k_new, v_new, k_cache, v_cache, seq_lens, out,
                      workspace, workspace_bytes, B, H, K, S_max, max_seq_len, d, scale, dtype,
                      out_dtype, stream);
+}
+
+// ---- the allocation-free decode step ----
+// The partials of gqa_decode_append_noalloc live in this file-scope device
+// array (one copy per GPU, held until the process ends).  Its name is a
+// host-side stand-in in host code: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device and kept.  Nothing in it must start at zero: every partition that
+// the combine pass reads is written by the partition pass of the same call.
+// Calls that overlap on one GPU share the array and race.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int static_scratch(void** ptr) {
+  int dev = -1;
+  if (int r = check_hip(hipGetDevice(&dev), "hipGetDevice")) return r;
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GQA_ERR_UNSUPPORTED, "static scratch: device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (int r = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+      return r;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return fail(GQA_ERR_HIP, "static scratch: bad device address %p", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return GQA_OK;
+}
+
+int gqa_decode_append_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, int32_t* seq_lens, void* out, int B, int H, int K,
+                              int S_max, int max_seq_len, int d, float scale, int dtype,
+                              int out_dtype, void* stream) {
+  if (!k_new || !v_new) return fail(GQA_ERR_INVALID, "gqa_decode_append_noalloc: null pointer");
+  return decode_impl("gqa_decode_append_noalloc", q, k_new, v_new, k_cache, v_cache, seq_lens, out,
+                     nullptr, 0, B, H, K, S_max, max_seq_len, d, scale, dtype, out_dtype, stream,
+                     /*use_static=*/true);
 }
 
 // Paged KV cache: the largest partition whose block ids fit one per lane.

@@ -133,6 +133,26 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
                       int d, float scale, int dtype, int out_dtype, void* stream);
 
 /*
+ * gqa_decode_append without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and
+ * kernels as gqa_decode_append; the partial results go to a static device
+ * array inside the library of 64 MiB (67,108,864 bytes) per GPU, held from
+ * the first call on that GPU until the process ends.  Sizes whose
+ * gqa_decode_workspace_bytes(B, H, K, max_seq_len, d) exceeds that return
+ * GQA_ERR_WORKSPACE before anything is enqueued.  The call allocates and
+ * frees nothing.  Every call on one GPU uses the same array: calls that
+ * overlap in time on one GPU (different streams, or different host threads)
+ * race and must be serialised by the caller.  The first call on a device
+ * looks up the array's address on the current device (hipGetDevice), so the
+ * stream must belong to the current device.
+ */
+int gqa_decode_append_noalloc(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, int32_t* seq_lens, void* out, int B, int H, int K,
+                              int S_max, int max_seq_len, int d, float scale, int dtype,
+                              int out_dtype, void* stream);
+
+/*
  * Paged KV cache.  The K and V pools are [num_blocks, K, block_size, d]:
  * physical block n holds block_size consecutive positions of every KV head,
  * one row of d elements per (head, position).  block_table is [B, max_blocks]

@@ -11,6 +11,7 @@ import pytest
 
 import grouped_query_kv_amd as gqa
 from grouped_query_kv_amd import _binding as B
+from grouped_query_kv_amd import _binding as B_
 
 GOLDEN = Path(__file__).resolve().parent / "golden" / "kv_cache_bytes.json"
 FAKE = 0x10000  # 16-byte aligned, never dereferenced (validation fails first)
@@ -454,3 +455,19 @@ def test_build_rejects_undefined_launch_stub(tmp_path):
     subprocess.run(["gcc", "-shared", "-fPIC", "-o", str(so), str(src)], check=True)
     with pytest.raises(RuntimeError, match="launch stubs are undefined"):
         _check_launch_stubs(so)
+
+
+def test_noalloc_rejects_sizes_beyond_the_static_scratch(lib):
+    """gqa_decode_append_noalloc refuses sizes whose partials exceed its
+    64 MiB static scratch, on the host, before any HIP call."""
+    B, H, K, d = 4096, 128, 8, 128
+    assert lib.gqa_decode_workspace_bytes(B, H, K, 4096, d) > 64 << 20
+    code = lib.gqa_decode_append_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, B, H, K, 4096, 4096, d,
+                                         0.1, B_.GQA_BF16, B_.GQA_BF16, None)
+    assert code == B_.GQA_ERR_WORKSPACE
+    assert "static scratch holds" in lib.gqa_last_error().decode()
+    # invalid arguments are still reported as such (validation comes first)
+    assert lib.gqa_decode_append_noalloc(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64, 64, 128,
+                                         0.1, B_.GQA_BF16, B_.GQA_BF16, None) == B_.GQA_ERR_INVALID
+    assert lib.gqa_decode_append_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 3, 64, 64, 128,
+                                         0.1, B_.GQA_BF16, B_.GQA_BF16, None) == B_.GQA_ERR_INVALID
