@@ -62,6 +62,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-baseline time budget")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations timed beside the headline decode workload")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed steps per additional configuration (warm-up: min(--warmup, 5))")
     return ap.parse_args()
 
 
@@ -171,7 +175,7 @@ def cpu_baseline_decode(inp, w, budget_s):
                       f"{t_used:.1f} s of fp64 NumPy on {cores} BLAS threads"}
 
 
-def bench_decode(args, w):
+def bench_decode(args, w, sub=False):
     import grouped_query_kv_amd as gqa
     from grouped_query_kv_amd.inputs import paged_layout, workload_inputs
 
@@ -287,7 +291,7 @@ def bench_decode(args, w):
     # warm figure: the same cache copy every step (it partly stays in the
     # 256 MB Infinity Cache); never the headline
     warm_ms = None
-    if not (paged or int8):
+    if not (paged or int8 or sub):
         wev = (gqa.HipEvent(), gqa.HipEvent())
         c0 = copies[0]
         for _ in range(6):
@@ -299,7 +303,7 @@ def bench_decode(args, w):
             gqa.gqa_set_timing_events(None, None)
             wts.append(wev[0].elapsed_ms(wev[1]))
         warm_ms = float(np.median(wts))
-    copy_gbs = copy_ceiling(dev)
+    copy_gbs = None if sub else copy_ceiling(dev)
     res = {
         "metric": "GQA decode KV-read GB/s (% of HBM peak) + attention tokens/s, 1\u00d7MI355X",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -329,7 +333,7 @@ def bench_decode(args, w):
                                                  "decode_split_bf16_kernel" + ("_paged" if paged else ""), w.name),
                      "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled),
                      "kernel_us_p10_p50_p90": [round(p10 * 1e3, 2), round(p50 * 1e3, 2), round(p90 * 1e3, 2)],
-                     "copy_ceiling_GBps": round(copy_gbs, 1),
+                     **({"copy_ceiling_GBps": round(copy_gbs, 1)} if copy_gbs is not None else {}),
                      **({"warm_kernel_us": round(warm_ms * 1e3, 2)} if warm_ms is not None else {})},
         "input_gen_s": round(t_gen, 1),
     }
@@ -637,6 +641,58 @@ def cpu_baseline_meanpool(src, w, budget_s):
             "sample": f"{mats} whole matrices, {t_used:.1f} s of fp64 NumPy (element-wise: one thread)"}
 
 
+HEADLINE = "decode_llama3_8b"
+# The five configurations of the decode/prefill problem statement, by number;
+# the headline line is configuration 2, the others are timed beside it.
+CONFIGS = {1: "decode_tiny_f32", 2: "decode_llama3_8b", 3: "decode_70b_ragged", 4: "decode_long_131k",
+           5: "prefill_causal_4k"}
+
+
+def _compact(n, r):
+    """The fields of one configuration's result kept in the sub-key."""
+    rf = r["roofline"]
+    c = {"config": n, "workload": r["config"]["workload"], "value": r["value"], "unit": r["unit"],
+         "ms_per_step": r["ms_per_step"], "steps": r["steps"], "warmup": r["warmup"], "dtype": r["dtype"],
+         "tokens_per_s": r.get("tokens_per_s"),
+         "roofline": {k: rf[k] for k in ("kernel", "bound", "achieved", "peak", "unit", "frac", "traffic",
+                                         "avg_kernel_us") if k in rf}}
+    if "hbm_frac" in r:
+        c["hbm_frac"] = r["hbm_frac"]
+    if n == 1:
+        c["note"] = ("0.5 MB of KV: held in the caches, latency-bound; the GB/s figures are no HBM claim "
+                     "(the time per step is the result)")
+    return c
+
+
+def bench_other_configs(args):
+    """Configurations 1, 3, 4 and 5, each timed on its own inputs (no CPU
+    baseline), in the same run as the headline."""
+    import copy
+
+    from grouped_query_kv_amd.inputs import WORKLOADS
+
+    out = {}
+    for n, name in CONFIGS.items():
+        if name == HEADLINE:
+            continue
+        w = WORKLOADS[name]
+        sub = copy.copy(args)
+        sub.steps, sub.warmup = max(1, args.config_steps), min(args.warmup, 5)
+        if w.kind == "prefill":
+            # the matrix-core clock ramps over the first few hundred
+            # microseconds of sustained work: warm it like the headline run
+            sub.steps, sub.warmup = max(sub.steps, 50), max(sub.warmup, 20)
+        print(f"bench: config {n} ({name}), {sub.steps} steps", file=sys.stderr, flush=True)
+        if w.kind == "prefill":
+            r, inp = bench_prefill(sub, w)
+        else:
+            r, inp = bench_decode(sub, w, sub=True)
+        out[str(n)] = _compact(n, r)
+        del inp, r
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -662,6 +718,9 @@ def main():
         res, inp = bench_decode(args, w)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = cpu_baseline_decode(inp, w, args.cpu_seconds)
+    if args.workload == HEADLINE and not args.no_configs:
+        del inp
+        res["configs"] = bench_other_configs(args)
     print(json.dumps(res), flush=True)
 
 

@@ -98,3 +98,37 @@ def run_decode(inp: dict, out_dtype=None, max_seq_len=None, append=False):
 def scale_of(d: int) -> float:
     """fp32 value of 1/sqrt(d), passed identically to the GPU and the oracle."""
     return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def oracle_by_kv_head(fn, q, k, v, *args, workers: int | None = None) -> np.ndarray:
+    """Evaluate an oracle attention function ``fn(q, k, v, *args)`` (q [B, H,
+    S_q, d], k/v [B, K, S_kv, d], any extra per-sequence arrays in ``args``
+    indexed by b) one (sequence, KV head) slice at a time, the slices spread
+    over host threads (NumPy releases the GIL inside its kernels; BLAS runs
+    single-threaded per slice).  The slices are independent, so the result
+    is exactly what one call over the whole batch returns."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    B, H, Sq, d = q.shape
+    K = k.shape[1]
+    G = H // K
+    out = np.zeros((B, H, Sq, d))
+    if workers is None:
+        try:
+            workers = len(os.sched_getaffinity(0))
+        except AttributeError:
+            workers = os.cpu_count() or 1
+        workers = max(1, min(16, workers))
+
+    def one(bk):
+        b, kh = bk
+        sl = [a[b:b + 1] for a in args]
+        out[b:b + 1, kh * G:(kh + 1) * G] = fn(q[b:b + 1, kh * G:(kh + 1) * G], k[b:b + 1, kh:kh + 1],
+                                              v[b:b + 1, kh:kh + 1], *sl)
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, [(b, kh) for b in range(B) for kh in range(K)]))
+    return out

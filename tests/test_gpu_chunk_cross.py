@@ -7,7 +7,7 @@ import torch
 
 import grouped_query_kv_amd as gqa
 from grouped_query_kv_amd.inputs import WORKLOADS, attention_inputs, prefill_inputs, workload_inputs
-from gpu_util import DEV, TOL, bf16_bound, f64, guarded, guards_intact, note, report, scale_of
+from gpu_util import oracle_by_kv_head, DEV, TOL, bf16_bound, f64, guarded, guards_intact, note, report, scale_of
 from oracle import cross_attention_ref, kv_append_rows_ref, prefill_causal_ref, prefill_chunk_ref
 
 pytestmark = pytest.mark.gpu
@@ -146,16 +146,11 @@ def test_append_rows_bit_exact(dtype):
     assert np.array_equal(dk.cpu().view(it).numpy(), k2) and np.array_equal(dv.cpu().view(it).numpy(), v2)
 
 
-def _sampled_rows(S_q):
-    return sorted({0, 1, 15, 16, 63, 64, S_q // 2, S_q - 17, S_q - 2, S_q - 1})
-
-
 def test_chunk_full_workload():
     """2048-token chunk over a 6144-row cache (B=2, H=64, K=8): append the
-    chunk, attend; sampled rows (all heads) against the oracle."""
+    chunk, attend; every row of every head against the oracle."""
     w = WORKLOADS["prefill_chunk_8k"]
     inp = workload_inputs(w, seed=0)
-    T = w.extra["chunk"]
     kc, vc, sl = inp["k"].to(DEV), inp["v"].to(DEV), inp["kv_lens"].to(DEV)
     note("chunk workload: GPU")
     gqa.gqa_kv_append_rows(inp["k_new"].to(DEV), inp["v_new"].to(DEV), kc, vc, sl)
@@ -164,23 +159,18 @@ def test_chunk_full_workload():
     gqa.gqa_prefill_chunk(q, kc, vc, sl, out, scale=scale_of(w.d))
     torch.cuda.synchronize()
     assert sl.cpu().tolist() == [w.L] * w.B
-    assert bool(torch.isfinite(out).all())
-    note("chunk workload: oracle")
-    rows = _sampled_rows(T)
+    note("chunk workload: oracle, every row (per sequence and KV head, threaded)")
     k_all, v_all = kc.cpu(), vc.cpu()
-    # sampled rows: row i of the chunk is a chunk of one query over L - T + i + 1 rows
-    got = f64(out[:, :, rows])
-    want = np.zeros_like(got)
-    for ri, i in enumerate(rows):
-        Li = w.L - T + i + 1
-        want[:, :, ri] = prefill_chunk_ref(f64(inp["q"][:, :, i:i + 1]), k_all.float().numpy(),
-                                           v_all.float().numpy(), np.array([Li] * w.B), scale_of(w.d))[:, :, 0]
-    r = report("chunk 8k sampled", got, want)
+    scale = scale_of(w.d)
+    want = oracle_by_kv_head(lambda q_, k_, v_, l_: prefill_chunk_ref(q_, k_, v_, l_, scale), f64(inp["q"]),
+                             k_all.float().numpy(), v_all.float().numpy(), np.array([w.L] * w.B))
+    r = report("chunk 8k every row", f64(out), want)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
     assert r["max_abs"] <= bf16_bound(want, _vmax(v_all, [w.L] * w.B), weights_in_denominator=True)
 
 
 def test_cross_full_workload():
+    """1024 queries over 4096 encoder rows (B=4, H=32, K=8), every row."""
     w = WORKLOADS["cross_attention_4k"]
     inp = workload_inputs(w, seed=0)
     q, k, v = inp["q"].to(DEV), inp["k"].to(DEV), inp["v"].to(DEV)
@@ -188,10 +178,10 @@ def test_cross_full_workload():
     note("cross workload: GPU")
     gqa.gqa_cross_attention(q, k, v, inp["kv_lens"].to(DEV), out, scale=scale_of(w.d))
     torch.cuda.synchronize()
-    assert bool(torch.isfinite(out).all())
-    rows = _sampled_rows(w.extra["S_q"])
-    ref = cross_attention_ref(f64(inp["q"][:, :, rows]), inp["k"].float().numpy(), inp["v"].float().numpy(),
-                              inp["kv_lens"].numpy(), scale_of(w.d))
-    r = report("cross 4k sampled", f64(out[:, :, rows]), ref)
+    note("cross workload: oracle, every row (per sequence and KV head, threaded)")
+    scale = scale_of(w.d)
+    ref = oracle_by_kv_head(lambda q_, k_, v_, l_: cross_attention_ref(q_, k_, v_, l_, scale), f64(inp["q"]),
+                            inp["k"].float().numpy(), inp["v"].float().numpy(), inp["kv_lens"].numpy())
+    r = report("cross 4k every row", f64(out), ref)
     assert r["finite"] and r["max_abs"] <= TOL["bf16"]
     assert r["max_abs"] <= bf16_bound(ref, _vmax(inp["v"], [w.L] * w.B), weights_in_denominator=True)
