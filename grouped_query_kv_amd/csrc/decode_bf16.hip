@@ -13,7 +13,9 @@
 //
 // How (pinghaoyang.com.cn "GQA 完全拆解", section 工程实现 (engineering): the
 // group's shared KV block is loaded once and reused by all its query heads):
-// one wavefront owns one partition and streams it in chunks of 32 positions.
+// one wavefront owns one flat range of (sequence, KV head, position) -- the
+// split of decode_flat.h, equal ranges for every workgroup however ragged
+// the batch -- and streams each of its segments in chunks of 32 positions.
 // Each K row is read from HBM once, straight into matrix-core operand
 // registers, and multiplies all (up to 16) query heads of the group in one
 // v_mfma_f32_16x16x32_bf16:  S^T[32 x 16] = K_chunk[32 x d] . Q_g^T[d x 16].
@@ -66,11 +68,11 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 // APPEND: fused cache append.  The step's new K/V rows (k_new, v_new) sit at
 // position L_in = seq_lens[b] (when the cache has room -- paged: when L_in is
 // below the table's capacity and the block id at L_in is a valid one, the
-// standalone paged append's rule): the partition that covers it reads that
-// row from k_new/v_new and writes it into the cache (head block 0 only;
-// nothing else reads that row in this launch), and the lengths after the
-// append go to `lens_out` for the combine pass, which publishes them to
-// seq_lens.
+// standalone paged append's rule): the segment that covers it reads that row
+// from k_new/v_new and writes it into the cache (head block 0 only; nothing
+// else reads that row in this launch).  Workgroup 0 records the lengths
+// attended over (after the append) with the split for the combine pass,
+// which publishes them to seq_lens.
 //
 // PAGED: kc/vc are block pools [num_blocks, K, block_size, D] and position j
 // of sequence b lives in physical block block_table[b][j / block_size], row
@@ -80,12 +82,12 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 // readlane.  Ids are clamped into [0, num_blocks) and lengths to the table's
 // capacity, so a malformed table cannot make a load leave the pool.
 template <int D, bool APPEND, bool PAGED>
-__global__ __launch_bounds__(64) void decode_split_bf16_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_bf16_kernel(
     const __bf16* __restrict__ q, __bf16* __restrict__ kc, __bf16* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
-    int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, PagedArgs pg, int p_slowest) {
+    float* __restrict__ part_ml, int B, int H, int K, int S_max, FlatArgs fa, int head_blocks,
+    float scale_log2, const __bf16* __restrict__ k_new, const __bf16* __restrict__ v_new,
+    int32_t* __restrict__ meta, PagedArgs pg) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;        // contraction steps of Q.K
   constexpr int NTILES = D / 16;        // 16-wide output tiles of P.V
@@ -96,48 +98,34 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
 
   __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * LDS_ROW];
 
-  // Work item of this workgroup.  With many partitions per sequence the
-  // grid is (partition, unit, b): consecutive workgroups stream adjacent
-  // parts of one head.  With few (large batches) it is one-dimensional with
-  // the partition index slowest, so every sequence's first partitions are
-  // dispatched before anyone's last and the short sequences of a ragged
-  // batch do not leave the end of the launch to a few long ones.
-  int p, y, b;
-  if (p_slowest) {
-    const int nub = gridDim.x / parts;  // units * B
-    p = blockIdx.x / nub;
-    const int rem = blockIdx.x - p * nub;
-    const int units = K * head_blocks;
-    b = rem / units;
-    y = rem - b * units;
-  } else {
-    p = blockIdx.x;
-    y = blockIdx.y;
-    b = blockIdx.z;
-  }
-  const int k = y / head_blocks;
-  const int hb = y - k * head_blocks;
+  // Work of this workgroup: head block hb of the flat range w (see
+  // decode_flat.h; groups of more than 128 heads run several head blocks,
+  // each re-reading the range).
+  const int w = blockIdx.x / head_blocks;
+  const int hb = blockIdx.x - w * head_blocks;
   const int G = H / K;
   const int cap = PAGED ? pg.max_blocks * pg.block_size : S_max;  // positions the cache holds
-  const int L_in = PAGED ? min(seq_lens[b], cap) : seq_lens[b];
-  int L = L_in, newpos = -1;
-  if (APPEND) {
-    bool room = L_in >= 0 && L_in < cap;
+  // lengths clamped into [0, cap], so no length can make a load leave the cache
+  auto len_in = [&](int bb) -> int { return min(max(seq_lens[bb], 0), cap); };
+  // length attended over: after the fused append when the cache has room
+  auto len_of = [&](int bb) -> int {
+    const int L_in = len_in(bb);
+    if (!APPEND) return min(L_in, fa.max_len);
+    bool room = L_in < cap;
     if (PAGED && room) {
-      const int id = pg.block_table[(size_t)b * pg.max_blocks + L_in / pg.block_size];
+      const int id = pg.block_table[(size_t)bb * pg.max_blocks + L_in / pg.block_size];
       room = id >= 0 && id < pg.num_blocks;
     }
-    if (room) {
-      newpos = L_in;
-      L = L_in + 1;
-    }
-    if (p == 0 && y == 0 && threadIdx.x == 0) lens_out[b] = L;
-  }
-  const int pt_b = balanced_part_tokens(L, part_tokens);
-  const int t0 = p * pt_b;
-  if (t0 >= L) return;  // partition beyond this sequence: nothing to do
-  const int t1 = min(t0 + pt_b, L);
+    return min(room ? L_in + 1 : L_in, fa.max_len);
+  };
+  // the lengths attended over and the split, for the combine pass
+  if (blockIdx.x == 0) flat_publish(B, K, len_of, meta);
+  const int total = flat_total(B, K, len_of);
+  const int R = flat_range(total, fa);
 
+  flat_for_each_segment(w, B, K, total, R, len_of,
+                        [&](int b, int k, int t0, int t1, int L, int slot) {
+  const int newpos = APPEND && L > len_in(b) ? L - 1 : -1;  // the appended row, if any
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -311,22 +299,23 @@ __global__ __launch_bounds__(64) void decode_split_bf16_kernel(
   l_run += __shfl_xor(l_run, 16);  // the head's denominator: sum of the lane groups' shares
   l_run += __shfl_xor(l_run, 32);
 
-  // ---- write the partition's partial state ----
-  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+  // ---- write the segment's partial state (slot rows = the group's heads) ----
+  const size_t row0 = (size_t)slot * G + (size_t)hb * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hl = 4 * g + i;
     if (hb * 16 + hl < G) {
-      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+      float* dst = part_acc + (row0 + hl) * D;
 #pragma unroll
       for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
     }
   }
   if (g == 0 && hq_ok) {
-    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    float* ml = part_ml + (row0 + n) * 2;
     ml[0] = m_run;
     ml[1] = l_run;
   }
+                        });
 }
 
 }  // namespace
@@ -339,13 +328,7 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
   if (decode_wide_supported(plan.head_blocks))  // G > 16: one KV read for all head blocks
     return launch_decode_wide_bf16(q, k_cache, v_cache, seq_lens, ws, plan, B, H, K, S_max, d,
                                    scale_log2, k_new, v_new, paged, stream);
-  // many (sequence, head) units -- a large batch -- : one-dimensional grid,
-  // partition slowest (measured on the ragged 70B layer, 512 units: 4%
-  // faster; on the Llama-3-8B layer, 128 units, the three-dimensional order
-  // is 1.3% faster)
-  const bool p_slowest = plan.parts > 1 && B * K * plan.head_blocks >= 256;
-  const dim3 grid = p_slowest ? dim3(plan.parts * K * plan.head_blocks * B)
-                              : dim3(plan.parts, K * plan.head_blocks, B);
+  const dim3 grid(plan.fa.n_wg * plan.head_blocks);
   const dim3 block(64);
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<__bf16*>(k_cache);
@@ -355,8 +338,8 @@ hipError_t launch_decode_split_bf16(const void* q, void* k_cache, void* v_cache,
   const PagedArgs pg = paged ? *paged : PagedArgs{nullptr, 16, 0, 1};
 #define GQA_SPLIT(DD, AP, PG)                                                                     \
   hipLaunchKernelGGL((decode_split_bf16_kernel<DD, AP, PG>), grid, block, 0, stream, qp, kp, vp,  \
-                     seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, plan.part_tokens, plan.parts, \
-                     plan.head_blocks, scale_log2, kn, vn, ws.lens, pg, p_slowest ? 1 : 0)
+                     seq_lens, ws.part_acc, ws.part_ml, B, H, K, S_max, plan.fa, plan.head_blocks,  \
+                     scale_log2, kn, vn, ws.meta, pg)
 #define GQA_SPLIT_D(DD)                                                                           \
   if (paged) {                                                                                    \
     if (k_new) GQA_SPLIT(DD, true, true); else GQA_SPLIT(DD, false, true);                        \

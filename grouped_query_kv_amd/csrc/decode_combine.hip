@@ -1,8 +1,9 @@
 // Decode combine pass: merges the partitions' online-softmax states.
 //
-// For query head h of sequence b with n active partitions (those starting
-// below L_b, of balanced_part_tokens(L_b, part_tokens) positions each)
-// holding (m_p, l_p, acc_p) in base-2 units:
+// For query head h of sequence b (KV head k = h / G), the partition pass left
+// one partial state per workgroup whose flat range met pair (b, k) (the flat
+// split of decode_flat.h, recomputed here from the same lengths); n such
+// partials (m_p, l_p, acc_p) in base-2 units merge as
 //     M = max_p m_p,  w_p = 2^(m_p - M),
 //     out = (sum_p w_p acc_p) / (sum_p w_p l_p),
 // which equals softmax-weighted sum over all L_b positions (the block-wise
@@ -18,24 +19,34 @@
 namespace gqa {
 namespace {
 
-// LENS_FROM_WS: after a fused append the lengths come from the workspace
-// (written by the partition pass), and the (b, h = 0) workgroup publishes them
-// to seq_lens -- no workgroup of this pass reads seq_lens, so there is no race.
-template <int D, bool OUT_BF16, bool LENS_FROM_WS>
+// The lengths come from the workspace (the partition pass recorded them with
+// the split).  PUBLISH_LENS: after a fused append the (b, h = 0) workgroup
+// writes them to seq_lens -- no workgroup of this pass reads seq_lens, so
+// there is no race.
+template <int D, bool OUT_BF16, bool PUBLISH_LENS>
 __global__ __launch_bounds__(64) void decode_combine_kernel(
     const float* __restrict__ part_acc, const float* __restrict__ part_ml,
-    int32_t* __restrict__ seq_lens, const int32_t* __restrict__ ws_lens, void* __restrict__ out,
-    int H, int part_tokens, int parts) {
+    int32_t* __restrict__ seq_lens, const int32_t* __restrict__ meta, void* __restrict__ out,
+    int B, int H, int K, FlatArgs fa) {
   constexpr int PER = D / 64;  // dims per lane
   __shared__ float wsh[64];
   const int bh = blockIdx.x;
   const int b = bh / H;
+  const int h = bh - b * H;
+  const int G = H / K;
+  const int k = h / G;
   const int lane = threadIdx.x;
-  const int L = LENS_FROM_WS ? ws_lens[b] : seq_lens[b];
-  const int pt_b = balanced_part_tokens(L, part_tokens);
-  const int n = L > 0 ? min(parts, (L + pt_b - 1) / pt_b) : 0;
-  const float2* ml = reinterpret_cast<const float2*>(part_ml) + (size_t)bh * parts;
-  const float* pa = part_acc + (size_t)bh * parts * D + lane * PER;
+  // the split the partition pass recorded: length, flat start, total
+  const int L = meta[b];
+  const int R = flat_range(meta[2 * B], fa);
+  const int base = meta[B + b] + k * pad32(L);  // flat start of pair (b, k)
+  const int w0 = base / R;
+  const int n = L > 0 ? (base + L - 1) / R - w0 + 1 : 0;  // partials of this pair
+  // partial p is slot w0 + p + b K + k, row h - k G
+  const size_t row = (size_t)(w0 + b * K + k) * G + (h - k * G);
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + row;
+  const float* pa = part_acc + row * D + lane * PER;
+  const size_t stride = (size_t)G;  // rows between consecutive slots
 
   // The first kEarly partitions' numerators are loaded up front, together
   // with the (max, sum) pairs, so the common case costs one memory round
@@ -45,11 +56,11 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 #pragma unroll
   for (int p = 0; p < kEarly; ++p)
 #pragma unroll
-    for (int j = 0; j < PER; ++j) early[p][j] = p < n ? pa[(size_t)p * D + j] : 0.f;
+    for (int j = 0; j < PER; ++j) early[p][j] = p < n ? pa[(size_t)p * stride * D + j] : 0.f;
 
   // global max over the partitions (lane-parallel loads)
   float M = -INFINITY;
-  for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p].x);
+  for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[p * stride].x);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
 
@@ -63,7 +74,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     const int p = p0 + lane;
     float w = 0.f;
     if (p < n) {
-      const float2 x = ml[p];
+      const float2 x = ml[p * stride];
       w = fast_exp2(x.x - M);
       den = fmaf(w, x.y, den);
     }
@@ -80,7 +91,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
     }
     for (int j2 = p0 == 0 ? kEarly : 0; j2 < cnt; ++j2) {
       const float wj = wsh[j2];
-      const float* src = pa + (size_t)(p0 + j2) * D;
+      const float* src = pa + (size_t)(p0 + j2) * stride * D;
 #pragma unroll
       for (int j = 0; j < PER; ++j) num[j] = fmaf(wj, src[j], num[j]);
     }
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
   const float inv = n > 0 ? 1.f / den : 0.f;
-  if (LENS_FROM_WS && bh - b * H == 0 && lane == 0) seq_lens[b] = L;
+  if (PUBLISH_LENS && h == 0 && lane == 0) seq_lens[b] = L;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const float o = n > 0 ? num[j] * inv : 0.f;
@@ -104,17 +115,17 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
 }  // namespace
 
 hipError_t launch_decode_combine(const DecodeWorkspace& ws, int32_t* seq_lens, void* out,
-                                 const DecodePlan& plan, int B, int H, int d, bool out_bf16,
-                                 bool lens_from_ws, hipStream_t stream) {
+                                 const DecodePlan& plan, int B, int H, int K, int d, bool out_bf16,
+                                 bool publish_lens, hipStream_t stream) {
   const dim3 grid(B * H), block(64);
 #define GQA_COMBINE(DD, OB, LW)                                                                  \
   hipLaunchKernelGGL((decode_combine_kernel<DD, OB, LW>), grid, block, 0, stream, ws.part_acc,   \
-                     ws.part_ml, seq_lens, ws.lens, out, H, plan.part_tokens, plan.parts)
+                     ws.part_ml, seq_lens, ws.meta, out, B, H, K, plan.fa)
 #define GQA_COMBINE_D(DD)                                                                        \
   if (out_bf16) {                                                                                \
-    if (lens_from_ws) GQA_COMBINE(DD, true, true); else GQA_COMBINE(DD, true, false);            \
+    if (publish_lens) GQA_COMBINE(DD, true, true); else GQA_COMBINE(DD, true, false);            \
   } else {                                                                                       \
-    if (lens_from_ws) GQA_COMBINE(DD, false, true); else GQA_COMBINE(DD, false, false);          \
+    if (publish_lens) GQA_COMBINE(DD, false, true); else GQA_COMBINE(DD, false, false);          \
   }
   if (d == 128) {
     GQA_COMBINE_D(128)

@@ -57,31 +57,31 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return as_bf16x8(u32x4{a.x, a.y, b.x, b.y});
 }
 
-// Three resident waves per SIMD (at most 168 registers): the in-flight K/V
-// chunk of a wave is half the bytes of the bf16 pass, so more waves are
-// needed to keep the same bytes in flight.  (Measured on the Llama-3-8B layer
-// and a 131072-token context: 10-15% faster than the unconstrained
-// allocation at two waves, and than 64-position chunks at two waves.)
+// Two resident waves per SIMD (at most 256 registers, no spills): the flat
+// split runs eight workgroups per CU (the in-flight K/V chunk of a wave is
+// half the bytes of the bf16 pass, so more waves than the bf16 pass's three
+// per CU are needed to keep the same bytes in flight; measured on the
+// Llama-3-8B layer: eight per CU 54.5 us, six 60.8 us, twelve 60.8 us).
 //
 // APPEND: the quantising append fused in.  The step's new rows k_new, v_new
 // (bf16) belong at position L_in = seq_lens[b] when the cache has room; it is
-// the last position of the sequence, so only workgroups of its last
-// partition see it.  Each of them quantises the rows by the cache rule (the
+// the last position of the sequence, so only the segment that ends the
+// sequence sees it.  Each of them quantises the rows by the cache rule (the
 // same fp32 operations as the standalone append, so the same codes and
 // scales) into its own slot of the workspace -- codes, and the 4-aligned
 // group of scales around the new position with the new scale in place --
 // and its loads take the slot instead of the cache for that position (a
 // pointer select, so the loop keeps its shape).  After the loop the first
 // head block copies the slot into the cache; no other workgroup of this
-// launch reads that cache row or scale.  The lengths after the append go to
-// `lens_out` for the combine pass.
+// launch reads that cache row or scale.  Workgroup 0 records the lengths
+// after the append with the split (decode_flat.h) for the combine pass.
 template <int D, bool APPEND>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void decode_split_int8_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_int8_kernel(
     const __bf16* __restrict__ q, int8_t* __restrict__ kc, int8_t* __restrict__ vc,
     float* __restrict__ ks, float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ part_acc, float* __restrict__ part_ml, int H, int K, int S_max,
-    int part_tokens, int parts, int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out, uint8_t* __restrict__ slots) {
+    float* __restrict__ part_acc, float* __restrict__ part_ml, int B, int H, int K, int S_max,
+    FlatArgs fa, int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ meta, uint8_t* __restrict__ slots) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;
   constexpr int NTILES = D / 16;
@@ -94,25 +94,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
 
   __shared__ __attribute__((aligned(16))) uint16_t vt[kChunk * LDS_ROW];
 
-  const int p = blockIdx.x;
-  const int k = blockIdx.y / head_blocks;
-  const int hb = blockIdx.y - k * head_blocks;
-  const int b = blockIdx.z;
+  // head block hb of flat range w (decode_flat.h; several head blocks only
+  // for groups of more than 128 heads)
+  const int w = blockIdx.x / head_blocks;
+  const int hb = blockIdx.x - w * head_blocks;
   const int G = H / K;
-  const int L_in = seq_lens[b];
-  int L = L_in, newpos = -1;
-  if (APPEND) {
-    if (L_in < S_max) {
-      newpos = L_in;
-      L = L_in + 1;
-    }
-    if (p == 0 && blockIdx.y == 0 && threadIdx.x == 0) lens_out[b] = L;
-  }
-  const int pt_b = balanced_part_tokens(L, part_tokens);
-  const int t0 = p * pt_b;
-  if (t0 >= L) return;
-  const int t1 = min(t0 + pt_b, L);
+  // length attended over: after the fused append when the cache has room
+  // lengths clamped into [0, S_max], so no length can make a load leave the cache
+  auto len_in = [&](int bb) -> int { return min(max(seq_lens[bb], 0), S_max); };
+  auto len_of = [&](int bb) -> int {
+    const int L_in = len_in(bb);
+    return min(APPEND && L_in < S_max ? L_in + 1 : L_in, fa.max_len);
+  };
+  // the lengths attended over and the split, for the combine pass
+  if (blockIdx.x == 0) flat_publish(B, K, len_of, meta);
+  const int total = flat_total(B, K, len_of);
+  const int R = flat_range(total, fa);
 
+  flat_for_each_segment(w, B, K, total, R, len_of,
+                        [&](int b, int k, int t0, int t1, int L, int slot_id) {
+  const int newpos = APPEND && L > len_in(b) ? L - 1 : -1;  // the appended row, if any
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
   const bool has_new = APPEND && newpos >= t0 && newpos < t1;  // wave-uniform
   const int s0_new = has_new ? (newpos & ~3) : -4;              // its scale group
   int8_t* slot = reinterpret_cast<int8_t*>(slots) +
-                 (APPEND ? ((size_t)blockIdx.z * gridDim.y + blockIdx.y) * (2 * D + 32) : 0);
+                 (APPEND ? (((size_t)b * K + k) * head_blocks + hb) * (2 * D + 32) : 0);
   float* slot_sc = reinterpret_cast<float*>(slot + 2 * D);
   if (has_new) {
     constexpr int E = D / 64;  // elements per lane
@@ -310,21 +311,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) void de
     if (lane < 2) (lane == 0 ? ksb : vsb)[newpos] = slot_sc[4 * lane + (newpos - s0_new)];
   }
 
-  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+  const size_t row0 = (size_t)slot_id * G + (size_t)hb * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hl = 4 * g + i;
     if (hb * 16 + hl < G) {
-      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+      float* dst = part_acc + (row0 + hl) * D;
 #pragma unroll
       for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
     }
   }
   if (g == 0 && hq_ok) {
-    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    float* ml = part_ml + (row0 + n) * 2;
     ml[0] = m_run;
     ml[1] = l_run;
   }
+                        });
 }
 
 }  // namespace
@@ -337,7 +339,7 @@ hipError_t launch_decode_split_int8(const void* q, void* k_codes, void* v_codes,
   if (decode_wide_supported(plan.head_blocks))  // G > 16: one code read for all head blocks
     return launch_decode_wide_int8(q, k_codes, v_codes, k_scales, v_scales, seq_lens, ws, plan, B,
                                    H, K, S_max, d, scale_log2, k_new, v_new, stream);
-  const dim3 grid(plan.parts, K * plan.head_blocks, B);
+  const dim3 grid(plan.fa.n_wg * plan.head_blocks);
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<int8_t*>(k_codes);
   auto vp = static_cast<int8_t*>(v_codes);
@@ -345,9 +347,8 @@ hipError_t launch_decode_split_int8(const void* q, void* k_codes, void* v_codes,
   auto vn = static_cast<const __bf16*>(v_new);
 #define GQA_I8(DD, AP)                                                                          \
   hipLaunchKernelGGL((decode_split_int8_kernel<DD, AP>), grid, dim3(64), 0, stream, qp, kp, vp,  \
-                     k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max,         \
-                     plan.part_tokens, plan.parts, plan.head_blocks, scale_log2, kn, vn, ws.lens, \
-                     ws.new_rows)
+                     k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, B, H, K, S_max,      \
+                     plan.fa, plan.head_blocks, scale_log2, kn, vn, ws.meta, ws.new_rows)
   if (d == 128) {
     if (k_new) GQA_I8(128, true); else GQA_I8(128, false);
   } else {

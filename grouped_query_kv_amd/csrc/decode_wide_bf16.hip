@@ -68,9 +68,9 @@ template <int D, bool APPEND, bool PAGED, int W, int SUB, int NS>
 __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
     const __bf16* __restrict__ q, __bf16* __restrict__ kc, __bf16* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, int H, int K, int S_max, int part_tokens, int parts,
+    float* __restrict__ part_ml, int B, int H, int K, int S_max, FlatArgs fa,
     float scale_log2, const __bf16* __restrict__ k_new, const __bf16* __restrict__ v_new,
-    int32_t* __restrict__ lens_out, PagedArgs pg) {
+    int32_t* __restrict__ meta, PagedArgs pg) {
   static_assert(D == 64 || D == 128, "head dimension");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   constexpr int KSTEPS = D / 32;
@@ -90,9 +90,6 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
   // never read), so every wave issues the same number of copies per block
   __shared__ __attribute__((aligned(16))) uint16_t sink[SURPLUS ? 512 : 8];
 
-  const int p = blockIdx.x;
-  const int k = blockIdx.y;
-  const int b = blockIdx.z;
   const int G = H / K;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -101,24 +98,27 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
   const int hb = wave;  // this wave's block of 16 heads
 
   const int cap = PAGED ? pg.max_blocks * pg.block_size : S_max;
-  const int L_in = PAGED ? min(seq_lens[b], cap) : seq_lens[b];
-  int L = L_in, newpos = -1;
-  if (APPEND) {
-    bool room = L_in >= 0 && L_in < cap;
+  // lengths clamped into [0, cap], so no length can make a load leave the cache
+  auto len_in = [&](int bb) -> int { return min(max(seq_lens[bb], 0), cap); };
+  // length attended over: after the fused append when the cache has room
+  auto len_of = [&](int bb) -> int {
+    const int L_in = len_in(bb);
+    if (!APPEND) return min(L_in, fa.max_len);
+    bool room = L_in < cap;
     if (PAGED && room) {
-      const int id = pg.block_table[(size_t)b * pg.max_blocks + L_in / pg.block_size];
+      const int id = pg.block_table[(size_t)bb * pg.max_blocks + L_in / pg.block_size];
       room = id >= 0 && id < pg.num_blocks;
     }
-    if (room) {
-      newpos = L_in;
-      L = L_in + 1;
-    }
-    if (p == 0 && k == 0 && threadIdx.x == 0) lens_out[b] = L;
-  }
-  const int pt_b = balanced_part_tokens(L, part_tokens);
-  const int t0 = p * pt_b;
-  if (t0 >= L) return;  // uniform over the workgroup
-  const int t1 = min(t0 + pt_b, L);
+    return min(room ? L_in + 1 : L_in, fa.max_len);
+  };
+  // the lengths attended over and the split, for the combine pass
+  if (blockIdx.x == 0 && wave == 0) flat_publish(B, K, len_of, meta);
+  const int total = flat_total(B, K, len_of);
+  const int R = flat_range(total, fa);
+
+  flat_for_each_segment(blockIdx.x, B, K, total, R, len_of,
+                        [&](int b, int k, int t0, int t1, int L, int slot) {
+  const int newpos = APPEND && L > len_in(b) ? L - 1 : -1;  // the appended row, if any
   const int last = t1 - 1;
 
   const int hq = hb * 16 + n;
@@ -306,21 +306,24 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+  const size_t row0 = (size_t)slot * G + (size_t)hb * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hl = 4 * g + i;
     if (hb * 16 + hl < G) {
-      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+      float* dst = part_acc + (row0 + hl) * D;
 #pragma unroll
       for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
     }
   }
   if (g == 0 && hq_ok) {
-    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    float* ml = part_ml + (row0 + n) * 2;
     ml[0] = m_run;
     ml[1] = l_run;
   }
+  // every wave is done with the ring before the next segment refills it
+  __syncthreads();
+                        });
 }
 
 }  // namespace
@@ -332,7 +335,7 @@ hipError_t launch_decode_wide_bf16(const void* q, void* k_cache, void* v_cache,
                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
                                    float scale_log2, const void* k_new, const void* v_new,
                                    const PagedArgs* paged, hipStream_t stream) {
-  const dim3 grid(plan.parts, K, B);
+  const dim3 grid(plan.fa.n_wg);
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<__bf16*>(k_cache);
   auto vp = static_cast<__bf16*>(v_cache);
@@ -342,8 +345,8 @@ hipError_t launch_decode_wide_bf16(const void* q, void* k_cache, void* v_cache,
   // one wave per 16-head block
 #define GQA_WIDE(DD, AP, PG, WW)                                                                  \
   hipLaunchKernelGGL((decode_wide_bf16_kernel<DD, AP, PG, WW, kSub, kRing>), grid,               \
-                     dim3(64 * WW), 0, stream, qp, kp, vp, seq_lens, ws.part_acc, ws.part_ml, H, K, \
-                     S_max, plan.part_tokens, plan.parts, scale_log2, kn, vn, ws.lens, pg)
+                     dim3(64 * WW), 0, stream, qp, kp, vp, seq_lens, ws.part_acc, ws.part_ml, B, H, K, \
+                     S_max, plan.fa, scale_log2, kn, vn, ws.meta, pg)
 #define GQA_WIDE_W(DD, AP, PG)                                                                   \
   switch (plan.head_blocks) {                                                                     \
     case 2: GQA_WIDE(DD, AP, PG, 2); break;                                                       \

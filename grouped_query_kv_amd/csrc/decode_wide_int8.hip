@@ -73,9 +73,9 @@ template <int D, bool APPEND, int W>
 __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     const __bf16* __restrict__ q, int8_t* __restrict__ kc, int8_t* __restrict__ vc,
     float* __restrict__ ks, float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ part_acc, float* __restrict__ part_ml, int H, int K, int S_max,
-    int part_tokens, int parts, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ lens_out) {
+    float* __restrict__ part_acc, float* __restrict__ part_ml, int B, int H, int K, int S_max,
+    FlatArgs fa, float scale_log2, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ meta) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;
   constexpr int NTILES = D / 16;
@@ -98,9 +98,6 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   // target of the surplus copies (they repeat a real copy; never read)
   __shared__ __attribute__((aligned(16))) int8_t sink[SURPLUS ? 1024 : 16];
 
-  const int p = blockIdx.x;
-  const int k = blockIdx.y;
-  const int b = blockIdx.z;
   const int G = H / K;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -108,19 +105,21 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   const int g = lane >> 4;
   const int hb = wave;  // this wave's block of 16 heads
 
-  const int L_in = seq_lens[b];
-  int L = L_in, newpos = -1;
-  if (APPEND) {
-    if (L_in < S_max) {
-      newpos = L_in;
-      L = L_in + 1;
-    }
-    if (p == 0 && k == 0 && threadIdx.x == 0) lens_out[b] = L;
-  }
-  const int pt_b = balanced_part_tokens(L, part_tokens);
-  const int t0 = p * pt_b;
-  if (t0 >= L) return;  // uniform over the workgroup
-  const int t1 = min(t0 + pt_b, L);
+  // length attended over: after the fused append when the cache has room
+  // lengths clamped into [0, S_max], so no length can make a load leave the cache
+  auto len_in = [&](int bb) -> int { return min(max(seq_lens[bb], 0), S_max); };
+  auto len_of = [&](int bb) -> int {
+    const int L_in = len_in(bb);
+    return min(APPEND && L_in < S_max ? L_in + 1 : L_in, fa.max_len);
+  };
+  // the lengths attended over and the split, for the combine pass
+  if (blockIdx.x == 0 && wave == 0) flat_publish(B, K, len_of, meta);
+  const int total = flat_total(B, K, len_of);
+  const int R = flat_range(total, fa);
+
+  flat_for_each_segment(blockIdx.x, B, K, total, R, len_of,
+                        [&](int b, int k, int t0, int t1, int L, int slot_id) {
+  const int newpos = APPEND && L > len_in(b) ? L - 1 : -1;  // the appended row, if any
   const int last = t1 - 1;
 
   const int hq = hb * 16 + n;
@@ -373,21 +372,25 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     }
   }
 
-  const size_t hrow0 = (size_t)b * H + (size_t)k * G + (size_t)hb * 16;
+  const size_t row0 = (size_t)slot_id * G + (size_t)hb * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int hl = 4 * g + i;
     if (hb * 16 + hl < G) {
-      float* dst = part_acc + ((hrow0 + hl) * parts + p) * D;
+      float* dst = part_acc + (row0 + hl) * D;
 #pragma unroll
       for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
     }
   }
   if (g == 0 && hq_ok) {
-    float* ml = part_ml + ((hrow0 + n) * parts + p) * 2;
+    float* ml = part_ml + (row0 + n) * 2;
     ml[0] = m_run;
     ml[1] = l_run;
   }
+  // every wave is done with the ring and the bf16 tiles before the next
+  // segment refills them
+  __syncthreads();
+                        });
 }
 
 }  // namespace
@@ -397,7 +400,7 @@ hipError_t launch_decode_wide_int8(const void* q, void* k_codes, void* v_codes, 
                                    const DecodeWorkspace& ws, const DecodePlan& plan, int B, int H,
                                    int K, int S_max, int d, float scale_log2, const void* k_new,
                                    const void* v_new, hipStream_t stream) {
-  const dim3 grid(plan.parts, K, B);
+  const dim3 grid(plan.fa.n_wg);
   auto qp = static_cast<const __bf16*>(q);
   auto kp = static_cast<int8_t*>(k_codes);
   auto vp = static_cast<int8_t*>(v_codes);
@@ -405,8 +408,8 @@ hipError_t launch_decode_wide_int8(const void* q, void* k_codes, void* v_codes, 
   auto vn = static_cast<const __bf16*>(v_new);
 #define GQA_WI8(DD, AP, WW)                                                                      \
   hipLaunchKernelGGL((decode_wide_int8_kernel<DD, AP, WW>), grid, dim3(64 * WW), 0, stream, qp,  \
-                     kp, vp, k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, H, K, S_max, \
-                     plan.part_tokens, plan.parts, scale_log2, kn, vn, ws.lens)
+                     kp, vp, k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, B, H, K,     \
+                     S_max, plan.fa, scale_log2, kn, vn, ws.meta)
 #define GQA_WI8_W(DD, AP)                                                                        \
   switch (plan.head_blocks) {                                                                     \
     case 2: GQA_WI8(DD, AP, 2); break;                                                            \

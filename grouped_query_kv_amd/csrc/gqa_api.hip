@@ -2,6 +2,7 @@
 // The declarations and their contracts are in include/gqa.h.
 #include <cmath>
 #include <cstdarg>
+#include <algorithm>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -54,52 +55,82 @@ struct TimedRegion {
 
 namespace gqa {
 
-DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, int max_part_tokens) {
+namespace {
+
+// Workgroups of each partition pass.  Every workgroup streams the same
+// number of positions, so the pass takes as long as the CU with the most
+// workgroups: counts are whole multiples of the 256 CUs (measured on the
+// decode workloads: a count just above a multiple of 256 leaves a few CUs one
+// range more and costs up to 20%).  Measured best per pass: the one-wave
+// bf16 pass three workgroups per CU (2-5% ahead of four, 10% ahead of two
+// and of eight); the int8 pass eight (two waves per SIMD); a multi-wave pass
+// (groups of more than 16 heads, one wave per 16-head block) four; the fp32
+// pass's 256-thread workgroups two.
+constexpr int kCUs = 256;
+int target_wgs(PassKind kind, int head_blocks) {
+  if (kind == PassKind::kF32) return 2 * kCUs;
+  if (head_blocks > 1) return 4 * kCUs;
+  return kind == PassKind::kInt8 ? 8 * kCUs : 3 * kCUs;
+}
+// the most workgroups any partition pass runs for these group sizes (what
+// the workspace is sized for, so one size serves every decode entry point)
+int max_target_wgs(int head_blocks) {
+  return std::max({target_wgs(PassKind::kBf16, head_blocks), target_wgs(PassKind::kInt8, head_blocks),
+                   target_wgs(PassKind::kF32, head_blocks)});
+}
+
+// Workgroups a call may need at most: the target, or more when a range is
+// capped (paged: the block ids of a segment fit one per lane) -- enough that
+// n_wg ranges of the capped length cover the largest possible total, still a
+// multiple of the CU count.
+long long needed_wgs(int B, int K, int max_seq_len, int r_max, long long target) {
+  if (r_max <= 0) return target;
+  const long long r = r_max / 32 * 32 - 32;  // flat_range may step 32 below the cap
+  const long long tmax = (long long)K * B * pad32(max_seq_len);
+  const long long n = (tmax + r - 1) / r;
+  return std::max(target, (n + kCUs - 1) / kCUs * kCUs);
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, PassKind kind, int r_max) {
   DecodePlan p{};
-  const int G = H / K;
-  p.head_blocks = (G + 15) / 16;
-  const long long units = (long long)B * K * p.head_blocks;
-  const int L = max_seq_len > 0 ? max_seq_len : 1;
-  // One single-wave workgroup per partition.  Aim at 3072 workgroups over
-  // the 256 CUs -- one round of the int8 pass's three resident waves per
-  // SIMD, one and a half of the bf16 pass's two (sweeps of the partition
-  // length put this within a few percent of the best fixed length on every
-  // decode workload) -- with equal partitions of a multiple of 32 positions.
-  const long long target = 256LL * 4 * 3;
-  long long parts = target / (units > 0 ? units : 1);
-  if (parts < 1) parts = 1;
-  long long t = (L + parts - 1) / parts;
-  t = (t + 31) / 32 * 32;
-  int pt = (int)(t < 64 ? 64 : t);
-  // Partition starts that are multiples of 64 KiB of cache rows make every
-  // partition of a head begin on the same HBM channel; measured on the ragged
-  // 70B layer: 512- and 768-position partitions (bf16, d = 128) are 8-15%
-  // slower than their neighbours.  Step past such lengths.
-  if (((long long)pt * d * 2) % 65536 == 0) pt += 32;
-  if (max_part_tokens > 0 && pt > max_part_tokens) pt = max_part_tokens / 32 * 32;
-  p.part_tokens = pt;
-  p.parts = (L + pt - 1) / pt;
+  p.G = H / K;
+  p.head_blocks = (p.G + 15) / 16;
+  const int eb = kind == PassKind::kF32 ? 4 : (kind == PassKind::kInt8 ? 1 : 2);
+  p.fa.n_wg = (int)needed_wgs(B, K, max_seq_len, r_max, target_wgs(kind, p.head_blocks));
+  p.fa.row_bytes = d * eb;
+  p.fa.r_min = 32;
+  p.fa.r_max = r_max > 0 ? r_max / 32 * 32 : (1 << 30);
+  p.fa.max_len = max_seq_len;
+  p.slots = needed_wgs(B, K, max_seq_len, r_max, max_target_wgs(p.head_blocks)) + (long long)B * K;
   return p;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d) {
-  const size_t rows = (size_t)B * H * p.parts;
+static size_t workspace_bytes_for(const DecodePlan& p, int B, int K, int d) {
+  const size_t rows = (size_t)p.slots * p.G;
   return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float)) +
-         align256((size_t)B * sizeof(int32_t)) + align256((size_t)B * H * (2 * d + 32));
+         align256((size_t)(2 * B + 1) * sizeof(int32_t)) +
+         align256((size_t)B * K * p.head_blocks * (2 * d + 32));
 }
 
-DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d) {
-  const size_t rows = (size_t)B * H * p.parts;
+size_t decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d, int r_max) {
+  const DecodePlan p = plan_decode(B, H, K, max_seq_len, d, PassKind::kBf16, r_max);
+  return workspace_bytes_for(p, B, K, d);
+}
+
+DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int K, int d) {
+  const size_t rows = (size_t)p.slots * p.G;
   char* c = static_cast<char*>(base);
   DecodeWorkspace w;
   w.part_acc = reinterpret_cast<float*>(c);
   c += align256(rows * d * sizeof(float));
   w.part_ml = reinterpret_cast<float*>(c);
   c += align256(rows * 2 * sizeof(float));
-  w.lens = reinterpret_cast<int32_t*>(c);
-  c += align256((size_t)B * sizeof(int32_t));
+  w.meta = reinterpret_cast<int32_t*>(c);
+  c += align256((size_t)(2 * B + 1) * sizeof(int32_t));
   w.new_rows = reinterpret_cast<uint8_t*>(c);
   return w;
 }
@@ -154,10 +185,15 @@ static int validate_heads(const char* fn, int B, int H, int K, int d) {
   return GQA_OK;
 }
 
+// The flat split indexes positions with 32-bit integers.
+static bool flat_fits(int B, int K, int max_seq_len) {
+  return (long long)K * B * gqa::pad32(max_seq_len) < (1LL << 30);
+}
+
 size_t gqa_decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d) {
   if (B < 1 || H < 1 || K < 1 || K > H || H % K || max_seq_len < 0 || (d != 64 && d != 128)) return 0;
-  const gqa::DecodePlan p = gqa::plan_decode(B, H, K, max_seq_len, d);
-  return gqa::decode_workspace_bytes(p, B, H, d);
+  if (!flat_fits(B, K, max_seq_len)) return 0;
+  return gqa::decode_workspace_bytes(B, H, K, max_seq_len, d);
 }
 
 // Shared body of gqa_decode and gqa_decode_append (k_new == nullptr: no append).
@@ -189,8 +225,11 @@ static int decode_impl(const char* fn, const void* q, const void* k_new, const v
       (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
     return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
-  const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d);
-  const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
+  if (!flat_fits(B, K, max_seq_len))
+    return fail(GQA_ERR_UNSUPPORTED, "%s: B * K * max_seq_len too large (2^30 positions)", fn);
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d,
+                                                dtype == GQA_BF16 ? gqa::PassKind::kBf16 : gqa::PassKind::kF32);
+  const size_t need = gqa::decode_workspace_bytes(B, H, K, max_seq_len, d);
   if (use_static) {
     if (need > kStaticScratchBytes)
       return fail(GQA_ERR_WORKSPACE,
@@ -202,7 +241,7 @@ static int decode_impl(const char* fn, const void* q, const void* k_new, const v
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
                 need, workspace ? workspace_bytes : (size_t)0);
-  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, H, d);
+  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, K, d);
   const float scale_log2 = scale * gqa::kLog2eHost;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int r;
@@ -217,8 +256,8 @@ static int decode_impl(const char* fn, const void* q, const void* k_new, const v
                   "partition-pass launch");
   }
   if (r) return r;
-  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16,
-                                           k_new != nullptr, s),
+  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, K, d,
+                                           out_dtype == GQA_BF16, k_new != nullptr, s),
                 "combine-pass launch");
   return r ? r : ok();
 }
@@ -321,8 +360,8 @@ size_t gqa_decode_paged_workspace_bytes(int B, int H, int K, int max_seq_len, in
   if (B < 1 || H < 1 || K < 1 || K > H || H % K || max_seq_len < 0 || (d != 64 && d != 128) ||
       block_size < 16 || block_size % 16)
     return 0;
-  const gqa::DecodePlan p = gqa::plan_decode(B, H, K, max_seq_len, d, paged_max_part_tokens(block_size));
-  return gqa::decode_workspace_bytes(p, B, H, d);
+  if (!flat_fits(B, K, max_seq_len)) return 0;
+  return gqa::decode_workspace_bytes(B, H, K, max_seq_len, d, paged_max_part_tokens(block_size));
 }
 
 // Shared body of gqa_decode_paged and gqa_decode_append_paged (k_new == nullptr: no append).
@@ -347,13 +386,16 @@ static int decode_paged_impl(const char* fn, const void* q, const void* k_new, c
       (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
       (reinterpret_cast<uintptr_t>(seq_lens) & 3u) || (reinterpret_cast<uintptr_t>(block_table) & 3u))
     return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
-  const gqa::DecodePlan plan =
-      gqa::plan_decode(B, H, K, max_seq_len, d, paged_max_part_tokens(block_size));
-  const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
+  if (!flat_fits(B, K, max_seq_len))
+    return fail(GQA_ERR_UNSUPPORTED, "%s: B * K * max_seq_len too large (2^30 positions)", fn);
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d, gqa::PassKind::kBf16,
+                                                paged_max_part_tokens(block_size));
+  const size_t need =
+      gqa::decode_workspace_bytes(B, H, K, max_seq_len, d, paged_max_part_tokens(block_size));
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
                 need, workspace ? workspace_bytes : (size_t)0);
-  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, H, d);
+  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, K, d);
   const gqa::PagedArgs pg{block_table, block_size, max_blocks, num_blocks};
   hipStream_t s = static_cast<hipStream_t>(stream);
   int r;
@@ -365,8 +407,8 @@ static int decode_paged_impl(const char* fn, const void* q, const void* k_new, c
                   "partition-pass launch");
   }
   if (r) return r;
-  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16,
-                                           k_new != nullptr, s),
+  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, K, d,
+                                           out_dtype == GQA_BF16, k_new != nullptr, s),
                 "combine-pass launch");
   return r ? r : ok();
 }
@@ -449,12 +491,14 @@ static int decode_int8_impl(const char* fn, const void* q, const void* k_new, co
       !aligned16(v_scales) || !aligned16(out) || (reinterpret_cast<uintptr_t>(seq_lens) & 3u) ||
       (k_new && (!aligned16(k_new) || !aligned16(v_new))))
     return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
-  const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d);
-  const size_t need = gqa::decode_workspace_bytes(plan, B, H, d);
+  if (!flat_fits(B, K, max_seq_len))
+    return fail(GQA_ERR_UNSUPPORTED, "%s: B * K * max_seq_len too large (2^30 positions)", fn);
+  const gqa::DecodePlan plan = gqa::plan_decode(B, H, K, max_seq_len, d, gqa::PassKind::kInt8);
+  const size_t need = gqa::decode_workspace_bytes(B, H, K, max_seq_len, d);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(GQA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn,
                 need, workspace ? workspace_bytes : (size_t)0);
-  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, H, d);
+  const gqa::DecodeWorkspace ws = gqa::carve_decode_workspace(workspace, plan, B, K, d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   int r;
   {
@@ -465,8 +509,8 @@ static int decode_int8_impl(const char* fn, const void* q, const void* k_new, co
                   "partition-pass launch");
   }
   if (r) return r;
-  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, d, out_dtype == GQA_BF16,
-                                           k_new != nullptr, s),
+  r = check_hip(gqa::launch_decode_combine(ws, seq_lens, out, plan, B, H, K, d,
+                                           out_dtype == GQA_BF16, k_new != nullptr, s),
                 "combine-pass launch");
   return r ? r : ok();
 }

@@ -6,51 +6,50 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "decode_flat.h"
+
 namespace gqa {
 
 constexpr float kLog2eHost = 1.4426950408889634f;  // 1 / ln(2)
 
-// Split plan of one decode call: the cache positions [0, max_seq_len) are
-// cut into `parts` partitions of `part_tokens` positions; the query heads of
-// a group are handled in `head_blocks` blocks of at most 16 heads.
+// Split plan of one decode call: the flat split of decode_flat.h.  The
+// partition pass runs fa.n_wg workgroups; the workspace holds `slots`
+// partial states of G head rows each (slot w + b K + k for workgroup w's
+// segment of pair (b, k), so at most n_wg + B K slots).
+enum class PassKind { kBf16, kInt8, kF32 };
+
 struct DecodePlan {
-  int part_tokens;
-  int parts;
-  int head_blocks;
+  FlatArgs fa;
+  int G;          // query heads per KV head (rows of a slot)
+  int head_blocks;  // ceil(G / 16): waves of the wide passes
+  long long slots;  // slots the workspace holds
 };
 
-DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, int max_part_tokens = 0);
-
-// Partition length of a sequence of L positions under a plan of `pt`
-// positions per partition: the ceil(L / pt) partitions are made equal
-// (rounded up to a multiple of 32, so never longer than pt), so that the
-// last partition of a short or ragged sequence is not a small leftover.
-// Every partition pass and the combine pass use it, so they agree on which
-// partitions exist: p is active iff p * balanced_part_tokens(L, pt) < L.
-__host__ __device__ inline int balanced_part_tokens(int L, int pt) {
-  if (L <= 0) return pt;
-  const int n = (L + pt - 1) / pt;
-  const int even = (L + n - 1) / n;
-  return (even + 31) / 32 * 32;
-}
+// kind: the partition pass that will run; r_max: largest range (paged:
+// 63 block_size rounded down to 32; else 0 = none).  ws_n_wg: the
+// workgroup count the workspace is sized for (the largest of any kind for
+// these sizes, so one workspace size serves every decode entry point).
+DecodePlan plan_decode(int B, int H, int K, int max_seq_len, int d, PassKind kind, int r_max = 0);
+size_t decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d, int r_max = 0);
 
 // Workspace layout of a decode call:
-//   part_acc [B*H][parts][d]   fp32 un-normalised partial outputs
-//   part_ml  [B*H][parts][2]   fp32 running max (log2 units) and running sum
-//   lens     [B]               int32 lengths after a fused append
-//   new_rows [B*H][2d + 32]    bytes: per workgroup slot of a fused int8
-//                              append (codes of the new K and V rows and
-//                              their 4-aligned scale groups); B*K*head_blocks
-//                              <= B*H slots are used
+//   part_acc [slots][G][d]      fp32 un-normalised partial outputs
+//   part_ml  [slots][G][2]      fp32 running max (log2 units) and running sum
+//   meta     [2B + 1]           int32: the lengths attended over, the flat
+//                               starts of the sequences and the total (the
+//                               split, recorded by the partition pass)
+//   new_rows [B*K*head_blocks][2d + 32]  bytes: per (sequence, KV head, head
+//                               block) slot of a fused int8 append in the
+//                               one-wave pass (codes of the new K and V rows
+//                               and their 4-aligned scale groups)
 struct DecodeWorkspace {
   float* part_acc;
   float* part_ml;
-  int32_t* lens;
+  int32_t* meta;
   uint8_t* new_rows;
 };
-size_t decode_workspace_bytes(const DecodePlan& p, int B, int H, int d);
-// (the workspace holds part_acc, part_ml, lens and new_rows, each 256-byte aligned)
-DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int H, int d);
+// (each region 256-byte aligned; sized for the plan's slots)
+DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int K, int d);
 
 // ---- launchers (each returns the hipGetLastError() of its launch) ----
 
@@ -128,11 +127,12 @@ hipError_t launch_decode_wide_int8(const void* q, void* k_codes, void* v_codes, 
                                    int K, int S_max, int d, float scale_log2, const void* k_new,
                                    const void* v_new, hipStream_t stream);
 
-// Combine pass: partials -> out (fp32 or bf16).  lens_from_ws: lengths come
-// from the workspace (fused append) and are published to seq_lens.
+// Combine pass: partials -> out (fp32 or bf16).
+// publish_lens: write the lengths the partition pass attended over (after a
+// fused append) to seq_lens.
 hipError_t launch_decode_combine(const DecodeWorkspace& ws, int32_t* seq_lens, void* out,
-                                 const DecodePlan& plan, int B, int H, int d, bool out_bf16,
-                                 bool lens_from_ws, hipStream_t stream);
+                                 const DecodePlan& plan, int B, int H, int K, int d, bool out_bf16,
+                                 bool publish_lens, hipStream_t stream);
 
 // Prefill family (bf16 in): S queries per sequence over L_b keys
 // (kv_lens[b], or S_kv when kv_lens is null); causal: key j visible to query
