@@ -88,10 +88,10 @@ def recorded_traffic(kernel: str, workload: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f)[kernel]
+            rec = json.load(f)["workloads"][workload]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("workload") != workload:
+    if rec.get("kernel") != kernel:
         return None
     if sources_code_sha256(rec["sources"]) != rec["sources_code_sha256"]:
         return None

@@ -27,13 +27,16 @@ def test_code_hash_separates_files(tmp_path):
 
 
 def test_traffic_records_are_well_formed():
-    """Each record names its workload, existing source files, a code hash
-    and byte counts; a record is only reported for its own workload."""
-    recs = json.loads((ROOT / "profiles" / "traffic.json").read_text())
-    for kernel, rec in recs.items():
-        if not isinstance(rec, dict):
-            continue
+    """Each record names its kernel, existing source files, a code hash, the
+    counter means and their scale factors, and byte counts that follow from
+    them; a record is only reported for its own workload and kernel."""
+    recs = json.loads((ROOT / "profiles" / "traffic.json").read_text())["workloads"]
+    assert {"decode_llama3_8b", "decode_70b_ragged", "decode_long_131k"} <= set(recs)
+    for workload, rec in recs.items():
         assert all((ROOT / s).is_file() for s in rec["sources"])
         assert len(rec["sources_code_sha256"]) == 64
         assert rec["read_bytes"] > 0 and rec["write_bytes"] > 0
-        assert bench.recorded_traffic(kernel, "no_such_workload") is None
+        assert abs(rec["read_bytes"] - rec["fetch_kib_mean"] * rec["fetch_scale"] * 1024) < 1024
+        assert abs(rec["write_bytes"] - rec["write_kib_mean"] * rec["write_scale"] * 1024) < 1024
+        assert bench.recorded_traffic(rec["kernel"], "no_such_workload") is None
+        assert bench.recorded_traffic("no_such_kernel", workload) is None
