@@ -476,32 +476,31 @@ def gqa_decode_append_int8(q, k_new, v_new, k_codes, v_codes, k_scales, v_scales
         GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
-def gqa_prefill_causal(q, k, v, out, scale: float, stream=None) -> None:
-    """Causal GQA over a prefix: q/out [B,H,S,d], k/v [B,K,S_max,d] (rows < S used)."""
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(k, "k", 4, (torch.bfloat16,))
-    _need(v, "v", 4, (torch.bfloat16,))
-    _need(out, "out", 4)
-    B, H, S, d = q.shape
-    Bk, K, S_max, dk = k.shape
-    if Bk != B or dk != d or v.shape != k.shape or tuple(out.shape) != (B, H, S, d):
-        raise ValueError("shape mismatch between q, k, v and out")
-    lib = load_library()
-    _check("gqa_prefill_causal", lib.gqa_prefill_causal(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, K, S, S_max, d,
-        float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
-
-
 def _prefill_shapes(q, k, v, out):
-    _need(q, "q", 4, (torch.bfloat16,))
-    _need(k, "k", 4, (torch.bfloat16,))
-    _need(v, "v", 4, (torch.bfloat16,))
+    """Shapes of a prefill-family call: bf16 inputs (bf16 or fp32 output) or
+    fp32 inputs and output; q/out [B,H,S,d], k/v [B,K,S_max,d]."""
+    _need(q, "q", 4)
+    _need(k, "k", 4)
+    _need(v, "v", 4)
     _need(out, "out", 4)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    if q.dtype == torch.float32 and out.dtype != torch.float32:
+        raise ValueError("fp32 inputs need an fp32 output")
     B, H, S, d = q.shape
     Bk, K, S_max, dk = k.shape
     if Bk != B or dk != d or v.shape != k.shape or tuple(out.shape) != (B, H, S, d):
         raise ValueError("shape mismatch between q, k, v and out")
     return B, H, S, d, K, S_max
+
+
+def gqa_prefill_causal(q, k, v, out, scale: float, stream=None) -> None:
+    """Causal GQA over a prefix: q/out [B,H,S,d], k/v [B,K,S_max,d] (rows < S used)."""
+    B, H, S, d, K, S_max = _prefill_shapes(q, k, v, out)
+    lib = load_library()
+    _check("gqa_prefill_causal", lib.gqa_prefill_causal(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, K, S, S_max, d,
+        float(scale), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def gqa_prefill_chunk(q, k_cache, v_cache, seq_lens, out, scale: float, stream=None) -> None:
@@ -513,7 +512,7 @@ def gqa_prefill_chunk(q, k_cache, v_cache, seq_lens, out, scale: float, stream=N
         raise ValueError("seq_lens must have B entries")
     _check("gqa_prefill_chunk", load_library().gqa_prefill_chunk(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
-        B, H, K, S, S_max, d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
+        B, H, K, S, S_max, d, float(scale), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def gqa_cross_attention(q, k, v, kv_lens, out, scale: float, stream=None) -> None:
@@ -525,7 +524,7 @@ def gqa_cross_attention(q, k, v, kv_lens, out, scale: float, stream=None) -> Non
         raise ValueError("kv_lens must have B entries")
     _check("gqa_cross_attention", load_library().gqa_cross_attention(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_lens.data_ptr(), out.data_ptr(),
-        B, H, K, S, S_max, d, float(scale), GQA_BF16, _DTYPE_CODE[out.dtype], _stream(stream)))
+        B, H, K, S, S_max, d, float(scale), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out.dtype], _stream(stream)))
 
 
 def gqa_kv_append_rows(k_new, v_new, k_cache, v_cache, seq_lens, stream=None) -> None:

@@ -465,9 +465,14 @@ static int prefill_impl(const char* fn, const void* q, const void* k, const void
     return fail(GQA_ERR_INVALID, "%s: need S >= 1 and key lengths <= S_max", fn);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(GQA_ERR_INVALID, "%s: scale must be finite and > 0", fn);
-  if (dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "%s: only bf16 inputs (matrix-core path)", fn);
-  if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
-    return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
+  if (dtype == GQA_F32) {
+    if (out_dtype != GQA_F32) return fail(GQA_ERR_UNSUPPORTED, "%s: f32 input needs f32 output", fn);
+  } else if (dtype == GQA_BF16) {
+    if (out_dtype != GQA_BF16 && out_dtype != GQA_F32)
+      return fail(GQA_ERR_UNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
+  } else {
+    return fail(GQA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  }
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       (reinterpret_cast<uintptr_t>(kv_lens) & 3u))
     return fail(GQA_ERR_INVALID, "%s: misaligned pointer", fn);
@@ -475,8 +480,11 @@ static int prefill_impl(const char* fn, const void* q, const void* k, const void
   int r;
   {
     TimedRegion timed(s);
-    r = check_hip(gqa::launch_prefill_bf16(q, k, v, out, kv_lens, B, H, K, S, S_kv, S_max, d,
-                                           scale * gqa::kLog2eHost, out_dtype == GQA_BF16, causal, s),
+    r = check_hip(dtype == GQA_BF16
+                      ? gqa::launch_prefill_bf16(q, k, v, out, kv_lens, B, H, K, S, S_kv, S_max, d,
+                                                 scale * gqa::kLog2eHost, out_dtype == GQA_BF16, causal, s)
+                      : gqa::launch_prefill_f32(q, k, v, out, kv_lens, B, H, K, S, S_kv, S_max, d,
+                                                scale * gqa::kLog2eHost, causal, s),
                   "prefill launch");
   }
   return r ? r : ok();

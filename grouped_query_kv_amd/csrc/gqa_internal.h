@@ -142,6 +142,11 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                int S_max, int d, float scale_log2, bool out_bf16, bool causal,
                                hipStream_t stream);
 
+// The same family for fp32 inputs and outputs (vector ALUs, fp32 throughout).
+hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* out,
+                              const int32_t* kv_lens, int B, int H, int K, int S, int S_kv, int S_max,
+                              int d, float scale_log2, bool causal, hipStream_t stream);
+
 // seq_lens[b] += T where L + T <= S_max (run after the launch that wrote the rows).
 hipError_t launch_bump_lens(int32_t* seq_lens, int B, int T, int S_max, hipStream_t stream);
 

@@ -297,8 +297,10 @@ int gqa_decode_append_int8(const void* q, const void* k_new, const void* v_new, 
  * for i in [0, S).  k and v are [B, K, S_max, d] with S <= S_max; rows >= S
  * are never read.  (pinghaoyang.com.cn, decode memory ledger: prefill
  * computes the whole prefix in parallel; row i equals decode step i.)
- * dtype must be GQA_BF16 (bf16 matrix-core path, fp32 accumulation);
- * out_dtype GQA_BF16 or GQA_F32; scale finite and > 0.
+ * dtype GQA_BF16 (bf16 matrix-core path, fp32 accumulation; out_dtype
+ * GQA_BF16 or GQA_F32) or GQA_F32 (vector-ALU path, fp32 throughout;
+ * out_dtype GQA_F32); scale finite and > 0.  Any other pair returns
+ * GQA_ERR_UNSUPPORTED.
  */
 int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
                        int B, int H, int K, int S, int S_max, int d, float scale,
@@ -315,7 +317,7 @@ int gqa_prefill_causal(const void* q, const void* k, const void* v, void* out,
  * positions at once -- a chunk is such a run continuing a cache.)
  * gqa_prefill_causal is the case L_b = S.  Device-side contract:
  * S <= seq_lens[b] <= S_max (a query with no visible row gets zeros).
- * dtype GQA_BF16; out_dtype GQA_BF16 or GQA_F32; scale finite and > 0.
+ * Types as gqa_prefill_causal; scale finite and > 0.
  */
 int gqa_prefill_chunk(const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* seq_lens, void* out, int B, int H, int K, int S, int S_max,

@@ -132,7 +132,10 @@ def test_append_rejects(lib, args, code):
 
 
 @pytest.mark.parametrize("args,code", [
-    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 8, 16, 128, 0.1, B.GQA_F32, B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 8, 16, 128, 0.1, B.GQA_F32, B.GQA_BF16), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 8, 16, 128, 0.1, 7, B.GQA_F32), B.GQA_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 8, 16, 128, float("nan"), B.GQA_F32, B.GQA_F32), B.GQA_ERR_INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 3, 16, 16, 128, 0.1, B.GQA_F32, B.GQA_F32), B.GQA_ERR_INVALID),
     ((FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 16, 8, 128, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_INVALID),
     ((FAKE, FAKE, FAKE, FAKE, 1, 8, 3, 16, 16, 128, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_INVALID),
     ((FAKE, FAKE, FAKE, None, 1, 8, 2, 16, 16, 128, 0.1, B.GQA_BF16, B.GQA_BF16), B.GQA_ERR_INVALID),
