@@ -111,5 +111,52 @@ def build(verbose: bool = True) -> Path:
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the whole
+# library, for the CPU tests of the C ABI's validation layer: every
+# -fsanitize flag applies to the host compilation only (device code is
+# built as usual), and the objects are linked by the host compiler.
+SAN_DIR = BUILD / "san"
+SAN_LIB = SAN_DIR / "libgqa.so"
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+HOST_CXX = os.environ.get("HOST_CXX", "/opt/rocm/llvm/bin/clang++")
+
+
+def asan_runtime() -> str:
+    """Path of the host compiler's shared AddressSanitizer runtime."""
+    r = subprocess.run([HOST_CXX, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build_sanitized(verbose: bool = True) -> Path:
+    """Compile every source with host ASan/UBSan and link _build/san/libgqa.so."""
+    SAN_DIR.mkdir(parents=True, exist_ok=True)
+    bid = build_id()
+
+    def comp(src: Path) -> Path:
+        obj = SAN_DIR / (src.stem + ".o")
+        cmd = [HIPCC, *CFLAGS, *SAN_HOST_FLAGS, f'-DGQA_BUILD_ID="{bid}"', "-c", str(src), "-o", str(obj)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitized compile failed for {src.name}:\n{r.stderr}")
+        return obj
+
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    rt_dir = str(Path(asan_runtime()).parent)
+    link = [HOST_CXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libsan", "-o", str(SAN_LIB),
+            *map(str, objs), "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", f"-Wl,-rpath,{rt_dir}"]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SAN_LIB} (host ASan/UBSan)", file=sys.stderr)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "sanitized":
+        build_sanitized()
+    else:
+        build()
