@@ -41,11 +41,15 @@
 // the first product is used directly as the P operand of the second, and the
 // softmax denominators come from the same product against a block of ones.
 // Blocks are issued last-position-first so the longest causal rows start
-// earliest.
+// earliest, and renumbered so that all blocks of one (sequence, KV head) run
+// on one XCD: gfx950 deals workgroups to its 8 XCDs round-robin, and
+// without the renumbering every XCD's L2 holds the K/V of every pair in
+// flight (L2 hit rate 0.89 -> 0.93, 7% faster at S = 4096).
 #include <type_traits>
 
 #include "common.h"
 #include "gqa_internal.h"
+#include "xcd_order.h"
 
 namespace gqa {
 namespace {
@@ -74,18 +78,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   constexpr int TILE = kBN * D;             // elements per staged tile
   constexpr int COPIES = kBN * CPR / 64 / 4;  // 1 KB copies per wave per tile and tensor
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TILE];  // [stage][K|V]
+  // The two stages of the K and V tiles are four distinct LDS objects, so
+  // the compiler can tell that reads of one stage never touch the stage the
+  // asynchronous copies are filling and does not make them wait for those
+  // copies.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[TILE];
 
   // the 8 row tiles of a workgroup: hpw heads x (8 / hpw) blocks of 16
   // positions (hpw = 8 unless the group has fewer heads)
   const int hpw = 1 << hpw_log2;
   const int qspan = kBQ * (8 >> hpw_log2);  // query positions per workgroup
   const int nqb = (S + qspan - 1) / qspan;
-  const int qb = nqb - 1 - (int)blockIdx.x;
+  // Workgroup (query block, KV head and head chunk, sequence), numbered so
+  // that all query blocks of one (sequence, KV head) run on one XCD, whose L2
+  // then holds that pair's K/V prefix for all of them.
+  const int nbx = gridDim.x, nby = gridDim.y;
+  const int wid = (int)blockIdx.x + nbx * ((int)blockIdx.y + nby * (int)blockIdx.z);
+  const int lid = xcd_block_id(wid, nbx * nby * (int)gridDim.z);
+  const int bx = lid % nbx, byz = lid / nbx;
+  const int by = byz % nby;
+  const int qb = nqb - 1 - bx;
   const int q0 = qb * qspan;
-  const int k = blockIdx.y / head_chunks;
-  const int hc = blockIdx.y - k * head_chunks;
-  const int b = blockIdx.z;
+  const int k = by / head_chunks;
+  const int hc = by - k * head_chunks;
+  const int b = byz / nby;
   const int G = H / K;
 
   const int tid = threadIdx.x;
@@ -179,8 +198,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         }
       }
       // uniform base + 32-bit byte offset: the scalar-base addressing form
-      __builtin_amdgcn_global_load_lds(k0 + (uint32_t)(2 * ko), (__attribute__((address_space(3))) void*)&lds[ST][0][(wave_s + 4 * r) * 512], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(v0 + (uint32_t)(2 * vo), (__attribute__((address_space(3))) void*)&lds[ST][1][(wave_s + 4 * r) * 512], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(k0 + (uint32_t)(2 * ko), (__attribute__((address_space(3))) void*)((ST == 0 ? k_lds0 : k_lds1) + (wave_s + 4 * r) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(v0 + (uint32_t)(2 * vo), (__attribute__((address_space(3))) void*)((ST == 0 ? v_lds0 : v_lds1) + (wave_s + 4 * r) * 512), 16, 0, 0);
     }
   };
 
@@ -205,8 +224,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
   auto tile = [&](int kb0, auto stage_c) {
     constexpr int ST = decltype(stage_c)::value;
-    const uint16_t* kt = lds[ST][0];
-    const uint16_t* vt = lds[ST][1];
+    const uint16_t* kt = ST == 0 ? k_lds0 : k_lds1;
+    const uint16_t* vt = ST == 0 ? v_lds0 : v_lds1;
     // ---- S^T = K_tile . Q^T for both row tiles (raw q.k) ----
     f32x4 st[2][4];
 #pragma unroll
@@ -227,6 +246,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
           st[jj][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], qf[jj][s2], st[jj][mt], 0, 0, 0);
+    }
+    // The K operands of k-step s + 1 are read while the MFMAs of k-step s
+    // run (the compiler left on its own waits for each step's reads).
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int s2 = 0; s2 < KSTEPS; ++s2) {
+      if (s2 + 2 < KSTEPS) __builtin_amdgcn_sched_group_barrier(0x008, 8, 0), __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     if (kb0 + kBN > mask_from) {  // diagonal / last tile: drop keys >= the row's limit
 #pragma unroll
