@@ -57,6 +57,19 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return as_bf16x8(u32x4{a.x, a.y, b.x, b.y});
 }
 
+// The 16 values of a row of 16 lanes, lane j's value to every lane of the
+// row (v_mov_b32 DPP row_newbcast:j): lo[j] for j < 8, hi[j - 8] after.
+template <int J>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + J, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void row_bcast8(float x, float (&lo)[8], float (&hi)[8]) {
+  lo[0] = row_bcast<0>(x);  lo[1] = row_bcast<1>(x);  lo[2] = row_bcast<2>(x);  lo[3] = row_bcast<3>(x);
+  lo[4] = row_bcast<4>(x);  lo[5] = row_bcast<5>(x);  lo[6] = row_bcast<6>(x);  lo[7] = row_bcast<7>(x);
+  hi[0] = row_bcast<8>(x);  hi[1] = row_bcast<9>(x);  hi[2] = row_bcast<10>(x); hi[3] = row_bcast<11>(x);
+  hi[4] = row_bcast<12>(x); hi[5] = row_bcast<13>(x); hi[6] = row_bcast<14>(x); hi[7] = row_bcast<15>(x);
+}
+
 // Two resident waves per SIMD (at most 256 registers, no spills): the flat
 // split runs eight workgroups per CU (the in-flight K/V chunk of a wave is
 // half the bytes of the bf16 pass, so more waves than the bf16 pass's three
@@ -66,22 +79,21 @@ __device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // APPEND: the quantising append fused in.  The step's new rows k_new, v_new
 // (bf16) belong at position L_in = seq_lens[b] when the cache has room; it is
 // the last position of the sequence, so only the segment that ends the
-// sequence sees it.  Each of them quantises the rows by the cache rule (the
-// same fp32 operations as the standalone append, so the same codes and
-// scales) into its own slot of the workspace -- codes, and the 4-aligned
-// group of scales around the new position with the new scale in place --
-// and its loads take the slot instead of the cache for that position (a
-// pointer select, so the loop keeps its shape).  After the loop the first
-// head block copies the slot into the cache; no other workgroup of this
-// launch reads that cache row or scale.  Workgroup 0 records the lengths
-// after the append with the split (decode_flat.h) for the combine pass.
+// sequence reads that cache row.  Before its first load that segment's
+// workgroup quantises the rows by the cache rule (the same fp32 operations
+// as the standalone append, so the same codes and scales) straight into the
+// cache row and scale, and fences so that its own loads see them.  With
+// several head blocks each of their workgroups writes the same bytes before
+// reading them; no other workgroup of the launch reads that row.  Workgroup
+// 0 records the lengths after the append with the split (decode_flat.h) for
+// the combine pass.
 template <int D, bool APPEND>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_int8_kernel(
     const __bf16* __restrict__ q, int8_t* __restrict__ kc, int8_t* __restrict__ vc,
     float* __restrict__ ks, float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
     float* __restrict__ part_acc, float* __restrict__ part_ml, int B, int H, int K, int S_max,
     FlatArgs fa, int head_blocks, float scale_log2, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int32_t* __restrict__ meta, uint8_t* __restrict__ slots) {
+    const __bf16* __restrict__ v_new, int32_t* __restrict__ meta) {
   static_assert(D == 64 || D == 128, "head dimension");
   constexpr int KSTEPS = D / 32;
   constexpr int NTILES = D / 16;
@@ -133,12 +145,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   float* ksb = ks + head_row0;
   float* vsb = vs + head_row0;
 
-  // The new rows: slot = [K codes (D) | V codes (D) | K scales (4) | V scales (4)].
+  // The new rows of the fused append, quantised into the cache before any load.
   const bool has_new = APPEND && newpos >= t0 && newpos < t1;  // wave-uniform
-  const int s0_new = has_new ? (newpos & ~3) : -4;              // its scale group
-  int8_t* slot = reinterpret_cast<int8_t*>(slots) +
-                 (APPEND ? (((size_t)b * K + k) * head_blocks + hb) * (2 * D + 32) : 0);
-  float* slot_sc = reinterpret_cast<float*>(slot + 2 * D);
   if (has_new) {
     constexpr int E = D / 64;  // elements per lane
 #pragma unroll
@@ -154,15 +162,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
       for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
       const float inv = amax > 0.f ? int8_inv(amax) : 0.f;
+      int8_t* dst = (r == 0 ? kbase : vbase) + (size_t)newpos * D + E * lane;
 #pragma unroll
-      for (int e = 0; e < E; ++e) slot[r * D + E * lane + e] = amax > 0.f ? (int8_t)int8_code(x[e], inv) : 0;
-      if (lane < 4) {  // scale group: cached scales before the new position, 0 after it
-        const int pos = s0_new + lane;
-        const float* rs = r == 0 ? ksb : vsb;
-        slot_sc[4 * r + lane] = pos < newpos ? rs[pos] : pos == newpos ? (amax > 0.f ? int8_scale(amax) : 0.f) : 0.f;
-      }
+      for (int e = 0; e < E; ++e) dst[e] = amax > 0.f ? (int8_t)int8_code(x[e], inv) : 0;
+      if (lane == 0) (r == 0 ? ksb : vsb)[newpos] = amax > 0.f ? int8_scale(amax) : 0.f;
     }
-    __syncthreads();  // the slot's stores are visible to every lane of the workgroup
+    // this workgroup's loads below see the stores (workgroup scope: the same
+    // wave writes and reads; an agent-scope fence would write back and
+    // invalidate the L2 in every segment that ends a sequence)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 
   float m_run = -INFINITY;
@@ -177,31 +186,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   u32x4 ka[2][KWORDS];
   u32x4 vr[VLOADS];
-  f32x4 ksv[2], vsv[2];
+  // Scales: one dword per lane per chunk.  Row g of the wave (lanes 16 g ..
+  // 16 g + 15; its lanes' scores are positions 16 mt + 4 g + i, i < 4) fetches
+  // the 16 scales the row needs -- lane j: tensor j / 8 (K, then V), tile
+  // (j / 4) % 2, position i = j % 4 -- and each lane takes its own from the
+  // row by broadcasts (DPP row_newbcast).  A chunk's scale traffic is then
+  // 256 bytes per wave instead of sixteen copies of every 16-byte group.
+  float scl;
   // Rows past the partition are fetched from its last row instead (valid
   // memory, finite codes; their scores and weights are masked below), so no
   // load is predicated.
   const int last = t1 - 1;
+  const float* sc_src = n < 8 ? ksb : vsb;
+  const int sc_off = 16 * ((n >> 2) & 1) + 4 * g + (n & 3);
   auto load_k = [&](int c0) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int tok = min(c0 + 16 * mt + n, last);
-      const int8_t* krow = (APPEND && tok == newpos ? slot : kbase + (size_t)tok * D) + KSEG * g;
+      const int8_t* krow = kbase + (size_t)tok * D + KSEG * g;
 #pragma unroll
       for (int w = 0; w < KWORDS; ++w) ka[mt][w] = ld16_stream(krow + 16 * w);
-      // scales of the positions this lane's scores belong to: 16mt + 4g + i
-      const int s0 = min(c0 + 16 * mt + 4 * g, last & ~3);
-      const bool sc_new = APPEND && s0 == s0_new;
-      ksv[mt] = *reinterpret_cast<const f32x4*>(sc_new ? slot_sc : ksb + s0);
-      vsv[mt] = *reinterpret_cast<const f32x4*>(sc_new ? slot_sc + 4 : vsb + s0);
     }
+    scl = sc_src[min(c0 + sc_off, last)];
   };
   auto load_v = [&](int c0) {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int tok = min(c0 + i * ROWS_PER_LOAD + vrow, last);
-      const int8_t* vrow_p = APPEND && tok == newpos ? slot + D : vbase + (size_t)tok * D;
-      vr[i] = ld16_stream(vrow_p + vcol);
+      vr[i] = ld16_stream(vbase + (size_t)tok * D + vcol);
     }
   };
   // A head's running max is raised (and its accumulators rescaled) only
@@ -229,13 +241,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
       }
     }
     float sk[8], sv[8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sk[4 * mt + i] = ksv[mt][i];
-        sv[4 * mt + i] = vsv[mt][i];
-      }
+    row_bcast8(scl, sk, sv);
     if (more) load_k(c0 + kChunk);
 
     // ---- online softmax for head n over positions {16mt + 4g + i} ----
@@ -302,15 +308,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  if (APPEND && has_new && hb == 0) {  // the appended rows join the cache
-    if (lane < 2 * (D / 16)) {
-      const int r = lane / (D / 16), w = lane % (D / 16);
-      *reinterpret_cast<u32x4*>((r == 0 ? kbase : vbase) + (size_t)newpos * D + 16 * w) =
-          ld16(slot + r * D + 16 * w);
-    }
-    if (lane < 2) (lane == 0 ? ksb : vsb)[newpos] = slot_sc[4 * lane + (newpos - s0_new)];
-  }
-
   const size_t row0 = (size_t)slot_id * G + (size_t)hb * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -348,7 +345,7 @@ hipError_t launch_decode_split_int8(const void* q, void* k_codes, void* v_codes,
 #define GQA_I8(DD, AP)                                                                          \
   hipLaunchKernelGGL((decode_split_int8_kernel<DD, AP>), grid, dim3(64), 0, stream, qp, kp, vp,  \
                      k_scales, v_scales, seq_lens, ws.part_acc, ws.part_ml, B, H, K, S_max,      \
-                     plan.fa, plan.head_blocks, scale_log2, kn, vn, ws.meta, ws.new_rows)
+                     plan.fa, plan.head_blocks, scale_log2, kn, vn, ws.meta)
   if (d == 128) {
     if (k_new) GQA_I8(128, true); else GQA_I8(128, false);
   } else {

@@ -64,8 +64,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static size_t workspace_bytes_for(const DecodePlan& p, int B, int K, int d) {
   const size_t rows = (size_t)p.slots * p.G;
   return align256(rows * d * sizeof(float)) + align256(rows * 2 * sizeof(float)) +
-         align256((size_t)(2 * B + 1) * sizeof(int32_t)) +
-         align256((size_t)B * K * p.head_blocks * (2 * d + 32));
+         align256((size_t)(2 * B + 1) * sizeof(int32_t));
 }
 
 size_t decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d, int r_max) {
@@ -82,8 +81,6 @@ DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, i
   w.part_ml = reinterpret_cast<float*>(c);
   c += align256(rows * 2 * sizeof(float));
   w.meta = reinterpret_cast<int32_t*>(c);
-  c += align256((size_t)(2 * B + 1) * sizeof(int32_t));
-  w.new_rows = reinterpret_cast<uint8_t*>(c);
   return w;
 }
 

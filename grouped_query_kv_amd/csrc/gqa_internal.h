@@ -38,15 +38,10 @@ size_t decode_workspace_bytes(int B, int H, int K, int max_seq_len, int d, int r
 //   meta     [2B + 1]           int32: the lengths attended over, the flat
 //                               starts of the sequences and the total (the
 //                               split, recorded by the partition pass)
-//   new_rows [B*K*head_blocks][2d + 32]  bytes: per (sequence, KV head, head
-//                               block) slot of a fused int8 append in the
-//                               one-wave pass (codes of the new K and V rows
-//                               and their 4-aligned scale groups)
 struct DecodeWorkspace {
   float* part_acc;
   float* part_ml;
   int32_t* meta;
-  uint8_t* new_rows;
 };
 // (each region 256-byte aligned; sized for the plan's slots)
 DecodeWorkspace carve_decode_workspace(void* base, const DecodePlan& p, int B, int K, int d);
