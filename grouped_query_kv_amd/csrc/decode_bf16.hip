@@ -227,21 +227,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     // l_run holds this lane's share of the denominator (its positions); the
     // shares are summed over the lane groups once, after the loop.
     constexpr float kLazy = 8.f;
-    float sv[8];
+    // Raw scores; positions past the segment (only in its last chunk) get
+    // -inf.  scale > 0, so the largest scaled score is the largest raw score
+    // times the scale, and each weight is one fma and one exponential.
+    if (c0 + kChunk > t1) {  // uniform
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c0 + 16 * mt + 4 * g + i >= t1) st[mt][i] = -INFINITY;
+    }
     float lmax = -INFINITY;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = c0 + 16 * mt + 4 * g + i;
-        const float x = tok < t1 ? st[mt][i] * scale_log2 : -INFINITY;
-        sv[4 * mt + i] = x;
-        lmax = fmaxf(lmax, x);
-      }
-    if (__any(lmax > m_run + kLazy)) {  // always on the first chunk (m_run = -inf)
+      for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, st[mt][i]);
+    if (__any(lmax * scale_log2 > m_run + kLazy)) {  // always on the first chunk (m_run = -inf)
       float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run, cmax);  // finite: the chunk has >= 1 position
+      const float m_new = fmaxf(m_run, cmax * scale_log2);  // finite: the chunk has >= 1 position
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -253,11 +257,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
         for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
       }
     }
+    const float mneg = -m_run;
     uint32_t pw[4];
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
-      const float e0 = fast_exp2(sv[j] - m_run);
-      const float e1 = fast_exp2(sv[j + 1] - m_run);
+      const float e0 = fast_exp2(fmaf(st[j >> 2][j & 3], scale_log2, mneg));
+      const float e1 = fast_exp2(fmaf(st[(j + 1) >> 2][(j + 1) & 3], scale_log2, mneg));
       l_run += e0 + e1;
       pw[j / 2] = pack_bf16x2(e0, e1);
     }

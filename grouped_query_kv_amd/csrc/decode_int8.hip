@@ -250,14 +250,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = c0 + 16 * mt + 4 * g + i;
-        const bool ok = tok < t1;
-        const float xv = ok ? st[mt][i] * (sk[4 * mt + i] * scale_log2) : -INFINITY;
-        x[4 * mt + i] = xv;
-        sv[4 * mt + i] = ok ? sv[4 * mt + i] : 0.f;  // rows past the end never reach the sum
-        lmax = fmaxf(lmax, xv);
-      }
+      for (int i = 0; i < 4; ++i) x[4 * mt + i] = st[mt][i] * (sk[4 * mt + i] * scale_log2);
+    if (c0 + kChunk > t1) {  // uniform: positions past the segment, only in its last chunk
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + 16 * (j >> 2) + 4 * g + (j & 3) >= t1) {
+          x[j] = -INFINITY;
+          sv[j] = 0.f;  // rows past the end never reach the sum
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lmax = fmaxf(lmax, x[j]);
     if (__any(lmax > m_run + kLazy)) {
       float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));

@@ -64,8 +64,13 @@ __device__ __forceinline__ int v_swizzle(int r) {
 
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (((vm >> 4) & 3) << 14); }
 
+// Four workgroups of W waves per CU: from W = 5 on, the d = 64 pass must fit six
+// waves per SIMD (at most 80 registers) so that four workgroups stay resident.
+template <int D, int W>
+constexpr int wide_min_waves() { return D == 64 && W >= 5 ? 6 : 1; }
+
 template <int D, bool APPEND, bool PAGED, int W, int SUB, int NS>
-__global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_min_waves<D, W>()))) void decode_wide_bf16_kernel(
     const __bf16* __restrict__ q, __bf16* __restrict__ kc, __bf16* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int B, int H, int K, int S_max, FlatArgs fa,
@@ -225,20 +230,25 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
         }
       }
       // ---- online softmax for head n over positions {16mt + 4g + i} ----
-      float sv[8];
+      // Raw scores; positions past the segment (only in its last chunk) get
+      // -inf.  scale > 0, so the largest scaled score is the largest raw score
+      // times the scale, and each weight is one fma and one exponential.
+      if (c0 + kChunk > t1) {  // uniform
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (c0 + 16 * mt + 4 * g + i >= t1) st[mt][i] = -INFINITY;
+      }
       float lmax = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = c0 + 16 * mt + 4 * g + i < t1 ? st[mt][i] * scale_log2 : -INFINITY;
-          sv[4 * mt + i] = x;
-          lmax = fmaxf(lmax, x);
-        }
-      if (__any(lmax > m_run + kLazy)) {
+        for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, st[mt][i]);
+      if (__any(lmax * scale_log2 > m_run + kLazy)) {
         float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float m_new = fmaxf(m_run, cmax);
+        const float m_new = fmaxf(m_run, cmax * scale_log2);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
@@ -249,11 +259,12 @@ __global__ __launch_bounds__(64 * W) void decode_wide_bf16_kernel(
           for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
         }
       }
+      const float mneg = -m_run;  // finite: the segment's first chunk set it
       uint32_t pw[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float e0 = fast_exp2(sv[j] - m_run);
-        const float e1 = fast_exp2(sv[j + 1] - m_run);
+        const float e0 = fast_exp2(fmaf(st[j >> 2][j & 3], scale_log2, mneg));
+        const float e1 = fast_exp2(fmaf(st[(j + 1) >> 2][(j + 1) & 3], scale_log2, mneg));
         l_run += e0 + e1;
         pw[j / 2] = pack_bf16x2(e0, e1);
       }
