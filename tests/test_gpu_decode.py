@@ -50,6 +50,10 @@ CASES = [
     (2, 16, 4, 64, [31, 32], "bf16"),
     (2, 56, 8, 128, [300, 5], "bf16"),         # G = 7
     (1, 71, 1, 64, [257], "bf16"),             # G = 71: five head blocks
+    (2, 64, 2, 64, [300, 41], "bf16"),         # d = 64, G = 32: two head blocks in one wave
+    (2, 48, 1, 64, [777, 31], "bf16"),         # d = 64, G = 48: three head blocks in one wave
+    (1, 64, 1, 64, [1025], "bf16"),            # d = 64, G = 64: four head blocks in one wave
+    (3, 160, 2, 64, [129, 0, 2000], "bf16"),   # d = 64, G = 80: five full head blocks, an empty sequence
     (2, 8, 8, 128, [2, 97], "bf16"),           # K = H (MHA)
     (2, 32, 1, 128, [129, 64], "bf16"),        # K = 1 (MQA), G = 32
     (2, 48, 1, 128, [777, 31], "bf16"),        # G = 48: three head blocks in a four-wave group
