@@ -115,6 +115,23 @@ def test_int8_decode_shapes(B, H, K, d, lens):
             assert torch.count_nonzero(out[b]).item() == 0
 
 
+@pytest.mark.parametrize("qmul", [2.0 ** 17, 2.0 ** -20])
+def test_int8_decode_query_range(qmul):
+    """Queries 2^17 times and 2^-20 times the workload's: scores spread so far
+    that the softmax is one-hot, and so little that the weights are nearly
+    uniform."""
+    B, H, K, d, lens = 2, 32, 8, 128, [257, 40]
+    note(f"int8 decode query range x{qmul}")
+    inp, kc, vc, ks, vs = _int8_case(B, H, K, d, lens, seed=83)
+    inp["q"] = (inp["q"].float() * qmul).to(torch.bfloat16)
+    out = _run(inp, kc, vc, ks, vs, max(lens))
+    ref = decode_int8_ref(f64(inp["q"]), kc.numpy(), vc.numpy(), ks.numpy(), vs.numpy(),
+                          inp["seq_lens"].numpy(), scale_of(d))
+    r = report(f"int8 q x{qmul}", f64(out), ref)
+    assert r["finite"] and r["max_abs"] <= TOL["bf16"]
+    assert r["max_abs"] <= bf16_bound(ref, _vmax(vc, vs, lens))
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_int8_out_dtype_and_guards(out_dtype):
     B, H, K, d, lens = 2, 32, 8, 128, [500, 77]
