@@ -329,6 +329,7 @@ def bench_decode(args, w, sub=False):
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("decode_split_int8_kernel" if int8 else
+                                                 "decode_split_f32_kernel" if w.dtype == "f32" else
                                                  "decode_wide_bf16_kernel" if wide else
                                                  "decode_split_bf16_kernel" + ("_paged" if paged else ""), w.name),
                      "avg_kernel_us": round(kern_avg_ms * 1e3, 3), "timed_launches": len(sampled),

@@ -65,6 +65,10 @@ WORKLOADS = {
         "decode_mqa_71h", "decode", B=32, H=71, K=1, d=64, dtype="bf16", L=32768,
         append=True, note="multi-query layer: 71 query heads sharing one KV head (the Falcon-7B head "
                           "layout), d=64, 32768 cached tokens + 1 appended"),
+    "decode_f32_mqa_71h": Workload(
+        "decode_f32_mqa_71h", "decode", B=8, H=71, K=1, d=128, dtype="f32", L=16384,
+        note="fp32 multi-query layer: 71 query heads sharing one KV head, d=128, 16384 cached "
+             "tokens (the fp32 pass reads each KV byte once for all five head blocks)"),
     "decode_paged_llama3_8b": Workload(
         "decode_paged_llama3_8b", "decode", B=16, H=32, K=8, d=128, dtype="bf16", L=8192,
         append=True, note="decode_llama3_8b over a paged cache: 16-token blocks in shuffled order",
