@@ -30,6 +30,12 @@
 namespace gqa {
 namespace {
 
+// 16-byte streaming load of four floats (non-temporal: read once per step)
+__device__ __forceinline__ float4 ld_f4_stream(const float* p) {
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return float4{v[0], v[1], v[2], v[3]};
+}
+
 constexpr int kThreads = 256;
 constexpr int kHB = 16;       // heads per block
 constexpr int kMaxHB = 8;     // head blocks per workgroup
@@ -123,8 +129,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
         const bool ok = row < n_tok;
         const float* kr = APPEND && tok == newpos ? knew_row : kbase + (size_t)tok * D;
         const float* vr = APPEND && tok == newpos ? vnew_row : vbase + (size_t)tok * D;
-        kv4[r] = ok ? reinterpret_cast<const float4*>(kr)[c4] : float4{0.f, 0.f, 0.f, 0.f};
-        vv4[r] = ok ? reinterpret_cast<const float4*>(vr)[c4] : float4{0.f, 0.f, 0.f, 0.f};
+        // streaming loads: every cache byte is read once per step
+        kv4[r] = ok ? ld_f4_stream(kr + 4 * c4) : float4{0.f, 0.f, 0.f, 0.f};
+        vv4[r] = ok ? ld_f4_stream(vr + 4 * c4) : float4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int r = 0; r < LOADS; ++r) {
