@@ -190,9 +190,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_min
   // Copy slot c of this wave is instruction i = wave + c W of the block (the
   // surplus slots, i >= NINST, repeat instruction i - NINST into the sink):
   // lane l fills LDS chunk 64 i + l = row r, physical chunk l % LPR, with the
-  // logical chunk that the swizzle puts there.  Rows past the partition end
-  // are fetched from its last row (valid memory; masked).
-  // (byte offsets of the lane's chunk inside its row)
+  // logical chunk that the swizzle puts there (ck, cv: that chunk's byte
+  // offset inside its K and V row).  Rows past the partition end are fetched
+  // from its last row (valid memory; masked).
   int crow[NI];
   uint32_t ck[NI], cv[NI];
 #pragma unroll
