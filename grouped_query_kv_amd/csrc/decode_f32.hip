@@ -1,77 +1,86 @@
-// Decode partition pass for fp32 caches, on the vector ALUs.
+// Decode partition pass for fp32 caches, on the gfx950 matrix cores in fp32.
 //
-// Same contract as the bf16 pass (see decode_bf16.hip): for partition
-// [t0, t1) of sequence b, KV head k and a block of up to 16 query heads of
-// that group it produces the base-2 online-softmax state (m, l, acc) that the
-// combine pass merges.  fp32 keeps full single precision end to end (the
-// matrix cores would round operands), which is what fp32 callers ask for.
+// Same contract as the bf16 passes (decode_bf16.hip, decode_wide_bf16.hip):
+// for partition [t0, t1) of sequence b and KV head k it produces, for every
+// query head of the group, the base-2 online-softmax state (m, l, acc) that
+// the combine pass merges.  Everything stays in single precision:
+// v_mfma_f32_16x16x4_f32 multiplies fp32 operands and accumulates in fp32
+// (on this GPU its error over a 128-term dot product equals that of a chain
+// of fp32 fma instructions), and the softmax weights are not rounded.
 //
-// One 256-thread workgroup per flat range (decode_flat.h) and up to eight
-// 16-head blocks of the group; positions are processed in chunks of CF (64
-// for d = 64, 32 for d = 128):
-//   0. the chunk's K and V rows are copied into LDS with every load of the
-//      chunk in flight at once (one memory round trip per chunk);
-//   then for each head block of the workgroup (the chunk stays in LDS):
-//   1. scores: thread (t, hs) dots position t's K row with its heads
-//      (query rows broadcast from LDS);
-//   2. softmax: wave w updates (m, l) of heads w, w+4, w+8, w+12 with
-//      wavefront max/sum reductions, leaving probabilities in LDS;
-//   3. values: thread (dim c, head slice) accumulates p * V[t][c] for its
-//      heads.
-// The group's K and V rows are read from memory once per workgroup and
-// serve every head of the group (pinghaoyang.com.cn "GQA 完全拆解", section
-// 工程实现: the group's KV block is loaded once for all its query heads);
-// only groups of more than 128 heads take several workgroups per range.
-// With more than one head block the block's query rows are re-staged from
-// the (cache-resident) queries for every chunk.
+// Structure (that of the multi-wave bf16 pass): one workgroup of W waves per
+// flat range (decode_flat.h), one wave per 16-head block of the group (up to
+// 8 blocks; larger groups take several workgroups per range, each re-reading
+// the range), so the K and V rows of the range are read from memory once for
+// all heads of the group (pinghaoyang.com.cn "GQA 完全拆解", section 工程实现:
+// the group's KV block is loaded once and reused by its query heads).  Rows
+// are staged in chunks of 32 positions through a two-buffer LDS ring filled
+// by direct global-to-LDS copies (global_load_lds_dwordx4, non-temporal);
+// per chunk and wave:
+//   S^T[32 x 16] = K_chunk . Q^T   (two 16-position tiles, D/4 products each)
+//   lazy base-2 online softmax of head n over the chunk (fp32 weights)
+//   O[16 x D]   += P . V_chunk     (D/16 tiles, 8 products each)
+//
+// Operand layouts of v_mfma_f32_16x16x4_f32 (wave64, lane l, n = l % 16,
+// g = l / 16): A row m = n holds one k-value chosen by g; B column n holds
+// the same k-value; C/D lane l holds D[4g + i][n], i = 0..3.  As in the bf16
+// passes the contraction index is relabelled on both sides alike:
+//   Q.K: product (j, c) of a tile gives lane (n, g) head dimension
+//        16j + 4g + c, so one 16-byte LDS read of a K row feeds four products
+//        and the queries sit in registers as matching float4s;
+//   P.V: the scores come out as lane (n = head, g) holding positions
+//        16mt + 4g + i, which become that lane's contraction slots (product
+//        (mt, i)), so P needs no data movement; V[16mt + 4g + i][16t + n]
+//        is one 4-byte LDS read per product.
+// LDS rows are whole rows of D floats, 16-byte chunks XOR-swizzled by row:
+// K: chunk ^ (row % 16) puts the 16 rows of a K read in 16 distinct bank
+// groups; V: chunk ^ 4 ((row / 4) % 4) puts the four rows of a V read (rows
+// 4g + i for the four lane groups) in four distinct 64-byte bank ranges.
 #include "common.h"
 #include "gqa_internal.h"
 
 namespace gqa {
 namespace {
 
-// 16-byte streaming load of four floats (non-temporal: read once per step)
-__device__ __forceinline__ float4 ld_f4_stream(const float* p) {
-  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-  return float4{v[0], v[1], v[2], v[3]};
-}
+constexpr int kChunk = 32;   // positions per chunk
+constexpr int kHB = 16;      // heads per block (one wave)
+constexpr int kMaxW = 8;     // head blocks (waves) per workgroup
+// cache policy of the copies: non-temporal (each cache byte is read once per
+// step); the nt bit of the instruction's cache-policy field
+constexpr int kStreamAux = 2;
 
-constexpr int kThreads = 256;
-constexpr int kHB = 16;       // heads per block
-constexpr int kMaxHB = 8;     // head blocks per workgroup
+// s_waitcnt immediate (gfx9 encoding): vector-memory count 0, LDS count 0
+constexpr int kWaitAll = 0x0070;
 
-// APPEND: fused cache append, as in decode_bf16.hip.
-template <int D, bool APPEND>
-__global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
+template <int D, bool APPEND, int W>
+__global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     const float* __restrict__ q, float* __restrict__ kc, float* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
     float* __restrict__ part_ml, int B, int H, int K, int S_max, FlatArgs fa, int wg_per_range,
     float scale_log2, const float* __restrict__ k_new, const float* __restrict__ v_new,
     int32_t* __restrict__ meta) {
-  constexpr int CF = D == 64 ? 64 : 32;                  // positions per chunk
-  constexpr int HEADS_PER_THREAD = kHB * D / kThreads;   // phase 3: 8 (D=128) or 4 (D=64)
-  constexpr int HPT1 = kHB * CF / kThreads;              // phase 1: 2 (D=128) or 4 (D=64)
-  constexpr int KROW = D + 4;  // padded K row: a 16-byte shift per row spreads the
-                               // phase-1 reads of consecutive rows over the banks
-  constexpr int ROW4 = D / 4;  // float4 per row
-  constexpr int LOADS = CF * ROW4 / kThreads;            // float4 per thread per tensor
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int CPR = D / 4;                 // 16-byte chunks per row
+  constexpr int TILE = kChunk * D;           // floats per staged tensor
+  constexpr int NINST = TILE / 256;          // 1 KB copies per tensor and chunk
+  constexpr int NI = (NINST + W - 1) / W;    // copies per wave per tensor and chunk
+  constexpr bool SURPLUS = NINST % W != 0;   // some waves have one copy too many
+  constexpr int DJ = D / 16;                 // float4 query pieces per lane
+  constexpr int NTILES = D / 16;             // 16-dim output tiles
 
-  __shared__ __attribute__((aligned(16))) float qs[kHB][D];
-  __shared__ __attribute__((aligned(16))) float ks[CF][KROW];
-  __shared__ __attribute__((aligned(16))) float vs[CF][D];
-  __shared__ __attribute__((aligned(16))) float ps[kHB][CF];
-  __shared__ float alpha_s[kHB];
-  __shared__ float m_s[kMaxHB][kHB];
-  __shared__ float l_s[kMaxHB][kHB];
+  __shared__ __attribute__((aligned(16))) float lds[2][2][TILE];  // [buffer][K|V]
+  // target of the surplus copies (they repeat a real copy; never read)
+  __shared__ __attribute__((aligned(16))) float sink[SURPLUS ? 256 : 4];
 
   const int w = blockIdx.x / wg_per_range;
   const int hg = blockIdx.x - w * wg_per_range;  // this workgroup's group of head blocks
   const int G = H / K;
-  const int hb0 = hg * kMaxHB;
-  const int nhb = min(kMaxHB, (G + kHB - 1) / kHB - hb0);  // head blocks of this workgroup
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int hb = hg * kMaxW + wave;              // this wave's block of 16 heads
+  const bool has_heads = hb * kHB < G;           // wave-uniform
 
   // lengths clamped into [0, S_max], so no length can make a load leave the cache
   auto len_in = [&](int bb) -> int { return min(max(seq_lens[bb], 0), S_max); };
@@ -87,186 +96,195 @@ __global__ __launch_bounds__(kThreads) void decode_split_f32_kernel(
   flat_for_each_segment(w, B, K, total, R, len_of,
                         [&](int b, int k, int t0, int t1, int L, int slot) {
   const int newpos = APPEND && L > len_in(b) ? L - 1 : -1;  // the appended row, if any
-  const size_t grow0 = (size_t)b * H + (size_t)k * G;         // the group's first query row
-
-  // query rows of head block hb (zeros past the group)
-  auto stage_q = [&](int hb) {
-    const int nh = min(kHB, G - hb * kHB);
-    for (int i = tid; i < kHB * D; i += kThreads) {
-      const int h = i / D, c = i - h * D;
-      qs[h][c] = h < nh ? q[(grow0 + hb * kHB + h) * D + c] : 0.f;
-    }
-  };
-  if (nhb == 1) stage_q(hb0);
-  if (tid < kMaxHB * kHB) {
-    m_s[tid / kHB][tid % kHB] = -INFINITY;
-    l_s[tid / kHB][tid % kHB] = 0.f;
-  }
+  const int last = t1 - 1;
   const size_t head_base = ((size_t)b * K + k) * (size_t)S_max * D;
   float* kbase = kc + head_base;
   float* vbase = vc + head_base;
-  const float* knew_row = APPEND ? k_new + ((size_t)b * K + k) * D : nullptr;
-  const float* vnew_row = APPEND ? v_new + ((size_t)b * K + k) * D : nullptr;
 
-  const int c_own = tid % D;            // value dimension owned in phase 3
-  const int slice = tid / D;            // head slice owned in phase 3
-  float acc[kMaxHB][HEADS_PER_THREAD];
-#pragma unroll
-  for (int u = 0; u < kMaxHB; ++u)
-#pragma unroll
-    for (int j = 0; j < HEADS_PER_THREAD; ++j) acc[u][j] = 0.f;
-
-  for (int c0 = t0; c0 < t1; c0 += CF) {
-    const int n_tok = min(CF, t1 - c0);
-    // 0. stage the chunk's K and V rows (rows past the segment: zeros)
-    {
-      float4 kv4[LOADS], vv4[LOADS];
-#pragma unroll
-      for (int r = 0; r < LOADS; ++r) {
-        const int i = tid + r * kThreads;
-        const int row = i / ROW4, c4 = i - row * ROW4;
-        const int tok = c0 + row;
-        const bool ok = row < n_tok;
-        const float* kr = APPEND && tok == newpos ? knew_row : kbase + (size_t)tok * D;
-        const float* vr = APPEND && tok == newpos ? vnew_row : vbase + (size_t)tok * D;
-        // streaming loads: every cache byte is read once per step
-        kv4[r] = ok ? ld_f4_stream(kr + 4 * c4) : float4{0.f, 0.f, 0.f, 0.f};
-        vv4[r] = ok ? ld_f4_stream(vr + 4 * c4) : float4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int r = 0; r < LOADS; ++r) {
-        const int i = tid + r * kThreads;
-        const int row = i / ROW4, c4 = i - row * ROW4;
-        *reinterpret_cast<float4*>(&ks[row][4 * c4]) = kv4[r];
-        *reinterpret_cast<float4*>(&vs[row][4 * c4]) = vv4[r];
-      }
+  // The fused append: the workgroup(s) whose partition holds the appended
+  // position write the new rows into the cache before anything is copied
+  // (every workgroup of the range writes the same values), so the copies
+  // read the cache alone; workgroup-scope release and acquire around the
+  // barrier order wave 0's stores before the other waves' copies.
+  if (APPEND && newpos >= t0 && newpos < t1) {  // uniform
+    if (wave == 0 && lane < CPR) {
+      const float* kn = k_new + ((size_t)b * K + k) * D;
+      const float* vn = v_new + ((size_t)b * K + k) * D;
+      *reinterpret_cast<f32x4*>(kbase + (size_t)newpos * D + 4 * lane) =
+          *reinterpret_cast<const f32x4*>(kn + 4 * lane);
+      *reinterpret_cast<f32x4*>(vbase + (size_t)newpos * D + 4 * lane) =
+          *reinterpret_cast<const f32x4*>(vn + 4 * lane);
     }
-#pragma unroll
-    for (int u = 0; u < kMaxHB; ++u) {
-      if (u >= nhb) break;  // uniform
-      if (nhb > 1) {
-        __syncthreads();  // the previous head block is done with qs and ps
-        stage_q(hb0 + u);
-      }
-      __syncthreads();
-      // 1. scores
-      {
-        const int t = tid % CF;
-        const int hs = tid / CF;  // heads hs, hs + 256/CF, ...
-        float s[HPT1];
-#pragma unroll
-        for (int r = 0; r < HPT1; ++r) s[r] = 0.f;
-#pragma unroll 8
-        for (int c4 = 0; c4 < ROW4; ++c4) {
-          const float4 kv = *reinterpret_cast<const float4*>(&ks[t][4 * c4]);
-#pragma unroll
-          for (int r = 0; r < HPT1; ++r) {
-            const float* qq = &qs[hs + (kThreads / CF) * r][4 * c4];
-            s[r] = fmaf(kv.x, qq[0], s[r]);
-            s[r] = fmaf(kv.y, qq[1], s[r]);
-            s[r] = fmaf(kv.z, qq[2], s[r]);
-            s[r] = fmaf(kv.w, qq[3], s[r]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < HPT1; ++r)
-          ps[hs + (kThreads / CF) * r][t] = t < n_tok ? s[r] * scale_log2 : -INFINITY;
-      }
-      __syncthreads();
-      // 2. online softmax, wave w owns heads w, w+4, w+8, w+12 (lane = position);
-      // the four heads' reductions are interleaved (independent shuffle chains)
-      {
-        float x[4], mx[4], mnew[4], e[4], sum[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = lane < CF ? ps[wave + 4 * r][lane] : -INFINITY;
-          mx[r] = x[r];
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], off));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          mnew[r] = fmaxf(m_s[u][wave + 4 * r], mx[r]);
-          e[r] = fast_exp2(x[r] - mnew[r]);
-          sum[r] = e[r];
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sum[r] += __shfl_xor(sum[r], off);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (lane < CF) ps[wave + 4 * r][lane] = e[r];
-        if (lane == 0) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int h = wave + 4 * r;
-            const float a = fast_exp2(m_s[u][h] - mnew[r]);
-            alpha_s[h] = a;
-            l_s[u][h] = l_s[u][h] * a + sum[r];
-            m_s[u][h] = mnew[r];
-          }
-        }
-      }
-      __syncthreads();
-      // 3. values
-#pragma unroll
-      for (int j = 0; j < HEADS_PER_THREAD; ++j) acc[u][j] *= alpha_s[slice * HEADS_PER_THREAD + j];
-      // eight positions per step, their LDS reads issued together
-      int t = 0;
-      for (; t + 8 <= n_tok; t += 8) {
-        float v[8];
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) v[e8] = vs[t + e8][c_own];
-#pragma unroll
-        for (int j = 0; j < HEADS_PER_THREAD; ++j) {
-          const float4 pa = *reinterpret_cast<const float4*>(&ps[slice * HEADS_PER_THREAD + j][t]);
-          const float4 pb = *reinterpret_cast<const float4*>(&ps[slice * HEADS_PER_THREAD + j][t + 4]);
-          acc[u][j] = fmaf(pa.x, v[0], acc[u][j]);
-          acc[u][j] = fmaf(pa.y, v[1], acc[u][j]);
-          acc[u][j] = fmaf(pa.z, v[2], acc[u][j]);
-          acc[u][j] = fmaf(pa.w, v[3], acc[u][j]);
-          acc[u][j] = fmaf(pb.x, v[4], acc[u][j]);
-          acc[u][j] = fmaf(pb.y, v[5], acc[u][j]);
-          acc[u][j] = fmaf(pb.z, v[6], acc[u][j]);
-          acc[u][j] = fmaf(pb.w, v[7], acc[u][j]);
-        }
-      }
-      for (; t < n_tok; ++t) {
-        const float v = vs[t][c_own];
-#pragma unroll
-        for (int j = 0; j < HEADS_PER_THREAD; ++j)
-          acc[u][j] = fmaf(ps[slice * HEADS_PER_THREAD + j][t], v, acc[u][j]);
-      }
-    }
-    __syncthreads();  // every thread is done with ks, vs, ps before the next chunk
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 
-  if (APPEND && hg == 0 && newpos >= t0 && newpos < t1 && tid < D) {
-    // the appended rows join the cache
-    kbase[(size_t)newpos * D + tid] = knew_row[tid];
-    vbase[(size_t)newpos * D + tid] = vnew_row[tid];
-  }
+  // queries of head hb*16 + n as float4 pieces 16j + 4g .. +3 (zeros past the group)
+  const int hq = hb * kHB + n;
+  const bool hq_ok = hq < G;
+  f32x4 qf[DJ];
+  {
+    const float* qrow = q + ((size_t)b * H + (size_t)k * G + (hq_ok ? hq : 0)) * D;
 #pragma unroll
-  for (int u = 0; u < kMaxHB; ++u) {
-    if (u >= nhb) break;
-    const int hb = hb0 + u;
-    const int nh = min(kHB, G - hb * kHB);
+    for (int j = 0; j < DJ; ++j)
+      qf[j] = hq_ok ? *reinterpret_cast<const f32x4*>(qrow + 16 * j + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Copy slot c of this wave is instruction i = wave + c W of the chunk (the
+  // surplus slots, i >= NINST, repeat instruction i - NINST into the sink):
+  // lane l fills LDS chunk 64 i + l = row r, physical chunk l % CPR, with the
+  // logical chunk the swizzle puts there (ck, cv: its byte offset in the row).
+  // Rows past the partition end are fetched from its last row (valid memory;
+  // their scores are masked).
+  int crow[NI];
+  uint32_t ck[NI], cv[NI];
+#pragma unroll
+  for (int c = 0; c < NI; ++c) {
+    const int i = (wave + c * W) % NINST;
+    const int r = (64 * i + lane) / CPR, ph = lane % CPR;
+    crow[c] = r;
+    ck[c] = 16 * (ph ^ (r & 15));
+    cv[c] = 16 * (ph ^ (((r >> 2) & 3) << 2));
+  }
+  auto copy_chunk = [&](int c0, int buf) {
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      const int i = wave + c * W;  // uniform
+      // the chunk's first row (uniform) plus a small per-lane offset
+      const uint32_t ro = (uint32_t)min(crow[c], last - c0) * (uint32_t)(4 * D);
+      const char* kp = reinterpret_cast<const char*>(kbase + (size_t)c0 * D) + (ro + ck[c]);
+      const char* vp = reinterpret_cast<const char*>(vbase + (size_t)c0 * D) + (ro + cv[c]);
+      float* kd = i < NINST ? &lds[buf][0][i * 256] : sink;
+      float* vd = i < NINST ? &lds[buf][1][i * 256] : sink;
+      __builtin_amdgcn_global_load_lds(kp, (__attribute__((address_space(3))) void*)kd, 16, 0, kStreamAux);
+      __builtin_amdgcn_global_load_lds(vp, (__attribute__((address_space(3))) void*)vd, 16, 0, kStreamAux);
+    }
+  };
+
+  // loop-invariant LDS offsets (floats): K piece j of tile mt is row 16mt + n,
+  // logical chunk 4j + g; V read of product (mt, i), tile t is row
+  // 16mt + 4g + i, logical chunk 4t + n/4, float n % 4
+  int ka_off[DJ];
+#pragma unroll
+  for (int j = 0; j < DJ; ++j) ka_off[j] = n * D + 4 * ((4 * j + g) ^ n);
+  const int vswz = g << 2;  // ((row / 4) % 4) << 2 for rows 16mt + 4g + i
+  int vb_off[NTILES];
+#pragma unroll
+  for (int t = 0; t < NTILES; ++t) vb_off[t] = 4 * g * D + 4 * ((4 * t + (n >> 2)) ^ vswz) + (n & 3);
+
+  float m_run = -INFINITY;  // running max of head n (replicated over g)
+  float l_run = 0.f;        // this lane's share of the running sum of head n
+  f32x4 acc[NTILES];
+#pragma unroll
+  for (int t = 0; t < NTILES; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // A head's running max is raised (and its accumulators rescaled) only when
+  // some score of the chunk exceeds it by more than 2^kLazy; otherwise the
+  // stale max stays and numerator and denominator share it.
+  constexpr float kLazy = 8.f;
+
+  auto compute_chunk = [&](int c0, int buf) {
+    const float* kt = lds[buf][0];
+    const float* vt = lds[buf][1];
+    // ---- S^T = K . Q^T (raw q.k) ----
+    f32x4 st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < DJ; ++j) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&kt[16 * mt * D + ka_off[j]]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          st[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[c], qf[j][c], st[mt], 0, 0, 0);
+      }
+    }
+    // positions past the segment (only in its last chunk) get -inf
+    if (c0 + kChunk > t1) {  // uniform
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c0 + 16 * mt + 4 * g + i >= t1) st[mt][i] = -INFINITY;
+    }
+    // ---- lazy online softmax for head n over positions {16mt + 4g + i} ----
+    // scale > 0: the largest scaled score is the largest raw score times the scale
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, st[mt][i]);
+    if (__any(lmax * scale_log2 > m_run + kLazy)) {
+      float cmax = fmaxf(lmax, __shfl_xor(lmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run, cmax * scale_log2);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int t = 0; t < NTILES; ++t) acc[t][i] *= a;
+      }
+    }
+    const float mneg = -m_run;  // finite: the segment's first chunk set it
+    float p[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[mt][i] = fast_exp2(fmaf(st[mt][i], scale_log2, mneg));
+        l_run += p[mt][i];
+      }
+    // ---- O += P . V ----
+#pragma unroll
+    for (int t = 0; t < NTILES; ++t)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[mt][i], vt[vb_off[t] + (16 * mt + i) * D], acc[t],
+                                                        0, 0, 0);
+  };
+
+  // ---- the ring: one chunk in flight while the previous one is multiplied ----
+  const int nchunk = (t1 - t0 + kChunk - 1) / kChunk;
+  copy_chunk(t0, 0);
+  for (int j = 0; j < nchunk; ++j) {
+    // this wave's copies of chunk j have landed; after the barrier every
+    // wave's have, and every wave is done reading chunk j-1 (whose buffer is
+    // refilled next).  A bare s_barrier: a fence would also wait for the
+    // copies of chunk j+1 issued after it.
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (j + 1 < nchunk) copy_chunk(t0 + (j + 1) * kChunk, (j + 1) & 1);
+    if (has_heads) compute_chunk(t0 + j * kChunk, j & 1);
+  }
+
+  if (has_heads) {
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
     const size_t row0 = (size_t)slot * G + (size_t)hb * kHB;
 #pragma unroll
-    for (int j = 0; j < HEADS_PER_THREAD; ++j) {
-      const int h = slice * HEADS_PER_THREAD + j;
-      if (h < nh) part_acc[(row0 + h) * D + c_own] = acc[u][j];
+    for (int i = 0; i < 4; ++i) {
+      const int hl = 4 * g + i;
+      if (hb * kHB + hl < G) {
+        float* dst = part_acc + (row0 + hl) * D;
+#pragma unroll
+        for (int t = 0; t < NTILES; ++t) dst[16 * t + n] = acc[t][i];
+      }
     }
-    if (tid < nh) {
-      float* ml = part_ml + (row0 + tid) * 2;
-      ml[0] = m_s[u][tid];
-      ml[1] = l_s[u][tid];
+    if (g == 0 && hq_ok) {
+      float* ml = part_ml + (row0 + n) * 2;
+      ml[0] = m_run;
+      ml[1] = l_run;
     }
   }
-  __syncthreads();  // m_s, l_s and qs are re-initialised by the next segment
+  // every wave is done with the ring before the next segment refills it
+  __syncthreads();
                         });
 }
 
@@ -277,25 +295,38 @@ hipError_t launch_decode_split_f32(const void* q, void* k_cache, void* v_cache,
                                    const DecodePlan& plan, int B, int H, int K, int S_max, int d,
                                    float scale_log2, const void* k_new, const void* v_new,
                                    hipStream_t stream) {
-  const int wg_per_range = (plan.head_blocks + kMaxHB - 1) / kMaxHB;
+  // one wave per 16-head block, at most kMaxW per workgroup
+  const int wg_per_range = (plan.head_blocks + kMaxW - 1) / kMaxW;
+  const int W = plan.head_blocks < kMaxW ? plan.head_blocks : kMaxW;
   const dim3 grid(plan.fa.n_wg * wg_per_range);
-  const dim3 block(kThreads);
   auto qp = static_cast<const float*>(q);
   auto kp = static_cast<float*>(k_cache);
   auto vp = static_cast<float*>(v_cache);
   auto kn = static_cast<const float*>(k_new);
   auto vn = static_cast<const float*>(v_new);
   const bool app = k_new != nullptr;
-#define GQA_SPLIT(DD, AP)                                                                         \
-  hipLaunchKernelGGL((decode_split_f32_kernel<DD, AP>), grid, block, 0, stream, qp, kp, vp,       \
-                     seq_lens, ws.part_acc, ws.part_ml, B, H, K, S_max, plan.fa, wg_per_range,     \
+#define GQA_F32(DD, AP, WW)                                                                       \
+  hipLaunchKernelGGL((decode_split_f32_kernel<DD, AP, WW>), grid, dim3(64 * WW), 0, stream, qp, kp, \
+                     vp, seq_lens, ws.part_acc, ws.part_ml, B, H, K, S_max, plan.fa, wg_per_range,  \
                      scale_log2, kn, vn, ws.meta)
-  if (d == 128) {
-    if (app) GQA_SPLIT(128, true); else GQA_SPLIT(128, false);
-  } else {
-    if (app) GQA_SPLIT(64, true); else GQA_SPLIT(64, false);
+#define GQA_F32_W(DD, AP)                                                                         \
+  switch (W) {                                                                                    \
+    case 1: GQA_F32(DD, AP, 1); break;                                                            \
+    case 2: GQA_F32(DD, AP, 2); break;                                                            \
+    case 3: GQA_F32(DD, AP, 3); break;                                                            \
+    case 4: GQA_F32(DD, AP, 4); break;                                                            \
+    case 5: GQA_F32(DD, AP, 5); break;                                                            \
+    case 6: GQA_F32(DD, AP, 6); break;                                                            \
+    case 7: GQA_F32(DD, AP, 7); break;                                                            \
+    default: GQA_F32(DD, AP, 8); break;                                                           \
   }
-#undef GQA_SPLIT
+  if (d == 128) {
+    if (app) { GQA_F32_W(128, true) } else { GQA_F32_W(128, false) }
+  } else {
+    if (app) { GQA_F32_W(64, true) } else { GQA_F32_W(64, false) }
+  }
+#undef GQA_F32_W
+#undef GQA_F32
   return hipGetLastError();
 }
 

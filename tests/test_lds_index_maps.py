@@ -93,3 +93,52 @@ def test_wide_int8_copies_conversion_and_reads(D, W):
                 vt[cv + e], vt[(cv ^ 8) + e] = (r, 16 * lp + e), (r, 16 * lp + 8 + e)
     assert len(kt) == len(vt) == 32 * D
     _check_bf16_reads(D, kt, vt)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("W", range(1, 9))
+def test_f32_copies_and_reads(D, W):
+    """fp32 pass (decode_f32.hip): 16-byte chunks of fp32 rows, K chunk ^
+    (row % 16), V chunk ^ 4 ((row / 4) % 4); K read as float4 pieces of row
+    16mt + n, V read one float per product; also the bank groups of the K
+    reads (16 lanes of a lane group) and of the V reads (all 64 lanes)."""
+    CPR = D // 4
+    NINST = 32 * D // 256
+    NI = (NINST + W - 1) // W
+    kt, vt = {}, {}
+    for wave in range(W):
+        for c in range(NI):
+            i = wave + c * W
+            ir = i % NINST
+            for lane in range(64):
+                r, ph = (64 * ir + lane) // CPR, lane % CPR
+                if i >= NINST:
+                    continue                                   # surplus copy: into the sink
+                base = 256 * i + 4 * lane                      # lane l lands at 16 l bytes
+                assert base == r * D + 4 * ph
+                for e in range(4):
+                    assert base + e not in kt
+                    kt[base + e] = (r, 4 * (ph ^ (r & 15)) + e)
+                    vt[base + e] = (r, 4 * (ph ^ (((r >> 2) & 3) << 2)) + e)
+    assert len(kt) == len(vt) == 32 * D
+    for mt in range(2):
+        for j in range(D // 16):
+            banks = {}
+            for lane in range(64):
+                n, g = lane & 15, lane >> 4
+                off = 16 * mt * D + n * D + 4 * ((4 * j + g) ^ n)
+                for c in range(4):                             # product (j, c): dim 16j + 4g + c
+                    assert kt[off + c] == (16 * mt + n, 16 * j + 4 * g + c)
+                banks.setdefault(g, set()).add((off * 4 // 16) % 16)   # 16-byte bank group
+            assert all(len(v) == 16 for v in banks.values())
+    for mt in range(2):
+        for i in range(4):
+            for t in range(D // 16):
+                banks = set()
+                for lane in range(64):
+                    n, g = lane & 15, lane >> 4
+                    vb = 4 * g * D + 4 * ((4 * t + (n >> 2)) ^ (g << 2)) + (n & 3)
+                    off = vb + (16 * mt + i) * D
+                    assert vt[off] == (16 * mt + 4 * g + i, 16 * t + n)
+                    banks.add(off % 64)                        # 64 four-byte banks
+                assert len(banks) == 64
