@@ -14,10 +14,10 @@
 // the range), so the K and V rows of the range are read from memory once for
 // all heads of the group (pinghaoyang.com.cn "GQA 完全拆解", section 工程实现:
 // the group's KV block is loaded once and reused by its query heads).  Rows
-// are staged in chunks of 32 positions through a two-buffer LDS ring filled
-// by direct global-to-LDS copies (global_load_lds_dwordx4, non-temporal);
-// per chunk and wave:
-//   S^T[32 x 16] = K_chunk . Q^T   (two 16-position tiles, D/4 products each)
+// are staged in chunks of CH positions (16 at d = 128, 32 at d = 64) through a
+// two-buffer LDS ring filled by direct global-to-LDS copies
+// (global_load_lds_dwordx4, non-temporal); per chunk and wave:
+//   S^T[CH x 16] = K_chunk . Q^T   (CH/16 16-position tiles, D/4 products each)
 //   lazy base-2 online softmax of head n over the chunk (fp32 weights)
 //   O[16 x D]   += P . V_chunk     (D/16 tiles, 8 products each)
 //
@@ -42,7 +42,6 @@
 namespace gqa {
 namespace {
 
-constexpr int kChunk = 32;   // positions per chunk
 constexpr int kHB = 16;      // heads per block (one wave)
 constexpr int kMaxW = 8;     // head blocks (waves) per workgroup
 // cache policy of the copies: non-temporal (each cache byte is read once per
@@ -52,7 +51,8 @@ constexpr int kStreamAux = 2;
 // s_waitcnt immediate (gfx9 encoding): vector-memory count 0, LDS count 0
 constexpr int kWaitAll = 0x0070;
 
-template <int D, bool APPEND, int W>
+// CH: positions per chunk (16 or 32)
+template <int D, bool APPEND, int W, int CH>
 __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     const float* __restrict__ q, float* __restrict__ kc, float* __restrict__ vc,
     const int32_t* __restrict__ seq_lens, float* __restrict__ part_acc,
@@ -60,6 +60,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     float scale_log2, const float* __restrict__ k_new, const float* __restrict__ v_new,
     int32_t* __restrict__ meta) {
   static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(CH == 16 || CH == 32, "chunk length");
+  constexpr int kChunk = CH;
+  constexpr int MT = CH / 16;                // 16-position score tiles per chunk
   constexpr int CPR = D / 4;                 // 16-byte chunks per row
   constexpr int TILE = kChunk * D;           // floats per staged tensor
   constexpr int NINST = TILE / 256;          // 1 KB copies per tensor and chunk
@@ -187,9 +190,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     const float* kt = lds[buf][0];
     const float* vt = lds[buf][1];
     // ---- S^T = K . Q^T (raw q.k) ----
-    f32x4 st[2];
+    f32x4 st[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < DJ; ++j) {
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     // positions past the segment (only in its last chunk) get -inf
     if (c0 + kChunk > t1) {  // uniform
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (c0 + 16 * mt + 4 * g + i >= t1) st[mt][i] = -INFINITY;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     // scale > 0: the largest scaled score is the largest raw score times the scale
     float lmax = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, st[mt][i]);
     if (__any(lmax * scale_log2 > m_run + kLazy)) {
@@ -229,9 +232,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
       }
     }
     const float mneg = -m_run;  // finite: the segment's first chunk set it
-    float p[2][4];
+    float p[MT][4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[mt][i] = fast_exp2(fmaf(st[mt][i], scale_log2, mneg));
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
 #pragma unroll
     for (int t = 0; t < NTILES; ++t)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[mt][i], vt[vb_off[t] + (16 * mt + i) * D], acc[t],
@@ -305,10 +308,11 @@ hipError_t launch_decode_split_f32(const void* q, void* k_cache, void* v_cache,
   auto kn = static_cast<const float*>(k_new);
   auto vn = static_cast<const float*>(v_new);
   const bool app = k_new != nullptr;
-#define GQA_F32(DD, AP, WW)                                                                       \
-  hipLaunchKernelGGL((decode_split_f32_kernel<DD, AP, WW>), grid, dim3(64 * WW), 0, stream, qp, kp, \
-                     vp, seq_lens, ws.part_acc, ws.part_ml, B, H, K, S_max, plan.fa, wg_per_range,  \
-                     scale_log2, kn, vn, ws.meta)
+// chunks of 16 positions at d = 128 (32 KB of LDS per workgroup), 32 at d = 64
+#define GQA_F32(DD, AP, WW)                                                                        \
+  hipLaunchKernelGGL((decode_split_f32_kernel<DD, AP, WW, DD == 128 ? 16 : 32>), grid, dim3(64 * WW),  \
+                     0, stream, qp, kp, vp, seq_lens, ws.part_acc, ws.part_ml, B, H, K, S_max, plan.fa, \
+                     wg_per_range, scale_log2, kn, vn, ws.meta)
 #define GQA_F32_W(DD, AP)                                                                         \
   switch (W) {                                                                                    \
     case 1: GQA_F32(DD, AP, 1); break;                                                            \

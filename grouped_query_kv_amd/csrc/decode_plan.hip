@@ -17,10 +17,11 @@ namespace {
 // bf16 pass three workgroups per CU (2-5% ahead of four, 10% ahead of two
 // and of eight); the int8 pass eight (two waves per SIMD); a multi-wave pass
 // (groups of more than 16 heads, one wave per 16-head block) four; the fp32
-// pass's 256-thread workgroups two.
+// pass four one-wave workgroups (groups of up to 16 heads; 26% ahead of two
+// at d = 128) and two multi-wave ones.
 constexpr int kCUs = 256;
 int target_wgs(PassKind kind, int head_blocks) {
-  if (kind == PassKind::kF32) return 2 * kCUs;
+  if (kind == PassKind::kF32) return head_blocks > 1 ? 2 * kCUs : 4 * kCUs;
   if (head_blocks > 1) return 4 * kCUs;
   return kind == PassKind::kInt8 ? 8 * kCUs : 3 * kCUs;
 }
