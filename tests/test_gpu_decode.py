@@ -63,6 +63,14 @@ CASES = [
     (4, 64, 8, 128, [0, 1, 640, 641], "bf16"),  # empty sequence, partition edges
     (2, 12, 4, 128, [70, 3], "f32"),
     (1, 71, 1, 128, [200], "f32"),
+    # fp32 pass (one wave per 16-head block): head-block counts 1..9, both chunk lengths
+    (2, 32, 2, 64, [1000, 17], "f32"),         # G = 16: one wave
+    (2, 34, 2, 128, [100, 33], "f32"),         # G = 17: a second block with one head
+    (3, 160, 2, 64, [129, 0, 2000], "f32"),    # d = 64, G = 80: five waves, an empty sequence
+    (1, 128, 1, 128, [1500], "f32"),           # G = 128: eight waves
+    (1, 144, 1, 128, [300], "f32"),            # G = 144: two workgroups per range (8 + 1 blocks)
+    (1, 144, 1, 64, [300], "f32"),
+    (4, 64, 8, 128, [0, 1, 640, 641], "f32"),  # empty sequence, partition edges
 ]
 
 
