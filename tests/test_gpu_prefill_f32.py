@@ -1,6 +1,6 @@
-"""GPU parity of the fp32 prefill family (fp32 inputs and outputs, vector
-ALUs) against the fp64 oracle at the fp32 gate (max-abs 1e-5): causal
-prefill, a chunk over a cache, cross-attention."""
+"""GPU parity of the fp32 prefill family (fp32 inputs and outputs, the
+matrix cores in fp32) against the fp64 oracle at the fp32 gate (max-abs
+1e-5): causal prefill, a chunk over a cache, cross-attention."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +21,8 @@ CASES = [
     (1, 6, 2, 17, 128, 17),      # G = 3: an idle head row block
     (2, 8, 8, 1, 64, 1),         # one position
     (1, 71, 1, 20, 64, 24),      # G = 71: eighteen head chunks, the last holding 3 heads
+    (1, 16, 2, 300, 128, 320),   # G = 8: ten 32-key tiles, nineteen query blocks
+    (2, 32, 8, 257, 64, 260),    # G = 4: 32-position query blocks, a ragged last tile
 ]
 
 

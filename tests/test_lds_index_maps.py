@@ -142,3 +142,37 @@ def test_f32_copies_and_reads(D, W):
                     assert vt[off] == (16 * mt + 4 * g + i, 16 * t + n)
                     banks.add(off % 64)                        # 64 four-byte banks
                 assert len(banks) == 64
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_f32_prefill_copies_and_reads(D):
+    """fp32 prefill (prefill_f32.hip): 32-key tiles copied by the four waves
+    (copy r of wave w is instruction w + 4r), the fp32 decode pass's
+    swizzles; every element lands once and every K / V read finds it."""
+    CPR = D // 4
+    COPIES = 32 * D // 256 // 4
+    kt, vt = {}, {}
+    for wave in range(4):
+        for r in range(COPIES):
+            i = wave + 4 * r
+            for lane in range(64):
+                c = 64 * i + lane
+                row, cp = c // CPR, c % CPR
+                base = 256 * i + 4 * lane
+                assert base == row * D + 4 * cp
+                for e in range(4):
+                    assert base + e not in kt
+                    kt[base + e] = (row, 4 * (cp ^ (row & 15)) + e)
+                    vt[base + e] = (row, 4 * (cp ^ (((row >> 2) & 3) << 2)) + e)
+    assert len(kt) == len(vt) == 32 * D
+    for lane in range(64):
+        n, g = lane & 15, lane >> 4
+        for mt in range(2):
+            for jj in range(D // 16):
+                off = 16 * mt * D + n * D + 4 * ((4 * jj + g) ^ n)
+                for c in range(4):
+                    assert kt[off + c] == (16 * mt + n, 16 * jj + 4 * g + c)
+            for i in range(4):
+                for t in range(D // 16):
+                    vb = 4 * g * D + 4 * ((4 * t + (n >> 2)) ^ (g << 2)) + (n & 3)
+                    assert vt[vb + (16 * mt + i) * D] == (16 * mt + 4 * g + i, 16 * t + n)
