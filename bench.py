@@ -50,6 +50,7 @@ import torch
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix-core peak
+F32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 matrix-core peak
 
 
 def parse():
@@ -467,17 +468,22 @@ def bench_prefill(args, w):
     S_q = {"prefill": w.L, "chunk": w.extra.get("chunk"), "cross": w.extra.get("S_q")}[w.kind]
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "K": w.K, "d": w.d, "S_q": S_q, "kv_len": w.L,
            "parallelism": "single GPU"}
+    # a contraction takes the matrix-core peak of its own type
+    f32 = w.dtype == "f32"
+    peak = F32_MFMA_PEAK_TFLOPS if f32 else BF16_MFMA_PEAK_TFLOPS
     res = {
-        "metric": PREFILL_METRIC[w.kind],
+        "metric": PREFILL_METRIC[w.kind].replace("bf16 MFMA", "fp32 MFMA") if f32 else PREFILL_METRIC[w.kind],
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": cfg,
         "tokens_per_s": round(w.B * S_q / (ms_per_step * 1e-3), 1),
-        "roofline": {"kernel": f"{w.kind} attention (prefill_kernel)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic("prefill_causal_kernel", w.name) if w.kind == "prefill" else None,
+        "roofline": {"kernel": f"{w.kind} attention ({'prefill_f32_kernel' if f32 else 'prefill_kernel'})",
+                     "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": (recorded_traffic("prefill_causal_kernel", w.name)
+                                 if w.kind == "prefill" and not f32 else None),
                      "avg_kernel_us": round(kern_ms * 1e3, 3)},
         "input_gen_s": round(t_gen, 1),
     }

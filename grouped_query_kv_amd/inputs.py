@@ -96,6 +96,9 @@ WORKLOADS = {
     "prefill_causal_4k": Workload(
         "prefill_causal_4k", "prefill", B=2, H=64, K=8, d=128, dtype="bf16", L=4096,
         note="causal prefill, S=4096, 64 query heads over 8 KV heads"),
+    "prefill_causal_4k_f32": Workload(
+        "prefill_causal_4k_f32", "prefill", B=2, H=64, K=8, d=128, dtype="f32", L=4096,
+        note="prefill_causal_4k with fp32 inputs and outputs"),
 }
 
 
