@@ -120,3 +120,52 @@ def test_random_chunk_and_cross(case):
     ref2 = cross_attention_ref(f64(inp["q"]), inp["k"].float().numpy(), inp["v"].float().numpy(), kl2.numpy(), sc)
     r2 = report("cross", f64(out2), ref2)
     assert r2["finite"] and r2["max_abs"] <= min(TOL["bf16"], bf16_bound(ref2, vmax, weights_in_denominator=True))
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_decode_f32(case):
+    """The fp32 decode pass (matrix cores in fp32) over the same seeded group
+    sizes, small and large, at the fp32 gate."""
+    groups = SMALL_GROUPS if case % 2 == 0 else LARGE_GROUPS
+    B, H, K, d, lens = _cases(2027 + case % 2, groups)[case]
+    note(f"random f32 decode B={B} H={H} K={K} d={d} lens={lens}")
+    s_max = max(lens) + 1
+    inp = decode_inputs(B, H, K, d, "f32", seed=900 + case, lens=lens, s_max=s_max)
+    msl = max(max(lens), 1)
+    ws = torch.empty(max(gqa.gqa_decode_workspace_bytes(B, H, K, msl, d), 16), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, H, d), dtype=torch.float32, device=DEV)
+    gqa.gqa_decode(inp["q"].to(DEV), inp["k_cache"].to(DEV), inp["v_cache"].to(DEV), inp["seq_lens"].to(DEV), out,
+                   ws, msl, scale=scale_of(d))
+    torch.cuda.synchronize()
+    ref = decode_ref(f64(inp["q"]), inp["k_cache"].double().numpy(), inp["v_cache"].double().numpy(), lens,
+                     scale_of(d))
+    r = report("f32 decode", f64(out), ref)
+    assert r["finite"] and r["max_abs"] <= TOL["f32"]
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_chunk_and_cross_f32(case):
+    """The fp32 prefill family (matrix cores in fp32): a chunk over a cache and
+    cross-attention on seeded shapes, at the fp32 gate."""
+    B, H, K, d, lens = _cases(2028)[case]
+    r = np.random.default_rng(1000 + case)
+    S_q = int(r.integers(1, 200))
+    kv = [max(L, S_q) for L in lens]
+    note(f"random f32 chunk/cross B={B} H={H} K={K} d={d} S_q={S_q} kv={kv}")
+    inp = attention_inputs(B, H, K, S_q, d, "f32", seed=1100 + case, kv_lens=kv, s_max=max(kv) + 2)
+    q, k, v, kl = (inp[n].to(DEV) for n in ("q", "k", "v", "kv_lens"))
+    sc = scale_of(d)
+    out = torch.empty(q.shape, dtype=torch.float32, device=DEV)
+    gqa.gqa_prefill_chunk(q, k, v, kl, out, scale=sc)
+    torch.cuda.synchronize()
+    ref = prefill_chunk_ref(f64(inp["q"]), inp["k"].double().numpy(), inp["v"].double().numpy(), np.array(kv), sc)
+    r1 = report("f32 chunk", f64(out), ref)
+    assert r1["finite"] and r1["max_abs"] <= TOL["f32"]
+    kl2 = torch.tensor(lens, dtype=torch.int32)
+    out2 = torch.empty_like(out)
+    gqa.gqa_cross_attention(q, k, v, kl2.to(DEV), out2, scale=sc)
+    torch.cuda.synchronize()
+    ref2 = cross_attention_ref(f64(inp["q"]), inp["k"].double().numpy(), inp["v"].double().numpy(), kl2.numpy(),
+                               sc)
+    r2 = report("f32 cross", f64(out2), ref2)
+    assert r2["finite"] and r2["max_abs"] <= TOL["f32"]
