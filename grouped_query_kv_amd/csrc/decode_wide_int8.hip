@@ -39,10 +39,11 @@
 namespace gqa {
 namespace {
 
-// Cache policy of the global-to-LDS copies of the cache: non-temporal (every
-// byte is read once per step), as in the bf16 multi-wave pass, where it was
-// measured 5-12% faster than the default policy on multi-query shapes.
-constexpr int kStreamAux = 2;  // the nt bit of the instruction's cache-policy field
+// Cache policy of the global-to-LDS copies of the cache: the default.  (The
+// non-temporal bit, 5-12% faster in the bf16 multi-wave pass, measured 2-4%
+// slower here: 128 against 124.5 us on a 71-head int8 layer at d = 64, 80
+// against 78 us with 32 heads per KV head at d = 128.)
+constexpr int kStreamAux = 0;
 
 constexpr int kChunk = 32;
 
