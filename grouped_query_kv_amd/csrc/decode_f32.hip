@@ -44,9 +44,12 @@ namespace {
 
 constexpr int kHB = 16;      // heads per block (one wave)
 constexpr int kMaxW = 8;     // head blocks (waves) per workgroup
-// cache policy of the copies: non-temporal (each cache byte is read once per
-// step); the nt bit of the instruction's cache-policy field
-constexpr int kStreamAux = 2;
+// cache policy of the copies: non-temporal (the nt bit of the instruction's
+// cache-policy field; each cache byte is read once per step) for one-wave
+// workgroups, which stream at the rate of HBM (10% faster on an fp32
+// Llama-3-8B-shaped layer), the default for multi-wave ones, which are bound
+// by their products (2-5% faster without it on multi-query layers)
+constexpr int kStreamAuxOneWave = 2;
 
 // s_waitcnt immediate (gfx9 encoding): vector-memory count 0, LDS count 0
 constexpr int kWaitAll = 0x0070;
@@ -150,6 +153,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     ck[c] = 16 * (ph ^ (r & 15));
     cv[c] = 16 * (ph ^ (((r >> 2) & 3) << 2));
   }
+  constexpr int kAux = W == 1 ? kStreamAuxOneWave : 0;
   auto copy_chunk = [&](int c0, int buf) {
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
@@ -160,8 +164,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
       const char* vp = reinterpret_cast<const char*>(vbase + (size_t)c0 * D) + (ro + cv[c]);
       float* kd = i < NINST ? &lds[buf][0][i * 256] : sink;
       float* vd = i < NINST ? &lds[buf][1][i * 256] : sink;
-      __builtin_amdgcn_global_load_lds(kp, (__attribute__((address_space(3))) void*)kd, 16, 0, kStreamAux);
-      __builtin_amdgcn_global_load_lds(vp, (__attribute__((address_space(3))) void*)vd, 16, 0, kStreamAux);
+      __builtin_amdgcn_global_load_lds(kp, (__attribute__((address_space(3))) void*)kd, 16, 0, kAux);
+      __builtin_amdgcn_global_load_lds(vp, (__attribute__((address_space(3))) void*)vd, 16, 0, kAux);
     }
   };
 
