@@ -16,7 +16,8 @@
 // the group's KV block is loaded once and reused by its query heads).  Rows
 // are staged in chunks of CH positions (16 at d = 128, 32 at d = 64) through a
 // two-buffer LDS ring filled by direct global-to-LDS copies
-// (global_load_lds_dwordx4, non-temporal); per chunk and wave:
+// (global_load_lds_dwordx4; non-temporal in one-wave workgroups); per chunk
+// and wave:
 //   S^T[CH x 16] = K_chunk . Q^T   (CH/16 16-position tiles, D/4 products each)
 //   lazy base-2 online softmax of head n over the chunk (fp32 weights)
 //   O[16 x D]   += P . V_chunk     (D/16 tiles, 8 products each)
