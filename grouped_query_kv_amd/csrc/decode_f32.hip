@@ -111,8 +111,9 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
   // The fused append: the workgroup(s) whose partition holds the appended
   // position write the new rows into the cache before anything is copied
   // (every workgroup of the range writes the same values), so the copies
-  // read the cache alone; workgroup-scope release and acquire around the
-  // barrier order wave 0's stores before the other waves' copies.
+  // read the cache alone; wave 0 waits for its stores to complete
+  // (vmcnt(0): a workgroup-scope release alone compiles to no wait here)
+  // before the barrier, so no other wave's copy of the row can overtake them.
   if (APPEND && newpos >= t0 && newpos < t1) {  // uniform
     if (wave == 0 && lane < CPR) {
       const float* kn = k_new + ((size_t)b * K + k) * D;
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
       *reinterpret_cast<f32x4*>(vbase + (size_t)newpos * D + 4 * lane) =
           *reinterpret_cast<const f32x4*>(vn + 4 * lane);
     }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");

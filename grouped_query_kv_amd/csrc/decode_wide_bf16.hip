@@ -73,12 +73,13 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// s_waitcnt immediate (gfx9 encoding): vector-memory count <= vm, LDS count 0
+// physical-chunk XOR of a staged V row r (the layout described above)
 template <int D>
 __device__ __forceinline__ int v_swizzle(int r) {
   return D == 64 ? ((r >> 1) & 3) << 1 : (r & 7) << 1;
 }
 
+// s_waitcnt immediate (gfx9 encoding): vector-memory count <= vm, LDS count 0
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (((vm >> 4) & 3) << 14); }
 
 // Four workgroups of W waves per CU: from W = 5 on, the d = 64 pass must fit six
@@ -172,9 +173,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_min
   };
   // The fused append: the workgroup whose partition holds the appended
   // position writes the new K and V rows into the cache before anything is
-  // copied, so every copy below reads the cache alone.  Workgroup-scope
-  // release and acquire around the barrier order the stores of wave 0 before
-  // the other waves' copies (all waves of a workgroup share one CU's caches).
+  // copied, so every copy below reads the cache alone.  Wave 0 waits for
+  // its stores to complete (vmcnt(0): a workgroup-scope release alone
+  // compiles to no wait here) before the barrier, so no other wave's copy of
+  // the row can overtake them.
   if (APPEND && newpos >= t0 && newpos < t1) {  // uniform
     if (wave == 0 && lane < LPR) {
       const __bf16* knew_row = k_new + ((size_t)b * K + k) * D;
@@ -182,6 +184,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_min
       *reinterpret_cast<u32x4*>(row_of(kbase, newpos, newpos) + 8 * lane) = ld16(knew_row + 8 * lane);
       *reinterpret_cast<u32x4*>(row_of(vbase, newpos, newpos) + 8 * lane) = ld16(vnew_row + 8 * lane);
     }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");

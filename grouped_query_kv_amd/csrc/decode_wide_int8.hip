@@ -15,15 +15,15 @@
 // with codes converted to bf16 (exact; see below) and the value scale
 // folded into each position's bf16 weight, and the same quantising append.
 //
-// Fused append: the first wave quantises the step's new K and V rows into
-// its registers (the int8 pass's fp32 rule, shared helpers).  The new row is
-// the last position of its sequence, so it lies in the last chunk of the
-// last partition; that chunk's copies fetch the (not yet written) cache row,
-// and once every wave's copies have landed the first wave overwrites the
-// row's staged codes and its two scales in LDS, and a barrier orders that
-// before the conversion.  No other wave reads data another wave wrote to
-// global memory in this launch.  After the loop the first wave writes the
-// codes and scales into the cache.
+// Fused append: the workgroup whose partition holds the new position (the
+// last position of its sequence) quantises the step's K and V rows by the
+// int8 pass's fp32 rule (shared helpers) straight into the cache row and its
+// two scales before its first copy; the writing wave waits for its stores
+// to complete (vmcnt(0)) and a barrier follows, so the copies that stage
+// that row afterwards read the new codes.  Holding the quantised row in
+// registers through the loop instead (and patching it into LDS) cost the
+// registers that kept four five-wave workgroups per CU resident: 124 against
+// 95 us on a 71-head int8 layer at d = 64.
 //
 // Each chunk's codes are converted to bf16 once, by all threads of the
 // workgroup together (each thread a share of the 16-byte pieces), into bf16
@@ -41,8 +41,9 @@ namespace {
 
 // Cache policy of the global-to-LDS copies of the cache: the default.  (The
 // non-temporal bit, 5-12% faster in the bf16 multi-wave pass, measured 2-4%
-// slower here: 128 against 124.5 us on a 71-head int8 layer at d = 64, 80
-// against 78 us with 32 heads per KV head at d = 128.)
+// slower here, before the occupancy bound below: 128 against 124.5 us on a
+// 71-head int8 layer at d = 64, 80 against 78 us with 32 heads per KV head
+// at d = 128.)
 constexpr int kStreamAux = 0;
 
 constexpr int kChunk = 32;
@@ -75,8 +76,15 @@ __device__ __forceinline__ int piece_swizzle(int r) {
   return r & (D / 16 - 1);
 }
 
+// Four workgroups per CU: from W = 5 on, the d = 64 pass is held to five
+// waves per SIMD (at most 96 registers; two pointers spill outside the
+// loop).  Measured on a 71-head layer at d = 64: 95 against 124 us without
+// the bound.
+template <int D, int W>
+constexpr int wide_int8_min_waves() { return D == 64 && W >= 5 ? 5 : 1; }
+
 template <int D, bool APPEND, int W>
-__global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_int8_min_waves<D, W>()))) void decode_wide_int8_kernel(
     const __bf16* __restrict__ q, int8_t* __restrict__ kc, int8_t* __restrict__ vc,
     float* __restrict__ ks, float* __restrict__ vs, const int32_t* __restrict__ seq_lens,
     float* __restrict__ part_acc, float* __restrict__ part_ml, int B, int H, int K, int S_max,
@@ -144,33 +152,44 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
   float* ksb = ks + head_row0;
   float* vsb = vs + head_row0;
 
-  // The new rows (fused append): wave 0 quantises them into registers,
-  // lane l holding the codes of elements E l .. E l + E - 1 of each row.
+  // The fused append: the workgroup whose partition holds the new position
+  // quantises the step's K and V rows (wave 0, lane l elements E l ..
+  // E l + E - 1) straight into the cache row and its scale before anything
+  // is copied, so every copy below reads the cache alone.  Wave 0 waits for
+  // its stores to complete (vmcnt(0)) before the barrier, so no other wave's
+  // copy of the row can overtake them.
   constexpr int E = D / 64;  // elements per lane
-  const bool has_new = APPEND && newpos >= t0 && newpos < t1;  // uniform
-  uint32_t new_codes[2] = {0u, 0u};  // K, V: E code bytes, little-endian
-  float new_scale[2] = {0.f, 0.f};
-  if (has_new && wave == 0) {
+  if (APPEND && newpos >= t0 && newpos < t1) {  // uniform
+    if (wave == 0) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const __bf16* src = (r == 0 ? k_new : v_new) + ((size_t)b * K + k) * D + E * lane;
-      float x[E];
-      float amax = 0.f;
+      for (int r = 0; r < 2; ++r) {
+        const __bf16* src = (r == 0 ? k_new : v_new) + ((size_t)b * K + k) * D + E * lane;
+        float x[E];
+        float amax = 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        x[e] = static_cast<float>(src[e]);
-        amax = fmaxf(amax, fabsf(x[e]));
+        for (int e = 0; e < E; ++e) {
+          x[e] = static_cast<float>(src[e]);
+          amax = fmaxf(amax, fabsf(x[e]));
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
+        const float inv = amax > 0.f ? int8_inv(amax) : 0.f;
+        uint32_t w = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          w |= (uint32_t)(uint8_t)(amax > 0.f ? (int8_t)int8_code(x[e], inv) : (int8_t)0) << (8 * e);
+        int8_t* dst = (r == 0 ? kbase : vbase) + (size_t)newpos * D + E * lane;
+        if (E == 2)
+          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w;
+        else
+          *dst = (int8_t)w;
+        if (lane == 0) (r == 0 ? ksb : vsb)[newpos] = amax > 0.f ? int8_scale(amax) : 0.f;
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o /= 2) amax = fmaxf(amax, __shfl_xor(amax, o));
-      const float inv = amax > 0.f ? int8_inv(amax) : 0.f;
-      uint32_t w = 0u;
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        w |= (uint32_t)(uint8_t)(amax > 0.f ? (int8_t)int8_code(x[e], inv) : (int8_t)0) << (8 * e);
-      new_codes[r] = w;
-      new_scale[r] = amax > 0.f ? int8_scale(amax) : 0.f;
     }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0): the stores are complete
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 
   // Copy slot c of this wave: instruction i = wave + c W of a chunk (surplus
@@ -269,30 +288,6 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (c0 + kChunk < t1) copy_chunk(c0 + kChunk, buf ^ 1);
-    if (has_new && c0 + kChunk >= t1) {  // uniform: the chunk holding the new row
-      // every copy of this chunk has landed (the barrier above); replace the
-      // new row's staged codes and scales, then order that before convert
-      if (wave == 0) {
-        const int rn = newpos - c0;
-        const int x = E * lane;  // first element of this lane (E <= 2: one piece)
-        const int off = rn * D + 16 * ((x >> 4) ^ piece_swizzle<D>(rn)) + (x & 15);
-        if (E == 2) {
-          *reinterpret_cast<uint16_t*>(&kq[buf][off]) = (uint16_t)new_codes[0];
-          *reinterpret_cast<uint16_t*>(&vq[buf][off]) = (uint16_t)new_codes[1];
-        } else {
-          kq[buf][off] = (int8_t)new_codes[0];
-          vq[buf][off] = (int8_t)new_codes[1];
-        }
-        if (lane == 0) {
-          ksc[buf][rn] = new_scale[0];
-          vsc[buf][rn] = new_scale[1];
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the LDS stores are done
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
     convert(buf);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's bf16 stores are done
     asm volatile("" ::: "memory");
@@ -361,22 +356,6 @@ __global__ __launch_bounds__(64 * W) void decode_wide_int8_kernel(
 
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-
-  if (APPEND && has_new && wave == 0) {  // the appended rows join the cache
-    int8_t* kd = kbase + (size_t)newpos * D + E * lane;
-    int8_t* vd = vbase + (size_t)newpos * D + E * lane;
-    if (E == 2) {
-      *reinterpret_cast<uint16_t*>(kd) = (uint16_t)new_codes[0];
-      *reinterpret_cast<uint16_t*>(vd) = (uint16_t)new_codes[1];
-    } else {
-      *kd = (int8_t)new_codes[0];
-      *vd = (int8_t)new_codes[1];
-    }
-    if (lane == 0) {
-      ksb[newpos] = new_scale[0];
-      vsb[newpos] = new_scale[1];
-    }
-  }
 
   const size_t row0 = (size_t)slot_id * G + (size_t)hb * 16;
 #pragma unroll
