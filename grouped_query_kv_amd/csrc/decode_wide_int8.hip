@@ -25,8 +25,8 @@
 // registers that kept four five-wave workgroups per CU resident: 124 against
 // 95 us on a 71-head int8 layer at d = 64.
 //
-// Each chunk's codes are converted to bf16 once, by all threads of the
-// workgroup together (each thread a share of the 16-byte pieces), into bf16
+// Each chunk's codes are converted to bf16 once, by the threads of the
+// workgroup together (each 16-byte piece of K or V by one thread), into bf16
 // tiles in LDS laid out as in the wide bf16 pass; every wave then reads its
 // operands from there exactly as that pass does (K as 16-byte operand reads,
 // V with transposed ds_read_b64_tr_b16 reads), so the conversion work is not
@@ -96,7 +96,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_int
   constexpr int LPR = D / 8;                // 16-byte chunks per bf16 row
   constexpr int CPR = D / 16;               // 16-byte pieces per code row
   constexpr int NPIECE = kChunk * CPR;      // pieces per staged code tile
-  constexpr int NCONV = (NPIECE + 64 * W - 1) / (64 * W);  // pieces per thread per tensor
+  constexpr int NUNIT = 2 * NPIECE;         // conversion units: the K pieces, then the V pieces
+  constexpr int NCONV = (NUNIT + 64 * W - 1) / (64 * W);  // units per thread
+  static_assert(NPIECE % 64 == 0, "a wave's units are all K or all V");
   constexpr int TILE = kChunk * D;          // bytes of a staged code tile
   constexpr int NINST = TILE / 1024;        // 1 KB copies per tensor and chunk
   constexpr int NI = (NINST + W - 1) / W;   // copies per wave per tensor and chunk
@@ -231,32 +233,36 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_int
     }
   };
 
-  // conversion share of this thread: staged piece pc = tid + 64 W i
-  // (row pc / CPR, logical piece pc % CPR) -> bf16 chunks 2 lp, 2 lp + 1
-  int cv_src[NCONV], cv_k[NCONV], cv_v[NCONV];
+  // conversion share of this thread: unit u = tid + 64 W i, the staged K
+  // piece u (u < NPIECE) or V piece u - NPIECE (row pc / CPR, logical piece
+  // pc % CPR) -> bf16 chunks 2 lp, 2 lp + 1.  Each unit is converted by one
+  // thread; threads past the last unit (whole waves) convert nothing.
+  int cv_src[NCONV], cv_dst[NCONV];
+  bool cv_isv[NCONV], cv_on[NCONV];  // wave-uniform
 #pragma unroll
   for (int i = 0; i < NCONV; ++i) {
-    const int pc = min((int)threadIdx.x + 64 * W * i, NPIECE - 1);  // extra threads redo the last piece
+    const int u = (int)threadIdx.x + 64 * W * i;
+    cv_on[i] = u < NUNIT;
+    const int uu = min(u, NUNIT - 1);
+    cv_isv[i] = uu >= NPIECE;
+    const int pc = cv_isv[i] ? uu - NPIECE : uu;
     const int r = pc / CPR, lp = pc % CPR;
     cv_src[i] = r * D + 16 * (lp ^ piece_swizzle<D>(r));
-    cv_k[i] = r * D + 8 * ((2 * lp) ^ (r & (LPR - 1)));        // chunk 2 lp; 2 lp + 1 is chunk ^ 1
-    cv_v[i] = r * D + 8 * ((2 * lp) ^ v_swizzle<D>(r));
+    // chunk 2 lp; chunk 2 lp + 1 is its neighbour ^ 1
+    cv_dst[i] = r * D + 8 * ((2 * lp) ^ (cv_isv[i] ? v_swizzle<D>(r) : (r & (LPR - 1))));
   }
   auto convert = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NCONV; ++i) {
-      const u32x4 ck = *reinterpret_cast<const u32x4*>(&kq[buf][cv_src[i]]);
-      const u32x4 cvv = *reinterpret_cast<const u32x4*>(&vq[buf][cv_src[i]]);
-      const uint2 k0 = codes_to_bf16x4(ck[0]), k1 = codes_to_bf16x4(ck[1]);
-      const uint2 k2 = codes_to_bf16x4(ck[2]), k3 = codes_to_bf16x4(ck[3]);
-      const uint2 v0 = codes_to_bf16x4(cvv[0]), v1 = codes_to_bf16x4(cvv[1]);
-      const uint2 v2 = codes_to_bf16x4(cvv[2]), v3 = codes_to_bf16x4(cvv[3]);
+      if (!cv_on[i]) continue;  // uniform
+      const u32x4 c = *reinterpret_cast<const u32x4*>(&(cv_isv[i] ? vq : kq)[buf][cv_src[i]]);
+      const uint2 w0 = codes_to_bf16x4(c[0]), w1 = codes_to_bf16x4(c[1]);
+      const uint2 w2 = codes_to_bf16x4(c[2]), w3 = codes_to_bf16x4(c[3]);
       // chunk 2lp ^ s lands at s, chunk 2lp+1 at s ^ 8 elements (the swizzle
       // flips whole 16-byte chunks and keeps pairs (2c, 2c+1) together)
-      *reinterpret_cast<u32x4*>(&kt[cv_k[i]]) = u32x4{k0.x, k0.y, k1.x, k1.y};
-      *reinterpret_cast<u32x4*>(&kt[cv_k[i] ^ 8]) = u32x4{k2.x, k2.y, k3.x, k3.y};
-      *reinterpret_cast<u32x4*>(&vt[cv_v[i]]) = u32x4{v0.x, v0.y, v1.x, v1.y};
-      *reinterpret_cast<u32x4*>(&vt[cv_v[i] ^ 8]) = u32x4{v2.x, v2.y, v3.x, v3.y};
+      uint16_t* dst = cv_isv[i] ? vt : kt;
+      *reinterpret_cast<u32x4*>(&dst[cv_dst[i]]) = u32x4{w0.x, w0.y, w1.x, w1.y};
+      *reinterpret_cast<u32x4*>(&dst[cv_dst[i] ^ 8]) = u32x4{w2.x, w2.y, w3.x, w3.y};
     }
   };
   // bf16 operand offsets, as in the wide bf16 pass

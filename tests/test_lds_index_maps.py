@@ -77,20 +77,31 @@ def test_wide_int8_copies_conversion_and_reads(D, W):
                 assert 1024 * i + 16 * lane == r * D + 16 * ph
                 staged[r * D + 16 * ph] = (r, ph ^ (r & (CPR - 1)))   # logical 16-code piece
     assert len(staged) == 32 * CPR
-    # every thread converts its share of pieces into the bf16 tiles
+    # conversion units: the K pieces, then the V pieces, one thread each;
+    # whole waves past the last unit convert nothing, and no bf16 element is
+    # written twice
     NP = 32 * CPR
-    NCONV = (NP + 64 * W - 1) // (64 * W)
+    NU = 2 * NP
+    NCONV = (NU + 64 * W - 1) // (64 * W)
     kt, vt = {}, {}
     for tid in range(64 * W):
         for i in range(NCONV):
-            pc = min(tid + 64 * W * i, NP - 1)
+            u = tid + 64 * W * i
+            first = (tid - tid % 64) + 64 * W * i            # lane 0 of this thread's wave
+            assert (u < NU) == (first < NU)                  # activity is wave-uniform
+            if u >= NU:
+                continue
+            isv = u >= NP
+            assert isv == (first >= NP)                      # so is the tensor
+            pc = u - NP if isv else u
             r, lp = pc // CPR, pc % CPR
             assert staged[r * D + 16 * (lp ^ (r & (CPR - 1)))] == (r, lp)
-            ck = r * D + 8 * ((2 * lp) ^ _bf16_k_swizzle(D, r))
-            cv = r * D + 8 * ((2 * lp) ^ _bf16_v_swizzle(D, r))
+            tile = vt if isv else kt
+            dst = r * D + 8 * ((2 * lp) ^ (_bf16_v_swizzle(D, r) if isv else _bf16_k_swizzle(D, r)))
             for e in range(8):
-                kt[ck + e], kt[(ck ^ 8) + e] = (r, 16 * lp + e), (r, 16 * lp + 8 + e)
-                vt[cv + e], vt[(cv ^ 8) + e] = (r, 16 * lp + e), (r, 16 * lp + 8 + e)
+                for off, val in ((dst + e, (r, 16 * lp + e)), ((dst ^ 8) + e, (r, 16 * lp + 8 + e))):
+                    assert off not in tile
+                    tile[off] = val
     assert len(kt) == len(vt) == 32 * D
     _check_bf16_reads(D, kt, vt)
 
