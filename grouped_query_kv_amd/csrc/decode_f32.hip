@@ -71,13 +71,10 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
   constexpr int TILE = kChunk * D;           // floats per staged tensor
   constexpr int NINST = TILE / 256;          // 1 KB copies per tensor and chunk
   constexpr int NI = (NINST + W - 1) / W;    // copies per wave per tensor and chunk
-  constexpr bool SURPLUS = NINST % W != 0;   // some waves have one copy too many
   constexpr int DJ = D / 16;                 // float4 query pieces per lane
   constexpr int NTILES = D / 16;             // 16-dim output tiles
 
   __shared__ __attribute__((aligned(16))) float lds[2][2][TILE];  // [buffer][K|V]
-  // target of the surplus copies (they repeat a real copy; never read)
-  __shared__ __attribute__((aligned(16))) float sink[SURPLUS ? 256 : 4];
 
   const int w = blockIdx.x / wg_per_range;
   const int hg = blockIdx.x - w * wg_per_range;  // this workgroup's group of head blocks
@@ -140,9 +137,8 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
       qf[j] = hq_ok ? *reinterpret_cast<const f32x4*>(qrow + 16 * j + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Copy slot c of this wave is instruction i = wave + c W of the chunk (the
-  // surplus slots, i >= NINST, repeat instruction i - NINST into the sink):
-  // lane l fills LDS chunk 64 i + l = row r, physical chunk l % CPR, with the
+  // Copy slot c of this wave is instruction i = wave + c W of the chunk
+  // (slots past the last instruction, i >= NINST, issue nothing): lane l fills LDS chunk 64 i + l = row r, physical chunk l % CPR, with the
   // logical chunk the swizzle puts there (ck, cv: its byte offset in the row).
   // Rows past the partition end are fetched from its last row (valid memory;
   // their scores are masked).
@@ -161,12 +157,13 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
       const int i = wave + c * W;  // uniform
+      if (i >= NINST) continue;
       // the chunk's first row (uniform) plus a small per-lane offset
       const uint32_t ro = (uint32_t)min(crow[c], last - c0) * (uint32_t)(4 * D);
       const char* kp = reinterpret_cast<const char*>(kbase + (size_t)c0 * D) + (ro + ck[c]);
       const char* vp = reinterpret_cast<const char*>(vbase + (size_t)c0 * D) + (ro + cv[c]);
-      float* kd = i < NINST ? &lds[buf][0][i * 256] : sink;
-      float* vd = i < NINST ? &lds[buf][1][i * 256] : sink;
+      float* kd = &lds[buf][0][i * 256];
+      float* vd = &lds[buf][1][i * 256];
       __builtin_amdgcn_global_load_lds(kp, (__attribute__((address_space(3))) void*)kd, 16, 0, kAux);
       __builtin_amdgcn_global_load_lds(vp, (__attribute__((address_space(3))) void*)vd, 16, 0, kAux);
     }

@@ -190,9 +190,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_min
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 
-  // Copy slot c of this wave is instruction i = wave + c W of the block (the
-  // surplus slots, i >= NINST, repeat instruction i - NINST into the sink):
-  // lane l fills LDS chunk 64 i + l = row r, physical chunk l % LPR, with the
+  // Copy slot c of this wave is instruction i = wave + c W of the block
+  // (surplus slots, i >= NINST: with a ring of three or more buffers they
+  // repeat instruction i - NINST into the sink, so that every wave issues the
+  // same number of copies per block as the ring's counted waits assume; with
+  // two, whose waits are for every copy, they are skipped): lane l fills LDS chunk 64 i + l = row r, physical chunk l % LPR, with the
   // logical chunk that the swizzle puts there (ck, cv: that chunk's byte
   // offset inside its K and V row).  Rows past the partition end are fetched
   // from its last row (valid memory; masked).
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(wide_min
 #pragma unroll
     for (int c = 0; c < NI; ++c) {
       const int i = wave + c * W;  // uniform
+      if (NS < 3 && i >= NINST) continue;
       const int ir = i % NINST;
       const char* kp;
       const char* vp;

@@ -1,8 +1,9 @@
 """Host checks of the LDS layouts of the multi-query decode passes
 (decode_wide_bf16.hip, decode_wide_int8.hip), restated from the kernels'
 index formulas: the direct global-to-LDS copies of one 32-position chunk
-fill every byte of the staged tile exactly once (a wave's surplus copies go
-to a sink), and every operand read -- K rows as matrix-core A operands, V
+fill every byte of the staged tile exactly once (a wave's surplus copy
+slots issue nothing, or go to a sink in rings of three or more buffers), and
+every operand read -- K rows as matrix-core A operands, V
 through the 16-bit transposed read -- finds the element it stands for.
 Exhaustive over d in {64, 128} and 2..8 waves; no GPU."""
 import pytest
