@@ -43,6 +43,12 @@ def test_decode_tiny_f32(K):
     assert r["finite"] and r["max_abs"] <= TOL["f32"]
 
 
+# batches past one 64-lane chunk of the device-side length scans (the flat
+# split's total, its sequence search and the recorded split walk the lengths
+# 64 at a time): ragged, with empty sequences
+RAGGED_130 = [0, 300, 1] + [int(x) for x in np.random.RandomState(7).randint(0, 301, 127)]
+RAGGED_70 = [0] + [int(x) for x in np.random.RandomState(8).randint(0, 700, 69)]
+
 # ---- bf16 (and fp32) shape sweep: group sizes, head dims, ragged lengths ----
 CASES = [
     # B, H, K, d, lens, dtype
@@ -71,6 +77,9 @@ CASES = [
     (1, 144, 1, 128, [300], "f32"),            # G = 144: two workgroups per range (8 + 1 blocks)
     (1, 144, 1, 64, [300], "f32"),
     (4, 64, 8, 128, [0, 1, 640, 641], "f32"),  # empty sequence, partition edges
+    (130, 8, 2, 64, RAGGED_130, "bf16"),       # B = 130: three chunks of the length scans
+    (70, 40, 2, 128, RAGGED_70, "bf16"),       # B = 70, G = 20: the multi-wave pass
+    (130, 8, 2, 64, RAGGED_130, "f32"),
 ]
 
 

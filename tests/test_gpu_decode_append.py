@@ -39,6 +39,10 @@ def _unfused(inp, max_seq_len, out_dtype=None):
     return out, kc, vc, sl
 
 
+# B = 130 (three 64-lane chunks of the length scans, the new lengths
+# published for all of them), ragged, one empty and one full cache
+RAGGED_130 = [0, 310, 1] + [int(x) for x in np.random.RandomState(9).randint(0, 301, 127)]
+
 CASES = [
     # B, H, K, d, lens, S_max, dtype
     (4, 32, 8, 128, [0, 1, 700, 4095], 4096, "bf16"),   # empty, one row, middle, last free row
@@ -51,6 +55,7 @@ CASES = [
     (2, 40, 1, 128, [500, 500], 500, "bf16"),           # G = 40, full caches: no append
     (3, 12, 4, 128, [0, 63, 200], 256, "f32"),
     (2, 16, 16, 64, [64, 64], 64, "f32"),               # full caches, fp32
+    (130, 8, 2, 64, RAGGED_130, 310, "bf16"),
 ]
 
 

@@ -83,6 +83,8 @@ def _vmax(vc, vs, lens):
     return max(float(np.abs(v[b, :, :L]).max()) if L else 0.0 for b, L in enumerate(lens))
 
 
+RAGGED_130 = [0, 300, 1] + [int(x) for x in np.random.RandomState(6).randint(0, 301, 127)]
+
 # a large ragged batch (>= 256 sequence-head units), lengths 0..600
 RAGGED_40 = [0, 1, 600] + [int(x) for x in np.random.RandomState(5).randint(0, 601, 37)]
 
@@ -97,6 +99,7 @@ CASES = [
     (1, 71, 1, 64, [257]),             # G = 71: five head blocks
     (1, 144, 1, 64, [300]),            # G = 144: nine head blocks (one wave per block)
     (40, 16, 8, 64, RAGGED_40),        # 320 units: one-dimensional grid, partition slowest
+    (130, 8, 2, 64, RAGGED_130),       # B = 130: three 64-lane chunks of the length scans
 ]
 
 

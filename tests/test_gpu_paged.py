@@ -54,6 +54,8 @@ CASES = [
     (1, 128, 2, 64, [1500], 16),              # G = 64: four head blocks
     # partitions capped at 62 blocks of 16 rows (992 positions)
     (40, 8, 8, 64, [8000 + 37 * i for i in range(40)], 16),
+    # B = 130: three 64-lane chunks of the length scans, ragged, an empty sequence
+    (130, 8, 2, 64, [0, 300, 1] + [int(x) for x in np.random.RandomState(4).randint(0, 301, 127)], 16),
 ]
 
 
