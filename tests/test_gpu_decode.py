@@ -77,6 +77,11 @@ CASES = [
     (1, 144, 1, 128, [300], "f32"),            # G = 144: two workgroups per range (8 + 1 blocks)
     (1, 144, 1, 64, [300], "f32"),
     (4, 64, 8, 128, [0, 1, 640, 641], "f32"),  # empty sequence, partition edges
+    (2, 64, 1, 128, [900, 33], "bf16"),        # d = 128, G = 64: four waves
+    (1, 96, 1, 128, [513], "bf16"),            # d = 128, G = 96: six waves
+    (1, 100, 1, 128, [700], "bf16"),           # d = 128, G = 100: seven waves, the last with four heads
+    (1, 128, 1, 128, [1500], "bf16"),          # d = 128, G = 128: eight waves
+    (1, 144, 1, 128, [300], "bf16"),           # d = 128, G = 144: one wave per block
     (130, 8, 2, 64, RAGGED_130, "bf16"),       # B = 130: three chunks of the length scans
     (70, 40, 2, 128, RAGGED_70, "bf16"),       # B = 70, G = 20: the multi-wave pass
     (130, 8, 2, 64, RAGGED_130, "f32"),

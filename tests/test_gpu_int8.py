@@ -100,6 +100,9 @@ CASES = [
     (1, 144, 1, 64, [300]),            # G = 144: nine head blocks (one wave per block)
     (40, 16, 8, 64, RAGGED_40),        # 320 units: one-dimensional grid, partition slowest
     (130, 8, 2, 64, RAGGED_130),       # B = 130: three 64-lane chunks of the length scans
+    (2, 64, 1, 128, [900, 33]),        # d = 128, G = 64: four waves
+    (1, 100, 1, 128, [700]),           # d = 128, G = 100: seven waves, the last with four heads
+    (1, 128, 1, 128, [1500]),          # d = 128, G = 128: eight waves
 ]
 
 
