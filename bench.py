@@ -315,7 +315,7 @@ def bench_decode(args, w, sub=False):
                    "append_per_step": bool(w.append), "cache_copies": R,
                    **({"block_size": w.extra["block_size"], "block_order": "shuffled"} if paged else {}),
                    **({"kv_dtype": "int8", "kv_row_bytes": d + 4} if int8 else {}),
-                   "parallelism": "single GPU"},
+                   "seed": args.seed, "parallelism": "single GPU"},
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(total_bytes / args.steps),
@@ -467,7 +467,7 @@ def bench_prefill(args, w):
     achieved = flops / (kern_ms * 1e-3) / 1e12
     S_q = {"prefill": w.L, "chunk": w.extra.get("chunk"), "cross": w.extra.get("S_q")}[w.kind]
     cfg = {"workload": w.name, "B": w.B, "H": w.H, "K": w.K, "d": w.d, "S_q": S_q, "kv_len": w.L,
-           "parallelism": "single GPU"}
+           "seed": args.seed, "parallelism": "single GPU"}
     # a contraction takes the matrix-core peak of its own type
     f32 = w.dtype == "f32"
     peak = F32_MFMA_PEAK_TFLOPS if f32 else BF16_MFMA_PEAK_TFLOPS
@@ -540,7 +540,7 @@ def bench_project(args, w):
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": T, "d_model": dm, "K": w.K, "d": w.d,
-                   "w_kv_copies": layers, "parallelism": "single GPU"},
+                   "w_kv_copies": layers, "seed": args.seed, "parallelism": "single GPU"},
         "tokens_per_s": round(w.B * T / (ms_per_step * 1e-3), 1),
         "roofline": {"kernel": "K/V projection (kv_project_kernel)",
                      "bound": "hbm",
@@ -620,7 +620,7 @@ def bench_meanpool(args, w):
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "outer": 1, "H": w.H, "K": w.K, "inner": inner, "matrices": n,
-                   "parallelism": "single GPU"},
+                   "seed": args.seed, "parallelism": "single GPU"},
         "roofline": {"kernel": "mean-pool conversion (meanpool_vec_kernel)", "bound": "hbm",
                      "achieved": round(byts / (kern_ms * 1e-3) / 1e9, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(byts / (kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
