@@ -36,10 +36,14 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(
   const int G = H / K;
   const int k = h / G;
   const int lane = threadIdx.x;
-  // the split the partition pass recorded: length, flat start, total
+  // the split the partition pass recorded: length, flat start, total (read
+  // before any arithmetic on them, so that the three loads are in flight
+  // together)
   const int L = meta[b];
-  const int R = flat_range(meta[2 * B], fa);
-  const int base = meta[B + b] + k * pad32(L);  // flat start of pair (b, k)
+  const int start_b = meta[B + b];
+  const int total = meta[2 * B];
+  const int R = flat_range(total, fa);
+  const int base = start_b + k * pad32(L);  // flat start of pair (b, k)
   const int w0 = base / R;
   const int n = L > 0 ? (base + L - 1) / R - w0 + 1 : 0;  // partials of this pair
   // partial p is slot w0 + p + b K + k, row h - k G
