@@ -93,11 +93,12 @@ __global__ __launch_bounds__(64 * W) void decode_split_f32_kernel(
     return min(APPEND && L_in < S_max ? L_in + 1 : L_in, fa.max_len);
   };
   // the lengths attended over and the split, for the combine pass
-  if (blockIdx.x == 0 && wave == 0) flat_publish(B, K, len_of, meta);
-  const int total = flat_total(B, K, len_of);
+  const int l0 = first_lengths(B, len_of);  // lengths of sequences 0..63, one per lane
+  if (blockIdx.x == 0 && wave == 0) flat_publish(B, K, l0, len_of, meta);
+  const int total = flat_total(B, K, l0, len_of);
   const int R = flat_range(total, fa);
 
-  flat_for_each_segment(w, B, K, total, R, len_of,
+  flat_for_each_segment(w, B, K, total, R, l0, len_of,
                         [&](int b, int k, int t0, int t1, int L, int slot) {
   const int newpos = APPEND && L > len_in(b) ? L - 1 : -1;  // the appended row, if any
   const int last = t1 - 1;

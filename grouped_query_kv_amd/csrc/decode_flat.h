@@ -77,27 +77,39 @@ __device__ inline int wave_incl_scan(int x) {
   return x;
 }
 
+// The lengths of sequences 0..63 are read once per wave, one per lane (l0 =
+// len_of(lane) for lane < B, else 0), and passed to the functions below, so
+// the split's total, its sequence search and the recorded split cost one
+// round trip to memory between them; sequences past 63 are read as needed.
+template <class LenFn>
+__device__ inline int first_lengths(int B, LenFn len_of) {
+  const int lane = threadIdx.x & 63;
+  return lane < B ? len_of(lane) : 0;
+}
+
+// Length of sequence i0 + lane (i0 a multiple of 64, wave-uniform).
+template <class LenFn>
+__device__ inline int chunk_length(int B, int i0, int l0, LenFn len_of) {
+  const int i = i0 + (threadIdx.x & 63);
+  return i0 == 0 ? l0 : (i < B ? len_of(i) : 0);
+}
+
 // K * sum_b pad32(len_of(b)).
 template <class LenFn>
-__device__ inline int flat_total(int B, int K, LenFn len_of) {
-  const int lane = threadIdx.x & 63;
+__device__ inline int flat_total(int B, int K, int l0, LenFn len_of) {
   int sum = 0;
-  for (int i0 = 0; i0 < B; i0 += 64) {
-    const int i = i0 + lane;
-    sum += wave_sum(i < B ? pad32(len_of(i)) : 0);
-  }
+  for (int i0 = 0; i0 < B; i0 += 64) sum += wave_sum(pad32(chunk_length(B, i0, l0, len_of)));
   return K * sum;
 }
 
 // The sequence whose flat run [start_b, start_b + K pad32(L_b)) holds flat
 // position `pos` (0 <= pos < total): sets b, start_b and L_b.
 template <class LenFn>
-__device__ inline void flat_find(int B, int K, int pos, LenFn len_of, int& b, int& start_b, int& L_b) {
-  const int lane = threadIdx.x & 63;
+__device__ inline void flat_find(int B, int K, int pos, int l0, LenFn len_of, int& b, int& start_b,
+                                 int& L_b) {
   int run = 0;  // flat start of sequence i0
   for (int i0 = 0; i0 < B; i0 += 64) {
-    const int i = i0 + lane;
-    const int L = i < B ? len_of(i) : 0;
+    const int L = chunk_length(B, i0, l0, len_of);
     const int incl = wave_incl_scan(K * pad32(L));
     const unsigned long long hit = __ballot(run + incl > pos);
     if (hit) {
@@ -130,12 +142,12 @@ __device__ inline int flat_start_of(int B, int K, int b, LenFn len_of) {
 // 0): meta[b] = the length of sequence b attended over, meta[B + b] = its
 // flat start, meta[2B] = the total.
 template <class LenFn>
-__device__ inline void flat_publish(int B, int K, LenFn len_of, int32_t* meta) {
+__device__ inline void flat_publish(int B, int K, int l0, LenFn len_of, int32_t* meta) {
   const int lane = threadIdx.x & 63;
   int run = 0;
   for (int i0 = 0; i0 < B; i0 += 64) {
     const int i = i0 + lane;
-    const int L = i < B ? len_of(i) : 0;
+    const int L = chunk_length(B, i0, l0, len_of);
     const int incl = wave_incl_scan(K * pad32(L));
     if (i < B) {
       meta[i] = L;
@@ -150,13 +162,13 @@ __device__ inline void flat_publish(int B, int K, LenFn len_of, int32_t* meta) {
 // every pair (b, k) whose valid positions meet the workgroup's range, in
 // flat order.  len_of(b) must give the same lengths in every workgroup.
 template <class LenFn, class SegFn>
-__device__ inline void flat_for_each_segment(int w, int B, int K, int total, int R, LenFn len_of,
-                                             SegFn seg) {
+__device__ inline void flat_for_each_segment(int w, int B, int K, int total, int R, int l0,
+                                             LenFn len_of, SegFn seg) {
   int pos = w * R;
   const int end = min(pos + R, total);
   if (pos >= end) return;
   int b, start_b, L_b;
-  flat_find(B, K, pos, len_of, b, start_b, L_b);
+  flat_find(B, K, pos, l0, len_of, b, start_b, L_b);
   int Lp = pad32(L_b);
   int k = (pos - start_b) / Lp;
   int base = start_b + k * Lp;  // flat start of pair (b, k)
@@ -170,7 +182,7 @@ __device__ inline void flat_for_each_segment(int w, int B, int K, int total, int
       k = 0;
       do {  // sequences of length 0 take no flat positions
         ++b;
-        L_b = b < B ? len_of(b) : 1;
+        L_b = b >= B ? 1 : (b < 64 ? uniform(__shfl(l0, b)) : len_of(b));
       } while (L_b == 0);
       if (b >= B) break;
       Lp = pad32(L_b);
